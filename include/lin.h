@@ -1,0 +1,156 @@
+/*
+ * lin.h -- decode-step linear layers for AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The operation.  A decode step multiplies every weight matrix of the model by
+ * the current activation: y = W . x, each weight read from memory once and used
+ * for one multiply-add (llm-rs benchmark post, section 2 "Decode with one request
+ * is a memory problem"; yalm post, CPU matmul section: W (d,n) @ x (n,) with W
+ * row-major).  A batch of M tokens reuses each weight M times, Y = X . W^T (llm-rs
+ * benchmark post, section 3 "Batching moves decode from memory toward math").
+ * Weights are bf16, or 4-bit integers with one fp16 scale per 64 weights along k
+ * (tinyinfer post, TL;DR).
+ *
+ * Layouts (all row-major, contiguous, leading dimension = K):
+ *   W   bf16    [N][K]     weights, N outputs by K inputs
+ *   Wq  uint8   [N][K/2]   int4 codes, two per byte along k: byte j of a row holds
+ *                          k = 2j in bits 0..3 and k = 2j+1 in bits 4..7; each
+ *                          code is 4-bit two's complement q in [-8, 7]
+ *   S   fp16    [N][K/64]  scale of each group of 64 consecutive k; w = q * s
+ *   x/X bf16    [M][K]     activations, one row per token
+ *   y/Y fp32    [M][N]     outputs, overwritten (no accumulation into y)
+ * Accumulation is fp32.  The result of every configuration is within
+ * 1e-3 * sum_k |W[n][k] * x[m][k]| of the exact product, per output.
+ *
+ * Ownership and execution.  Every pointer is a device pointer owned by the
+ * caller; the library never frees or retains them.  The compute entry points
+ * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemm_skinny_bf16, lin_quantize_q4g64)
+ * validate their arguments in O(1), enqueue kernels on `stream` (a hipStream_t;
+ * NULL = the null stream) and return without waiting: they never allocate,
+ * never synchronise and are safe inside HIP graph capture.  Results are
+ * deterministic: the same configuration on the same inputs gives the same bits.
+ * Calls may be made from several host threads; the tuning table is guarded.
+ *
+ * Errors.  Every entry point returns LIN_OK or a negative lin_status.  Argument
+ * errors are detected before anything is enqueued, so nothing has run.
+ * LIN_ERR_HIP means the HIP runtime reported an error (for example a launch
+ * failure); the stream may then hold partial work.  No C++ exception crosses
+ * this interface.  M == 0 or N == 0 is a valid empty call (nothing is enqueued;
+ * pointers may be NULL).  K == 0 writes zeros to y (W and x may be NULL).
+ */
+#ifndef LIN_H
+#define LIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lin_status {
+    LIN_OK = 0,
+    LIN_ERR_NULL = -1,        /* a required pointer is NULL */
+    LIN_ERR_SHAPE = -2,       /* M, N or K out of range, or K not a multiple of 8 (bf16) / 64 (int4) */
+    LIN_ERR_ALIGN = -3,       /* W, Wq, x or X not 16-byte aligned; y, Y not 4-byte; S not 2-byte */
+    LIN_ERR_UNSUPPORTED = -4, /* the requested configuration cannot run this shape */
+    LIN_ERR_HIP = -5,         /* the HIP runtime reported an error */
+    LIN_ERR_ARG = -6          /* unknown kind, malformed configuration, bad index */
+} lin_status;
+
+/* The three products; `kind` selects one in the tuning calls. */
+typedef enum lin_kind {
+    LIN_KIND_GEMV_BF16 = 0,   /* lin_gemv_bf16 */
+    LIN_KIND_GEMV_Q4G64 = 1,  /* lin_gemv_q4g64 */
+    LIN_KIND_SKINNY_BF16 = 2  /* lin_gemm_skinny_bf16 */
+} lin_kind;
+
+/* Kernel families. */
+typedef enum lin_algo {
+    LIN_ALGO_VALU = 1,        /* vector-ALU streaming product: each wavefront owns `rows` rows */
+    LIN_ALGO_MFMA = 2         /* matrix-core tiles (skinny bf16 product only) */
+} lin_algo;
+
+/* One launch configuration.  VALU: a wavefront owns `rows` consecutive rows and
+ * streams them with 16-byte loads, `unroll` loads per lane and row in flight;
+ * `split` wavefronts share a row group by splitting K and combine through LDS;
+ * `stage_x` = 1 stages x in LDS once per workgroup.  MFMA: `rows` is the W rows
+ * per workgroup, `tile_m` the tokens per workgroup tile; `split` = wavefronts per
+ * workgroup splitting K.  `us` is filled by lin_autotune (median microseconds
+ * per call, cold caches) and ignored on input. */
+typedef struct lin_config {
+    int32_t algo;
+    int32_t rows;
+    int32_t unroll;
+    int32_t split;
+    int32_t stage_x;
+    int32_t tile_m;
+    int32_t reserved[2];
+    float us;
+} lin_config;
+
+/* Largest M accepted by lin_gemv_bf16 / lin_gemv_q4g64, and by lin_gemm_skinny_bf16. */
+#define LIN_GEMV_MAX_M 8
+#define LIN_SKINNY_MAX_M 256
+/* Largest K accepted by every product. */
+#define LIN_MAX_K (1 << 22)
+
+/* y[m][n] = sum_k W[n][k] * x[m][k] for bf16 W [N][K], x [M][K]; fp32 y [M][N].
+ * 1 <= M <= LIN_GEMV_MAX_M (the batch-1 decode GEMV is M = 1), K % 8 == 0. */
+int lin_gemv_bf16(const void* W, const void* x, float* y,
+                  int64_t M, int64_t N, int64_t K, void* stream);
+
+/* The same product with int4-g64 weights: w[n][k] = q[n][k] * S[n][k/64].
+ * K % 64 == 0, 1 <= M <= LIN_GEMV_MAX_M. */
+int lin_gemv_q4g64(const void* Wq, const void* S, const void* x, float* y,
+                   int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Batched-token product Y = X . W^T for 1 <= M <= LIN_SKINNY_MAX_M tokens,
+ * K % 8 == 0.  Small M streams W once through the vector ALUs; larger M runs on
+ * the matrix cores; the crossover is part of the tuned configuration. */
+int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y,
+                         int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Load-time tuning (tinyinfer post, "v0.2": time the candidates on every
+ * distinct shape when the model loads, keep the fastest).  Times every
+ * candidate configuration of `kind` for (M, N, K) on the caller's buffers,
+ * which must be valid for that kind (S is used only by LIN_KIND_GEMV_Q4G64 and
+ * may be NULL otherwise; y receives scratch results).  Each timed call starts
+ * from cold caches.  The fastest configuration is stored in the per-device
+ * table and used by later calls with the same (kind, M, N, K); if `out` is not
+ * NULL it receives it, with `us` set.  Unlike the compute calls this one
+ * allocates a cache-flush buffer on first use (kept until process exit),
+ * synchronises `stream` and must not be called during graph capture. */
+int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y,
+                 int64_t M, int64_t N, int64_t K, void* stream, lin_config* out);
+
+/* Candidate configurations for (kind, M, N, K), in a fixed order: returns how
+ * many there are (>= 0) or a negative status.  lin_candidate writes number
+ * `index` to *out. */
+int lin_num_candidates(int kind, int64_t M, int64_t N, int64_t K);
+int lin_candidate(int kind, int64_t M, int64_t N, int64_t K, int index, lin_config* out);
+
+/* The configuration the next call of (kind, M, N, K) on the current device will
+ * use: the tuned or pinned entry if there is one, else the built-in default. */
+int lin_get_config(int kind, int64_t M, int64_t N, int64_t K, lin_config* out);
+
+/* Pin `cfg` for (kind, M, N, K) on the current device (it must be one of the
+ * candidates), or remove the entry when cfg is NULL. */
+int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg);
+
+/* Load-time weight preparation: quantise bf16 W [N][K] (K % 64 == 0) to the
+ * int4-g64 layout above.  Per row and group of 64 k: a = max |w|;
+ * s = fp16 nearest to a/7 (ties to even; saturates at 65504);
+ * q = s > 0 ? clamp(round_half_even(w / s), -8, 7) : 0, with w/s in fp64.
+ * Writes Wq [N][K/2] and S [N][K/64].  W must hold finite values. */
+int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, void* stream);
+
+/* Static description of a status code. */
+const char* lin_status_string(int status);
+
+/* Interface version: (major << 16) | minor. */
+int lin_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIN_H */

@@ -1,0 +1,243 @@
+"""Decode-step linear layers on MI355X (gfx950): Python binding of liblin.so.
+
+The functions here carry the names of the C entry points in include/lin.h and
+only marshal arguments: they check dtype, device, contiguity and shape, pass
+raw device pointers and torch's current HIP stream, and raise on a non-zero
+status.  Every step of every product runs in the library's HIP kernels.  The
+library must have been built (``__graft_entry__.build()`` or
+``python memory_bound_weight_amd/build.py``); importing fails loudly otherwise.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblin.so")
+
+LIN_OK = 0
+LIN_ERR_NULL = -1
+LIN_ERR_SHAPE = -2
+LIN_ERR_ALIGN = -3
+LIN_ERR_UNSUPPORTED = -4
+LIN_ERR_HIP = -5
+LIN_ERR_ARG = -6
+
+LIN_KIND_GEMV_BF16 = 0
+LIN_KIND_GEMV_Q4G64 = 1
+LIN_KIND_SKINNY_BF16 = 2
+
+LIN_ALGO_VALU = 1
+LIN_ALGO_MFMA = 2
+
+LIN_GEMV_MAX_M = 8
+LIN_SKINNY_MAX_M = 256
+
+# Every symbol include/lin.h declares.
+EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemm_skinny_bf16", "lin_autotune",
+           "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
+           "lin_quantize_q4g64", "lin_status_string", "lin_version")
+
+
+class LinConfig(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32), ("rows", ctypes.c_int32), ("unroll", ctypes.c_int32),
+                ("split", ctypes.c_int32), ("stage_x", ctypes.c_int32), ("tile_m", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2), ("us", ctypes.c_float)]
+
+    def as_dict(self):
+        return dict(algo=self.algo, rows=self.rows, unroll=self.unroll, split=self.split,
+                    stage_x=self.stage_x, tile_m=self.tile_m, us=self.us)
+
+    @classmethod
+    def from_dict(cls, d):
+        c = cls()
+        for k in ("algo", "rows", "unroll", "split", "stage_x", "tile_m"):
+            setattr(c, k, int(d[k]))
+        return c
+
+
+class LinError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__("%s failed: %s (%d)" % (where, status_string(status), status))
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("liblin.so is not built (%s); run __graft_entry__.build() or "
+                          "python memory_bound_weight_amd/build.py" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sig = {
+        "lin_gemv_bf16": [P, P, P, I64, I64, I64, P],
+        "lin_gemv_q4g64": [P, P, P, P, I64, I64, I64, P],
+        "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
+        "lin_autotune": [I, P, P, P, P, I64, I64, I64, P, ctypes.POINTER(LinConfig)],
+        "lin_num_candidates": [I, I64, I64, I64],
+        "lin_candidate": [I, I64, I64, I64, I, ctypes.POINTER(LinConfig)],
+        "lin_get_config": [I, I64, I64, I64, ctypes.POINTER(LinConfig)],
+        "lin_set_config": [I, I64, I64, I64, ctypes.POINTER(LinConfig)],
+        "lin_quantize_q4g64": [P, P, P, I64, I64, P],
+        "lin_status_string": [I],
+        "lin_version": [],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_char_p if name == "lin_status_string" else ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def status_string(status):
+    return _lib.lin_status_string(int(status)).decode()
+
+
+def lin_version():
+    return _lib.lin_version()
+
+
+def _check(st, where):
+    if st != LIN_OK:
+        raise LinError(st, where)
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, dtype, name, dims):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device" % name)
+    if t.dim() != dims:
+        raise ValueError("%s must have %d dimensions" % (name, dims))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _as2d(x):
+    return x.unsqueeze(0) if x.dim() == 1 else x
+
+
+def _out(y, M, N, dev):
+    if y is None:
+        return torch.empty((M, N), dtype=torch.float32, device=dev)
+    _need(y, torch.float32, "y", 2)
+    if tuple(y.shape) != (M, N):
+        raise ValueError("y must have shape (%d, %d)" % (M, N))
+    return y
+
+
+def lin_gemv_bf16(W, x, y=None):
+    """y[m][n] = sum_k W[n][k] x[m][k]; W bf16 [N, K], x bf16 [M, K] or [K]."""
+    x = _as2d(x)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    N, K = W.shape
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must have K = %d columns" % K)
+    y = _out(y, M, N, W.device)
+    _check(_lib.lin_gemv_bf16(W.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K, _stream(W)),
+           "lin_gemv_bf16")
+    return y
+
+
+def lin_gemv_q4g64(Wq, S, x, y=None):
+    """Same product with int4-g64 weights: Wq uint8 [N, K/2], S fp16 [N, K/64]."""
+    x = _as2d(x)
+    _need(Wq, torch.uint8, "Wq", 2)
+    _need(S, torch.float16, "S", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    N, K2 = Wq.shape
+    K = 2 * K2
+    M = x.shape[0]
+    if x.shape[1] != K or tuple(S.shape) != (N, K // 64):
+        raise ValueError("shape mismatch: Wq [N, K/2], S [N, K/64], x [M, K]")
+    y = _out(y, M, N, Wq.device)
+    _check(_lib.lin_gemv_q4g64(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(),
+                               M, N, K, _stream(Wq)), "lin_gemv_q4g64")
+    return y
+
+
+def lin_gemm_skinny_bf16(W, X, Y=None):
+    """Y = X . W^T for M <= 256 tokens; W bf16 [N, K], X bf16 [M, K]."""
+    X = _as2d(X)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(X, torch.bfloat16, "X", 2)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X must have K = %d columns" % K)
+    Y = _out(Y, M, N, W.device)
+    _check(_lib.lin_gemm_skinny_bf16(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K,
+                                     _stream(W)), "lin_gemm_skinny_bf16")
+    return Y
+
+
+def lin_quantize_q4g64(W, Wq=None, S=None):
+    """int4-g64 weights from bf16 W [N, K]: returns (Wq uint8 [N, K/2], S fp16 [N, K/64])."""
+    _need(W, torch.bfloat16, "W", 2)
+    N, K = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    if S is None:
+        S = torch.empty((N, K // 64), dtype=torch.float16, device=W.device)
+    _need(Wq, torch.uint8, "Wq", 2)
+    _need(S, torch.float16, "S", 2)
+    _check(_lib.lin_quantize_q4g64(W.data_ptr(), Wq.data_ptr(), S.data_ptr(), N, K, _stream(W)),
+           "lin_quantize_q4g64")
+    return Wq, S
+
+
+def _shape_args(kind, W, S, x):
+    x = _as2d(x)
+    if kind == LIN_KIND_GEMV_Q4G64:
+        return x, x.shape[0], W.shape[0], 2 * W.shape[1]
+    return x, x.shape[0], W.shape[0], W.shape[1]
+
+
+def lin_autotune(kind, W, x, y, S=None):
+    """Time every candidate for this shape on these buffers (cold caches), keep
+    the fastest for later calls; returns it as a dict with 'us'."""
+    x, M, N, K = _shape_args(kind, W, S, x)
+    cfg = LinConfig()
+    _check(_lib.lin_autotune(int(kind), W.data_ptr(), S.data_ptr() if S is not None else None,
+                             x.data_ptr(), y.data_ptr(), M, N, K, _stream(W), ctypes.byref(cfg)),
+           "lin_autotune")
+    return cfg.as_dict()
+
+
+def lin_num_candidates(kind, M, N, K):
+    n = _lib.lin_num_candidates(int(kind), M, N, K)
+    if n < 0:
+        raise LinError(n, "lin_num_candidates")
+    return n
+
+
+def lin_candidate(kind, M, N, K, index):
+    cfg = LinConfig()
+    _check(_lib.lin_candidate(int(kind), M, N, K, int(index), ctypes.byref(cfg)), "lin_candidate")
+    return cfg.as_dict()
+
+
+def lin_candidates(kind, M, N, K):
+    return [lin_candidate(kind, M, N, K, i) for i in range(lin_num_candidates(kind, M, N, K))]
+
+
+def lin_get_config(kind, M, N, K):
+    cfg = LinConfig()
+    _check(_lib.lin_get_config(int(kind), M, N, K, ctypes.byref(cfg)), "lin_get_config")
+    return cfg.as_dict()
+
+
+def lin_set_config(kind, M, N, K, cfg):
+    """Pin cfg (a dict from lin_candidate) for this shape; None removes the entry."""
+    p = ctypes.byref(LinConfig.from_dict(cfg)) if cfg is not None else None
+    _check(_lib.lin_set_config(int(kind), M, N, K, p), "lin_set_config")

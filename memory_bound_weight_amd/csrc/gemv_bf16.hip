@@ -1,0 +1,205 @@
+// bf16 streaming product on the vector ALUs: y[m][n] = sum_k W[n][k] x[m][k]
+// for a few tokens (M <= 32).  The weights are streamed from HBM exactly once
+// (llm-rs benchmark post, section 2: decode is weight streaming); the tokens of
+// a batch share each loaded weight (section 3 of the same post).
+//
+// Mapping.  A workgroup is four wavefronts.  A wavefront owns R consecutive
+// rows; its 64 lanes read consecutive 16-byte chunks of each row (eight bf16),
+// so one wavefront load instruction covers 1 KiB of a row, and a lane keeps
+// U x R independent loads in flight (tinyinfer post, "v0.2": several rows per
+// warp keep more requests in flight).  With SPLIT > 1, SPLIT wavefronts share
+// the same rows, each taking a contiguous part of K, and combine through LDS;
+// this fills the chip when N is small.  x is read from the cache hierarchy, or
+// staged in LDS once per workgroup when STAGE is set.  Products use
+// v_dot2_f32_bf16 (two exact bf16 products per instruction, fp32 sums); each
+// lane sums K/512 chunks, then a permlane/DPP tree sums the 64 lanes.
+#include "registry.h"
+
+namespace lin {
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+__global__ __launch_bounds__(kBlock) void gemv_bf16_valu(KArgs a) {
+    constexpr int GROUPS = 4 / SPLIT;
+    constexpr int V = R * MT;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = wave / SPLIT;
+    const int part = wave - grp * SPLIT;
+    const int M = a.M, N = a.N, K = a.K;
+    const int nch = K >> 3;   // 16-byte chunks per row
+    const uint16_t* __restrict__ W = (const uint16_t*)a.W;
+    const uint16_t* __restrict__ X = (const uint16_t*)a.X;
+
+    extern __shared__ u32x4 xs[];   // STAGE: [MT][nch] chunks of x
+    if constexpr (STAGE) {
+        for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
+            const int m = i / nch;
+            const int c = i - m * nch;
+            const int mm = m < M ? m : 0;
+            xs[i] = load_x16((const u32x4*)(X + (size_t)mm * K) + c);
+        }
+        __syncthreads();
+    }
+
+    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * R;
+    const u32x4* wp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int64_t row = row0 + r;
+        row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
+        wp[r] = (const u32x4*)(W + row * (int64_t)K);
+    }
+    const u32x4* xp[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xp[m] = (const u32x4*)(X + (size_t)(m < M ? m : 0) * K);
+
+    const int per = (nch + SPLIT - 1) / SPLIT;
+    const int cbeg = part * per;
+    const int cend = min(nch, cbeg + per);
+
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+
+    int cb = cbeg;
+    for (; cb + kWave * U <= cend; cb += kWave * U) {
+        u32x4 w[U][R];
+        u32x4 xv[U][MT];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r) w[u][r] = load_w16(wp[r] + cb + kWave * u + lane);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+                xv[u][m] = STAGE ? xs[m * nch + cb + kWave * u + lane]
+                                 : load_x16(xp[m] + cb + kWave * u + lane);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[r * MT + m] = dot2(w[u][r][j], xv[u][m][j], acc[r * MT + m]);
+    }
+    for (; cb < cend; cb += kWave) {   // ragged tail: one chunk per lane at most
+        const int c = cb + lane;
+        if (c < cend) {
+            u32x4 w[R];
+            u32x4 xv[MT];
+#pragma unroll
+            for (int r = 0; r < R; ++r) w[r] = load_w16(wp[r] + c);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) xv[m] = STAGE ? xs[m * nch + c] : load_x16(xp[m] + c);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[r * MT + m] = dot2(w[r][j], xv[m][j], acc[r * MT + m]);
+        }
+    }
+
+    wave_reduce<V>(acc);
+    if constexpr (SPLIT == 1) {
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) {
+            const int r = idx / MT, m = idx - (idx / MT) * MT;
+            if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = val;
+        });
+    } else {
+        __shared__ float red[4][V];
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) { red[wave][idx] = val; });
+        __syncthreads();
+        if (part == 0) {
+            for_each_reduced<V>(acc, lane, [&](int idx, float) {
+                const int r = idx / MT, m = idx - (idx / MT) * MT;
+                float s = red[wave][idx];
+#pragma unroll
+                for (int p = 1; p < SPLIT; ++p) s += red[wave + p][idx];
+                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = s;
+            });
+        }
+    }
+}
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static bool geom_bf16(const Variant&, int M, int N, int K, dim3* grid, size_t* lds) {
+    constexpr int rows_per_block = R * (4 / SPLIT);
+    size_t bytes = STAGE ? (size_t)MT * (size_t)(K / 8) * 16 : 0;
+    if (bytes > kMaxDynLds) return false;
+    (void)M;
+    *grid = dim3((unsigned)((N + rows_per_block - 1) / rows_per_block));
+    *lds = bytes;
+    return true;
+}
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static void add(std::vector<Variant>& out) {
+    Variant v{};
+    v.cfg.algo = LIN_ALGO_VALU;
+    v.cfg.rows = R;
+    v.cfg.unroll = U;
+    v.cfg.split = SPLIT;
+    v.cfg.stage_x = STAGE ? 1 : 0;
+    v.cfg.tile_m = MT;
+    v.mt = MT;
+    v.min_m = MT / 2 + 1;
+    v.func = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE>;
+    v.geometry = &geom_bf16<MT, R, U, SPLIT, STAGE>;
+    if (MT <= LIN_GEMV_MAX_M) {
+        v.kind = LIN_KIND_GEMV_BF16;
+        out.push_back(v);
+    }
+    v.kind = LIN_KIND_SKINNY_BF16;
+    out.push_back(v);
+}
+
+template <int MT, int R, int U>
+static void add_splits(std::vector<Variant>& out) {
+    add<MT, R, U, 1, false>(out);
+    add<MT, R, U, 2, false>(out);
+    add<MT, R, U, 4, false>(out);
+    if constexpr (MT >= 2) {
+        add<MT, R, U, 1, true>(out);
+        add<MT, R, U, 4, true>(out);
+    }
+}
+
+void register_gemv_bf16(std::vector<Variant>& out) {
+    add_splits<1, 1, 4>(out);
+    add_splits<1, 1, 8>(out);
+    add_splits<1, 2, 2>(out);
+    add_splits<1, 2, 4>(out);
+    add_splits<1, 4, 1>(out);
+    add_splits<1, 4, 2>(out);
+    add_splits<1, 8, 1>(out);
+
+    add_splits<2, 1, 4>(out);
+    add_splits<2, 2, 2>(out);
+    add_splits<2, 4, 2>(out);
+    add_splits<2, 8, 1>(out);
+
+    add_splits<4, 1, 4>(out);
+    add_splits<4, 2, 2>(out);
+    add_splits<4, 4, 1>(out);
+    add_splits<4, 4, 2>(out);
+
+    add_splits<8, 1, 2>(out);
+    add_splits<8, 1, 4>(out);
+    add_splits<8, 2, 2>(out);
+    add_splits<8, 4, 1>(out);
+
+    add_splits<16, 1, 2>(out);
+    add_splits<16, 2, 1>(out);
+    add_splits<16, 4, 1>(out);
+
+    add_splits<32, 1, 1>(out);
+    add_splits<32, 1, 2>(out);
+    add_splits<32, 2, 1>(out);
+}
+
+}  // namespace lin

@@ -1,0 +1,269 @@
+// int4-g64 streaming product on the vector ALUs: w[n][k] = q[n][k] * s[n][k/64],
+// y[m][n] = sum_k w[n][k] x[m][k], for M <= 8 tokens.  4-bit weights with one
+// fp16 scale per 64 (tinyinfer post, TL;DR) cut the streamed bytes to 0.53 B
+// per weight; unpacking must then cost almost nothing, since it is no longer
+// hidden behind the memory traffic (llm-rs benchmark post, section 6).
+//
+// Mapping.  As the bf16 kernel: four wavefronts per workgroup, a wavefront owns
+// R rows, each lane reads consecutive 16-byte chunks = 32 codes = half a scale
+// group, so lanes 2i and 2i+1 share one scale.
+//
+// Unpacking without conversions.  After XOR 0x88888888 every nibble holds
+// n' = q + 8 in [0, 15].  (n' | 0x4300) read as bf16 is exactly 128 + n' =
+// q + 136, so one AND-OR per pair of nibbles yields two bf16 "codes" that go
+// straight into v_dot2_f32_bf16.  Masking 0x000F000F after shifting a dword by
+// 0, 4, 8, 12 pairs nibble i with nibble i+4, i.e. k = 8d+i with k = 8d+i+4,
+// so x is re-paired the same way (one v_perm per pair).  The offset is removed
+// per chunk: sum_k q x = dot(codes, x) - 136 * sum_k x, where sum_k x over the
+// chunk is shared by all rows; the dot chain starts from -136 * sum x.  Then
+// acc += s * chunk sum.  Per 32 weights and row: 4 XOR + 28 unpack + 16 dot2 +
+// 2 for the scale, about 1.6 vector operations per weight.
+//
+// x handling: either re-paired from cached global loads per chunk (cost shared
+// by the R rows), or, with STAGE, re-paired once per workgroup into LDS as
+// [MT][4][chunks] 16-byte words (bank-conflict-free reads) plus the chunk sums.
+#include "registry.h"
+
+namespace lin {
+
+// 16 re-paired x dwords of one 32-k chunk: pair (x[8d+i], x[8d+i+4]) at 4d+i.
+struct XChunk {
+    u32x4 v[4];
+    float negsum;   // -136 * sum of the 32 x values
+};
+
+__device__ __forceinline__ void pair_x(const u32x4 (&xd)[4], XChunk& out) {
+    // xd[t/4][t%4] = natural dword t = (x[2t], x[2t+1]); dword d of the weights
+    // covers k = 8d .. 8d+7, i.e. natural dwords 4d .. 4d+3.
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t a0 = xd[d][0], a1 = xd[d][1], a2 = xd[d][2], a3 = xd[d][3];
+        out.v[d][0] = __builtin_amdgcn_perm(a2, a0, 0x05040100u);   // x0, x4
+        out.v[d][1] = __builtin_amdgcn_perm(a2, a0, 0x07060302u);   // x1, x5
+        out.v[d][2] = __builtin_amdgcn_perm(a3, a1, 0x05040100u);   // x2, x6
+        out.v[d][3] = __builtin_amdgcn_perm(a3, a1, 0x07060302u);   // x3, x7
+        s = dot2(a0, 0x3F803F80u, s);   // bf16 (1.0, 1.0)
+        s = dot2(a1, 0x3F803F80u, s);
+        s = dot2(a2, 0x3F803F80u, s);
+        s = dot2(a3, 0x3F803F80u, s);
+    }
+    out.negsum = -136.f * s;
+}
+
+// Sum over one chunk of 32 codes times re-paired x, minus the code offset.
+__device__ __forceinline__ float chunk_dot(const u32x4& wq, const XChunk& xc) {
+    float acc = xc.negsum;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t w = wq[d] ^ 0x88888888u;
+        acc = dot2((w & 0x000F000Fu) | 0x43004300u, xc.v[d][0], acc);
+        acc = dot2(((w >> 4) & 0x000F000Fu) | 0x43004300u, xc.v[d][1], acc);
+        acc = dot2(((w >> 8) & 0x000F000Fu) | 0x43004300u, xc.v[d][2], acc);
+        acc = dot2(((w >> 12) & 0x000F000Fu) | 0x43004300u, xc.v[d][3], acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float half_to_float(uint16_t h) {
+    return (float)__builtin_bit_cast(_Float16, h);
+}
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+__global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
+    constexpr int GROUPS = 4 / SPLIT;
+    constexpr int V = R * MT;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = wave / SPLIT;
+    const int part = wave - grp * SPLIT;
+    const int M = a.M, N = a.N, K = a.K;
+    const int nch = K >> 5;   // 16-byte chunks (32 codes) per row
+    const int G = K >> 6;     // scale groups per row
+    const uint8_t* __restrict__ Wq = (const uint8_t*)a.W;
+    const uint16_t* __restrict__ S = (const uint16_t*)a.S;
+    const uint16_t* __restrict__ X = (const uint16_t*)a.X;
+
+    extern __shared__ u32x4 xs[];   // STAGE: [MT][4][nch] words, then [MT][nch] floats
+    float* xsum = (float*)(xs + (size_t)MT * 4 * nch);
+    if constexpr (STAGE) {
+        for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
+            const int m = i / nch;
+            const int c = i - m * nch;
+            const int mm = m < M ? m : 0;
+            const u32x4* src = (const u32x4*)(X + (size_t)mm * K) + 4 * c;
+            u32x4 xd[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xd[t] = load_x16(src + t);
+            XChunk xc;
+            pair_x(xd, xc);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xs[(m * 4 + t) * nch + c] = xc.v[t];
+            xsum[m * nch + c] = xc.negsum;
+        }
+        __syncthreads();
+    }
+
+    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * R;
+    const u32x4* wp[R];
+    const uint16_t* sp[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int64_t row = row0 + r;
+        row = row < N ? row : N - 1;
+        wp[r] = (const u32x4*)(Wq + row * (int64_t)(K / 2));
+        sp[r] = S + row * (int64_t)G;
+    }
+    const u32x4* xp[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xp[m] = (const u32x4*)(X + (size_t)(m < M ? m : 0) * K);
+
+    const int per = (nch + SPLIT - 1) / SPLIT;
+    const int cbeg = part * per;
+    const int cend = min(nch, cbeg + per);
+
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+
+    auto get_x = [&](int m, int c, XChunk& xc) {
+        if constexpr (STAGE) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xc.v[t] = xs[(m * 4 + t) * nch + c];
+            xc.negsum = xsum[m * nch + c];
+        } else {
+            u32x4 xd[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xd[t] = load_x16(xp[m] + 4 * c + t);
+            pair_x(xd, xc);
+        }
+    };
+
+    int cb = cbeg;
+    for (; cb + kWave * U <= cend; cb += kWave * U) {
+        u32x4 w[U][R];
+        uint16_t sc[U][R];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int c = cb + kWave * u + lane;
+                w[u][r] = load_w16(wp[r] + c);
+                sc[u][r] = __builtin_nontemporal_load(sp[r] + (c >> 1));
+            }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = cb + kWave * u + lane;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                XChunk xc;
+                get_x(m, c, xc);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    acc[r * MT + m] = fmaf(half_to_float(sc[u][r]), chunk_dot(w[u][r], xc), acc[r * MT + m]);
+            }
+        }
+    }
+    for (; cb < cend; cb += kWave) {
+        const int c = cb + lane;
+        if (c < cend) {
+            u32x4 w[R];
+            uint16_t sc[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                w[r] = load_w16(wp[r] + c);
+                sc[r] = __builtin_nontemporal_load(sp[r] + (c >> 1));
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                XChunk xc;
+                get_x(m, c, xc);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    acc[r * MT + m] = fmaf(half_to_float(sc[r]), chunk_dot(w[r], xc), acc[r * MT + m]);
+            }
+        }
+    }
+
+    wave_reduce<V>(acc);
+    if constexpr (SPLIT == 1) {
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) {
+            const int r = idx / MT, m = idx - (idx / MT) * MT;
+            if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = val;
+        });
+    } else {
+        __shared__ float red[4][V];
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) { red[wave][idx] = val; });
+        __syncthreads();
+        if (part == 0) {
+            for_each_reduced<V>(acc, lane, [&](int idx, float) {
+                const int r = idx / MT, m = idx - (idx / MT) * MT;
+                float s = red[wave][idx];
+#pragma unroll
+                for (int p = 1; p < SPLIT; ++p) s += red[wave + p][idx];
+                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = s;
+            });
+        }
+    }
+}
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static bool geom_q4(const Variant&, int M, int N, int K, dim3* grid, size_t* lds) {
+    constexpr int rows_per_block = R * (4 / SPLIT);
+    size_t bytes = STAGE ? (size_t)MT * (size_t)(K / 32) * (64 + 4) : 0;
+    if (bytes > kMaxDynLds) return false;
+    (void)M;
+    *grid = dim3((unsigned)((N + rows_per_block - 1) / rows_per_block));
+    *lds = bytes;
+    return true;
+}
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static void add(std::vector<Variant>& out) {
+    Variant v{};
+    v.kind = LIN_KIND_GEMV_Q4G64;
+    v.cfg.algo = LIN_ALGO_VALU;
+    v.cfg.rows = R;
+    v.cfg.unroll = U;
+    v.cfg.split = SPLIT;
+    v.cfg.stage_x = STAGE ? 1 : 0;
+    v.cfg.tile_m = MT;
+    v.mt = MT;
+    v.min_m = MT / 2 + 1;
+    v.func = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE>;
+    v.geometry = &geom_q4<MT, R, U, SPLIT, STAGE>;
+    out.push_back(v);
+}
+
+template <int MT, int R, int U>
+static void add_splits(std::vector<Variant>& out) {
+    add<MT, R, U, 1, false>(out);
+    add<MT, R, U, 2, false>(out);
+    add<MT, R, U, 4, false>(out);
+    add<MT, R, U, 1, true>(out);
+    add<MT, R, U, 4, true>(out);
+}
+
+void register_gemv_q4g64(std::vector<Variant>& out) {
+    add_splits<1, 1, 2>(out);
+    add_splits<1, 1, 4>(out);
+    add_splits<1, 2, 1>(out);
+    add_splits<1, 2, 2>(out);
+    add_splits<1, 4, 1>(out);
+    add_splits<1, 4, 2>(out);
+    add_splits<1, 8, 1>(out);
+
+    add_splits<2, 1, 2>(out);
+    add_splits<2, 2, 1>(out);
+    add_splits<2, 4, 1>(out);
+
+    add_splits<4, 1, 2>(out);
+    add_splits<4, 2, 1>(out);
+    add_splits<4, 4, 1>(out);
+
+    add_splits<8, 1, 1>(out);
+    add_splits<8, 2, 1>(out);
+    add_splits<8, 4, 1>(out);
+}
+
+}  // namespace lin

@@ -1,0 +1,120 @@
+// Device helpers shared by the gfx950 kernels of the linear-layer library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lin {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Arguments common to every product kernel (passed by value).
+struct KArgs {
+    const void* W;   // bf16 [N][K] or packed int4 [N][K/2]
+    const void* S;   // fp16 [N][K/64] scales (int4 only)
+    const void* X;   // bf16 [M][K]
+    float* Y;        // fp32 [M][N]
+    int M, N, K;
+};
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;   // four wavefronts per workgroup
+
+// Weights are read exactly once per call: a non-temporal 16-byte load keeps
+// them from displacing the activations, which every wavefront re-reads.
+__device__ __forceinline__ u32x4 load_w16(const u32x4* p) {
+    return __builtin_nontemporal_load(p);
+}
+__device__ __forceinline__ u32x4 load_x16(const u32x4* p) { return *p; }
+
+// acc + a.lo*b.lo + a.hi*b.hi on two bf16 pairs (v_dot2_f32_bf16); the
+// bf16 x bf16 products are exact in fp32.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), acc, false);
+}
+
+__device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return bitsf((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum each of V per-lane values over the 64 lanes of a wavefront, V a power of
+// two <= 64.  Lane pairs l, l^32 and then l, l^16 are combined with the gfx950
+// permlane32/permlane16 swaps, which exchange half of the values in one
+// instruction, so V values cost about 2.5 V operations instead of 6 V.  The
+// rest is summed inside rows of 16 lanes with DPP.  Every lane must be active.
+//
+// On return, slot j < reduce_slots(V) of lane l holds the total of value index
+// reduce_index<V>(j, l); lanes of one 16-lane row hold the same totals.
+constexpr int reduce_slots(int V) { return V >= 4 ? V / 4 : 1; }
+
+template <int V>
+__device__ __forceinline__ int reduce_index(int j, int lane) {
+    constexpr int V1 = V >= 2 ? V / 2 : 1;
+    int idx = j;
+    if constexpr (V >= 2) idx += (V / 2) * ((lane >> 5) & 1);
+    if constexpr (V1 >= 2) idx += (V1 / 2) * ((lane >> 4) & 1);
+    return idx;
+}
+
+// True for the one lane per distinct total that should publish slot j.
+template <int V>
+__device__ __forceinline__ bool reduce_writer(int j, int lane) {
+    constexpr int V1 = V >= 2 ? V / 2 : 1;
+    bool w = (lane & 15) == j;
+    if constexpr (V < 2) w = w && ((lane & 32) == 0);
+    if constexpr (V1 < 2) w = w && ((lane & 16) == 0);
+    return w;
+}
+
+template <int V>
+__device__ __forceinline__ void wave_reduce(float (&v)[V]) {
+    static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "V must be a power of two <= 64");
+    if constexpr (V >= 2) {
+#pragma unroll
+        for (int j = 0; j < V / 2; ++j) {
+            auto p = __builtin_amdgcn_permlane32_swap(fbits(v[j]), fbits(v[j + V / 2]), false, false);
+            v[j] = bitsf(p[0]) + bitsf(p[1]);
+        }
+    } else {
+        auto p = __builtin_amdgcn_permlane32_swap(fbits(v[0]), fbits(v[0]), false, false);
+        v[0] = bitsf(p[0]) + bitsf(p[1]);
+    }
+    constexpr int V1 = V >= 2 ? V / 2 : 1;
+    if constexpr (V1 >= 2) {
+#pragma unroll
+        for (int j = 0; j < V1 / 2; ++j) {
+            auto p = __builtin_amdgcn_permlane16_swap(fbits(v[j]), fbits(v[j + V1 / 2]), false, false);
+            v[j] = bitsf(p[0]) + bitsf(p[1]);
+        }
+    } else {
+        auto p = __builtin_amdgcn_permlane16_swap(fbits(v[0]), fbits(v[0]), false, false);
+        v[0] = bitsf(p[0]) + bitsf(p[1]);
+    }
+    constexpr int V2 = V1 >= 2 ? V1 / 2 : 1;
+#pragma unroll
+    for (int j = 0; j < V2; ++j) {
+        v[j] += dpp<0xB1>(v[j]);    // quad_perm [1,0,3,2]
+        v[j] += dpp<0x4E>(v[j]);    // quad_perm [2,3,0,1]
+        v[j] += dpp<0x141>(v[j]);   // row_half_mirror
+        v[j] += dpp<0x140>(v[j]);   // row_mirror
+    }
+}
+
+// After wave_reduce: call f(index, total) once per value index, from the one
+// lane that publishes it.  Each slot is handled by its own (predicated) call,
+// so the per-lane values are never indexed dynamically.
+template <int V, typename F>
+__device__ __forceinline__ void for_each_reduced(const float (&v)[V], int lane, F&& f) {
+    constexpr int S = reduce_slots(V);
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        if (reduce_writer<V>(s, lane)) f(reduce_index<V>(s, lane), v[s]);
+}
+
+}  // namespace lin

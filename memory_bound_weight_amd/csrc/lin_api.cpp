@@ -1,0 +1,363 @@
+// C-ABI layer of the linear-layer library: argument checks, the per-device
+// configuration table, load-time tuning and kernel launches.  No entry point
+// that computes a product allocates or synchronises.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/lin.h"
+#include "registry.h"
+
+namespace lin {
+namespace {
+
+const std::vector<Variant>& registry() {
+    static std::vector<Variant>* reg = [] {
+        auto* r = new std::vector<Variant>();
+        register_gemv_bf16(*r);
+        register_gemv_q4g64(*r);
+        register_gemm_mfma(*r);
+        return r;
+    }();
+    return *reg;
+}
+
+using Key = std::tuple<int, int, int64_t, int64_t, int64_t>;   // device, kind, M, N, K
+
+std::mutex g_mu;
+std::map<Key, int>& table() {   // value: index into registry()
+    static auto* t = new std::map<Key, int>();
+    return *t;
+}
+
+int pow2ceil(int64_t m) {
+    int p = 1;
+    while (p < m) p <<= 1;
+    return p;
+}
+
+bool same_cfg(const lin_config& a, const lin_config& b) {
+    return a.algo == b.algo && a.rows == b.rows && a.unroll == b.unroll && a.split == b.split &&
+           a.stage_x == b.stage_x && a.tile_m == b.tile_m;
+}
+
+bool applicable(const Variant& v, int kind, int64_t M, int64_t N, int64_t K) {
+    if (v.kind != kind) return false;
+    if (v.cfg.algo == LIN_ALGO_VALU) {
+        if (v.mt != pow2ceil(M)) return false;
+    } else {
+        if (M < v.min_m || K == 0) return false;
+    }
+    dim3 g;
+    size_t lds;
+    return v.geometry(v, (int)M, (int)N, (int)K, &g, &lds);
+}
+
+std::vector<int> candidates(int kind, int64_t M, int64_t N, int64_t K) {
+    std::vector<int> out;
+    const auto& reg = registry();
+    for (int i = 0; i < (int)reg.size(); ++i)
+        if (applicable(reg[i], kind, M, N, K)) out.push_back(i);
+    return out;
+}
+
+int find_variant(int kind, int64_t M, int64_t N, int64_t K, const lin_config& cfg) {
+    for (int i : candidates(kind, M, N, K))
+        if (same_cfg(registry()[i].cfg, cfg)) return i;
+    return -1;
+}
+
+// Built-in choice for shapes that were neither tuned nor pinned.
+int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
+    lin_config want{};
+    want.algo = LIN_ALGO_VALU;
+    want.tile_m = pow2ceil(M);
+    const int mt = want.tile_m;
+    if (kind == LIN_KIND_GEMV_Q4G64) {
+        want.rows = mt <= 1 ? 4 : (mt <= 4 ? 2 : 1);
+        want.unroll = 1;
+        want.split = N >= 4096 ? 1 : (N >= 1024 ? 2 : 4);
+    } else {
+        if (kind == LIN_KIND_SKINNY_BF16 && M > 16) {
+            // matrix cores, when a variant applies
+            for (int i : candidates(kind, M, N, K))
+                if (registry()[i].cfg.algo == LIN_ALGO_MFMA) return i;
+        }
+        want.rows = mt <= 1 ? (N >= 8192 ? 2 : 1) : (mt <= 8 ? 2 : 1);
+        want.unroll = mt <= 1 ? (want.rows == 1 ? 4 : 2) : (mt <= 8 ? 2 : 1);
+        if (mt == 4 || mt == 8) want.rows = 2, want.unroll = 2;
+        if (mt >= 16) want.rows = 1, want.unroll = (mt == 16 ? 2 : 1);
+        want.split = N >= 8192 ? 1 : (N >= 2048 ? 2 : 4);
+    }
+    want.stage_x = 0;
+    int i = find_variant(kind, M, N, K, want);
+    if (i >= 0) return i;
+    auto c = candidates(kind, M, N, K);
+    return c.empty() ? -1 : c.front();
+}
+
+int current_device() {
+    int d = 0;
+    if (hipGetDevice(&d) != hipSuccess) return -1;
+    return d;
+}
+
+std::map<Key, int>& default_cache() {   // built-in choices already worked out
+    static auto* t = new std::map<Key, int>();
+    return *t;
+}
+
+// Variant for the next call: tuned or pinned entry, else the (cached) default.
+int lookup(int kind, int64_t M, int64_t N, int64_t K) {
+    const int dev = current_device();
+    const Key key(dev, kind, M, N, K);
+    const Key dkey(0, kind, M, N, K);
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = table().find(key);
+        if (it != table().end()) return it->second;
+        auto dt = default_cache().find(dkey);
+        if (dt != default_cache().end()) return dt->second;
+    }
+    const int vi = default_variant(kind, M, N, K);
+    std::lock_guard<std::mutex> lk(g_mu);
+    default_cache()[dkey] = vi;
+    return vi;
+}
+
+int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
+                   hipEvent_t ev1 = nullptr) {
+    const Variant& v = registry()[vi];
+    dim3 grid;
+    size_t lds = 0;
+    if (!v.geometry(v, a.M, a.N, a.K, &grid, &lds)) return LIN_ERR_UNSUPPORTED;
+    KArgs args = a;
+    void* params[] = {(void*)&args};
+    hipError_t e;
+    if (ev0 || ev1)
+        e = hipExtLaunchKernel(v.func, grid, dim3(kBlock), params, lds, stream, ev0, ev1, 0);
+    else
+        e = hipLaunchKernel(v.func, grid, dim3(kBlock), params, lds, stream);
+    return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared argument checks.  Returns LIN_OK, a negative status, or 1 for an
+// empty call (nothing to do).
+int check(int kind, const void* W, const void* S, const void* x, const float* y, int64_t M,
+          int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K < 0) return LIN_ERR_SHAPE;
+    const int64_t maxm = kind == LIN_KIND_SKINNY_BF16 ? LIN_SKINNY_MAX_M : LIN_GEMV_MAX_M;
+    if (M > maxm || N > 0x7FFFFFFF || K > LIN_MAX_K) return LIN_ERR_SHAPE;
+    if (kind == LIN_KIND_GEMV_Q4G64 ? (K % 64) : (K % 8)) return LIN_ERR_SHAPE;
+    if (M == 0 || N == 0) return 1;
+    if (!y) return LIN_ERR_NULL;
+    if (K > 0 && (!W || !x || (kind == LIN_KIND_GEMV_Q4G64 && !S))) return LIN_ERR_NULL;
+    if (!aligned(y, 4)) return LIN_ERR_ALIGN;
+    if (K > 0) {
+        if (!aligned(W, 16) || !aligned(x, 16)) return LIN_ERR_ALIGN;
+        if (kind == LIN_KIND_GEMV_Q4G64 && !aligned(S, 2)) return LIN_ERR_ALIGN;
+    }
+    return LIN_OK;
+}
+
+int run(int kind, const void* W, const void* S, const void* x, float* y, int64_t M, int64_t N,
+        int64_t K, void* stream) {
+    int st = check(kind, W, S, x, y, M, N, K);
+    if (st != LIN_OK) return st > 0 ? LIN_OK : st;
+    const int vi = lookup(kind, M, N, K);
+    if (vi < 0) return LIN_ERR_UNSUPPORTED;
+    KArgs a{W, S, x, y, (int)M, (int)N, (int)K};
+    return launch_variant(vi, a, (hipStream_t)stream);
+}
+
+struct Flush {
+    void* buf = nullptr;
+    size_t bytes = 0;
+};
+std::map<int, Flush>& flushes() {
+    static auto* f = new std::map<int, Flush>();
+    return *f;
+}
+
+}  // namespace
+}  // namespace lin
+
+using namespace lin;
+
+extern "C" {
+
+int lin_version(void) { return (1 << 16) | 0; }
+
+const char* lin_status_string(int status) {
+    switch (status) {
+        case LIN_OK: return "ok";
+        case LIN_ERR_NULL: return "a required pointer is NULL";
+        case LIN_ERR_SHAPE: return "M, N or K out of range for this product";
+        case LIN_ERR_ALIGN: return "a pointer is not aligned as the product requires";
+        case LIN_ERR_UNSUPPORTED: return "configuration not available for this shape";
+        case LIN_ERR_HIP: return "the HIP runtime reported an error";
+        case LIN_ERR_ARG: return "invalid argument";
+        default: return "unknown status";
+    }
+}
+
+int lin_gemv_bf16(const void* W, const void* x, float* y, int64_t M, int64_t N, int64_t K,
+                  void* stream) {
+    return run(LIN_KIND_GEMV_BF16, W, nullptr, x, y, M, N, K, stream);
+}
+
+int lin_gemv_q4g64(const void* Wq, const void* S, const void* x, float* y, int64_t M, int64_t N,
+                   int64_t K, void* stream) {
+    return run(LIN_KIND_GEMV_Q4G64, Wq, S, x, y, M, N, K, stream);
+}
+
+int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y, int64_t M, int64_t N, int64_t K,
+                         void* stream) {
+    return run(LIN_KIND_SKINNY_BF16, W, nullptr, X, Y, M, N, K, stream);
+}
+
+int lin_num_candidates(int kind, int64_t M, int64_t N, int64_t K) {
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_BF16) return LIN_ERR_ARG;
+    int st = check(kind, (void*)16, (void*)16, (void*)16, (float*)16, M, N, K);
+    if (st < 0) return st;
+    if (st > 0) return 0;
+    return (int)candidates(kind, M, N, K).size();
+}
+
+int lin_candidate(int kind, int64_t M, int64_t N, int64_t K, int index, lin_config* out) {
+    if (!out) return LIN_ERR_NULL;
+    int n = lin_num_candidates(kind, M, N, K);
+    if (n < 0) return n;
+    if (index < 0 || index >= n) return LIN_ERR_ARG;
+    *out = registry()[candidates(kind, M, N, K)[index]].cfg;
+    out->us = 0.f;
+    return LIN_OK;
+}
+
+int lin_get_config(int kind, int64_t M, int64_t N, int64_t K, lin_config* out) {
+    if (!out) return LIN_ERR_NULL;
+    int n = lin_num_candidates(kind, M, N, K);
+    if (n < 0) return n;
+    if (n == 0) return LIN_ERR_UNSUPPORTED;
+    const int vi = lookup(kind, M, N, K);
+    if (vi < 0) return LIN_ERR_UNSUPPORTED;
+    *out = registry()[vi].cfg;
+    out->us = 0.f;
+    return LIN_OK;
+}
+
+int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg) {
+    int n = lin_num_candidates(kind, M, N, K);
+    if (n < 0) return n;
+    const int dev = current_device();
+    if (dev < 0) return LIN_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!cfg) {
+        table().erase(Key(dev, kind, M, N, K));
+        return LIN_OK;
+    }
+    const int vi = find_variant(kind, M, N, K, *cfg);
+    if (vi < 0) return LIN_ERR_UNSUPPORTED;
+    table()[Key(dev, kind, M, N, K)] = vi;
+    return LIN_OK;
+}
+
+int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, void* stream) {
+    if (N < 0 || K < 0 || N > 0x7FFFFFFF || K > LIN_MAX_K || K % 64) return LIN_ERR_SHAPE;
+    if (N == 0 || K == 0) return LIN_OK;
+    if (!W || !Wq || !S) return LIN_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(S, 2)) return LIN_ERR_ALIGN;
+    hipError_t e = launch_quantize_q4g64(W, Wq, S, (int)N, (int)K, (hipStream_t)stream);
+    return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
+}
+
+int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y, int64_t M,
+                 int64_t N, int64_t K, void* stream, lin_config* out) {
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_BF16) return LIN_ERR_ARG;
+    int st = check(kind, W, S, x, y, M, N, K);
+    if (st < 0) return st;
+    if (st > 0) return LIN_OK;
+    const auto cand = candidates(kind, M, N, K);
+    if (cand.empty()) return LIN_ERR_UNSUPPORTED;
+    const int dev = current_device();
+    if (dev < 0) return LIN_ERR_HIP;
+    hipStream_t s = (hipStream_t)stream;
+
+    // A buffer larger than the last-level caches (4 MB L2 per XCD, 256 MB
+    // Infinity Cache); writing it before each timed call evicts the weights.
+    const size_t flush_bytes = (size_t)512 << 20;
+    Flush* fl;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        fl = &flushes()[dev];
+        if (!fl->buf) {
+            if (hipMalloc(&fl->buf, flush_bytes) != hipSuccess) {
+                fl->buf = nullptr;
+                return LIN_ERR_HIP;
+            }
+            fl->bytes = flush_bytes;
+        }
+    }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return LIN_ERR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return LIN_ERR_HIP;
+    }
+    KArgs a{W, S, x, y, (int)M, (int)N, (int)K};
+    const int reps = 7;
+    int best = -1;
+    float best_us = 0.f;
+    int rc = LIN_OK;
+    uint32_t salt = 1;
+    for (int vi : cand) {
+        std::vector<float> t;
+        if ((rc = launch_variant(vi, a, s)) != LIN_OK) break;   // warm-up (code load)
+        for (int r = 0; r < reps && rc == LIN_OK; ++r) {
+            if (launch_flush(fl->buf, fl->bytes / 16, salt++, s) != hipSuccess) {
+                rc = LIN_ERR_HIP;
+                break;
+            }
+            if ((rc = launch_variant(vi, a, s, e0, e1)) != LIN_OK) break;
+            if (hipEventSynchronize(e1) != hipSuccess) {
+                rc = LIN_ERR_HIP;
+                break;
+            }
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+                rc = LIN_ERR_HIP;
+                break;
+            }
+            t.push_back(ms * 1000.f);
+        }
+        if (rc != LIN_OK) break;
+        std::sort(t.begin(), t.end());
+        const float med = t[t.size() / 2];
+        if (best < 0 || med < best_us) {
+            best = vi;
+            best_us = med;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (rc != LIN_OK) return rc;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        table()[Key(dev, kind, M, N, K)] = best;
+    }
+    if (out) {
+        *out = registry()[best].cfg;
+        out->us = best_us;
+    }
+    return LIN_OK;
+}
+
+}  // extern "C"

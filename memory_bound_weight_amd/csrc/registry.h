@@ -1,0 +1,39 @@
+// Kernel variants known to the host library.  Each kernel source file appends
+// its instantiations to the registry; the C-ABI layer picks one per call.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/lin.h"
+#include "kern_common.h"
+
+namespace lin {
+
+struct Variant {
+    int kind;          // LIN_KIND_*
+    lin_config cfg;    // public description (algo, rows, unroll, split, stage_x, tile_m)
+    int mt;            // VALU: tokens per instance (M <= mt); MFMA: 0 (any M in range)
+    int min_m;         // smallest M this variant accepts
+    const void* func;  // __global__ function
+    // Workgroups and dynamic LDS bytes for a shape; returns false if the shape
+    // does not fit this variant (for example LDS too small for K).
+    bool (*geometry)(const Variant&, int M, int N, int K, dim3* grid, size_t* lds);
+};
+
+void register_gemv_bf16(std::vector<Variant>& out);
+void register_gemv_q4g64(std::vector<Variant>& out);
+void register_gemm_mfma(std::vector<Variant>& out);
+
+// Quantiser launch (int4-g64 weight preparation).
+hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream);
+
+// Cache-flush kernel used while tuning: writes n 16-byte words.
+hipError_t launch_flush(void* buf, size_t n16, uint32_t salt, hipStream_t stream);
+
+constexpr size_t kMaxDynLds = 64 * 1024;
+
+}  // namespace lin

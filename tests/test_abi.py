@@ -1,0 +1,111 @@
+"""The C-ABI library loads, exports every symbol include/lin.h declares, and
+rejects invalid arguments before touching the GPU.  CPU only: every call here
+returns from argument validation, no kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bound_weight_amd as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "lin.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(lin_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _header_functions()
+    assert len(names) >= 10
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.EXPORTS) == names
+
+
+def test_version_and_status_strings():
+    assert L.lin_version() >> 16 == 1
+    for st in (L.LIN_OK, L.LIN_ERR_NULL, L.LIN_ERR_SHAPE, L.LIN_ERR_ALIGN,
+               L.LIN_ERR_UNSUPPORTED, L.LIN_ERR_HIP, L.LIN_ERR_ARG):
+        assert L.status_string(st) != "unknown status"
+    assert L.status_string(12345) == "unknown status"
+
+
+P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
+
+
+@pytest.mark.parametrize("fn,args,expect", [
+    # shape checks come first
+    ("lin_gemv_bf16", (P, P, P, -1, 8, 8, None), L.LIN_ERR_SHAPE),
+    ("lin_gemv_bf16", (P, P, P, 9, 8, 8, None), L.LIN_ERR_SHAPE),
+    ("lin_gemv_bf16", (P, P, P, 1, 8, 12, None), L.LIN_ERR_SHAPE),
+    ("lin_gemv_bf16", (P, P, P, 1, 1 << 31, 8, None), L.LIN_ERR_SHAPE),
+    ("lin_gemv_bf16", (P, P, P, 1, 8, (1 << 22) + 8, None), L.LIN_ERR_SHAPE),
+    ("lin_gemv_q4g64", (P, P, P, P, 1, 8, 96, None), L.LIN_ERR_SHAPE),
+    ("lin_gemm_skinny_bf16", (P, P, P, 257, 8, 8, None), L.LIN_ERR_SHAPE),
+    # empty calls succeed without pointers
+    ("lin_gemv_bf16", (None, None, None, 0, 8, 8, None), L.LIN_OK),
+    ("lin_gemv_bf16", (None, None, None, 1, 0, 8, None), L.LIN_OK),
+    ("lin_gemv_q4g64", (None, None, None, None, 0, 0, 64, None), L.LIN_OK),
+    ("lin_gemm_skinny_bf16", (None, None, None, 0, 0, 0, None), L.LIN_OK),
+    # null pointers
+    ("lin_gemv_bf16", (P, P, None, 1, 8, 8, None), L.LIN_ERR_NULL),
+    ("lin_gemv_bf16", (None, P, P, 1, 8, 8, None), L.LIN_ERR_NULL),
+    ("lin_gemv_bf16", (P, None, P, 1, 8, 8, None), L.LIN_ERR_NULL),
+    ("lin_gemv_q4g64", (P, None, P, P, 1, 8, 64, None), L.LIN_ERR_NULL),
+    ("lin_gemm_skinny_bf16", (P, P, None, 4, 8, 8, None), L.LIN_ERR_NULL),
+    # alignment
+    ("lin_gemv_bf16", (P + 8, P, P, 1, 8, 8, None), L.LIN_ERR_ALIGN),
+    ("lin_gemv_bf16", (P, P + 2, P, 1, 8, 8, None), L.LIN_ERR_ALIGN),
+    ("lin_gemv_bf16", (P, P, P + 2, 1, 8, 8, None), L.LIN_ERR_ALIGN),
+    ("lin_gemv_q4g64", (P, P + 1, P, P, 1, 8, 64, None), L.LIN_ERR_ALIGN),
+    ("lin_gemm_skinny_bf16", (P + 4, P, P, 4, 8, 8, None), L.LIN_ERR_ALIGN),
+])
+def test_argument_validation(fn, args, expect):
+    assert getattr(L._lib, fn)(*args) == expect
+
+
+def test_quantizer_validation():
+    q = L._lib.lin_quantize_q4g64
+    assert q(P, P, P, 4, 96, None) == L.LIN_ERR_SHAPE
+    assert q(P, P, P, -1, 64, None) == L.LIN_ERR_SHAPE
+    assert q(None, None, None, 0, 64, None) == L.LIN_OK
+    assert q(None, P, P, 4, 64, None) == L.LIN_ERR_NULL
+    assert q(P + 8, P, P, 4, 64, None) == L.LIN_ERR_ALIGN
+    assert q(P, P, P + 1, 4, 64, None) == L.LIN_ERR_ALIGN
+
+
+def test_autotune_validation():
+    cfg = L.LinConfig()
+    t = L._lib.lin_autotune
+    assert t(7, P, P, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
+    assert t(0, P, None, P, P, 9, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_SHAPE
+    assert t(1, P, None, P, P, 1, 8, 64, None, ctypes.byref(cfg)) == L.LIN_ERR_NULL
+    assert t(0, None, None, None, None, 0, 8, 8, None, ctypes.byref(cfg)) == L.LIN_OK
+
+
+def test_candidate_enumeration():
+    for kind, M, N, K in [(0, 1, 2048, 2048), (0, 8, 512, 3584), (1, 1, 2048, 2048),
+                          (1, 3, 512, 18944), (2, 8, 4096, 4096), (2, 17, 1024, 4096)]:
+        n = L.lin_num_candidates(kind, M, N, K)
+        assert n > 0
+        cands = L.lin_candidates(kind, M, N, K)
+        assert len(cands) == n
+        keys = {tuple(sorted((k, v) for k, v in c.items() if k != "us")) for c in cands}
+        assert len(keys) == n                       # no duplicates
+        for c in cands:
+            assert c["algo"] in (L.LIN_ALGO_VALU, L.LIN_ALGO_MFMA)
+            if c["algo"] == L.LIN_ALGO_VALU:
+                assert c["tile_m"] >= M and c["tile_m"] < 2 * M or (M == 1 and c["tile_m"] == 1)
+        assert L.lin_get_config(kind, M, N, K) in [dict(c, us=0.0) for c in cands]
+    # staged x in LDS is only offered while it fits
+    big = L.lin_candidates(0, 8, 4096, 14336)
+    assert not any(c["stage_x"] for c in big)
+    with pytest.raises(L.LinError):
+        L.lin_candidate(0, 1, 8, 8, 10 ** 6)
+    assert L._lib.lin_num_candidates(0, 1, 8, 12) == L.LIN_ERR_SHAPE
+    assert L._lib.lin_num_candidates(5, 1, 8, 8) == L.LIN_ERR_ARG

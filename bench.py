@@ -49,17 +49,26 @@ def bytes_q4(N, K, M=1):
 # ---------------------------------------------------------------- weight sets
 
 class Mat:
-    def __init__(self, name, layer, idx, N, K):
-        self.name, self.layer, self.idx, self.N, self.K = name, layer, idx, N, K
+    """One launch: a matrix (or load-time concatenation of matrices sharing x)."""
+
+    def __init__(self, name, layer, N, K):
+        self.name, self.layer, self.N, self.K = name, layer, N, K
 
 
-def build_set(model, fmt, dev):
-    """Matrices of one decode step, each with its own seeded weights and x."""
+def build_set(model, fmt, dev, fused=True):
+    """Matrices of one decode step, each part with its own seeded weights; one
+    seeded x per launch group."""
     mats = []
-    for layer, idx, name, N, K in synth.decode_matrices(model):
-        m = Mat(name, layer, idx, N, K)
-        W = synth.weight(model["seed"], layer, idx, N, K, device=dev)
-        m.x = synth.activation(model["seed"], layer, idx, 1, K, device=dev)
+    for layer, parts in synth.decode_groups(model, fused):
+        K = parts[0][3]
+        N = sum(p[2] for p in parts)
+        m = Mat("|".join(p[1] for p in parts), layer, N, K)
+        W = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+        r = 0
+        for idx, name, n, k in parts:
+            W[r:r + n] = synth.weight(model["seed"], layer, idx, n, k, device=dev)
+            r += n
+        m.x = synth.activation(model["seed"], layer, parts[0][0], 1, K, device=dev)
         m.y = torch.empty((1, N), dtype=torch.float32, device=dev)
         if fmt == "bf16":
             m.W = W
@@ -85,12 +94,17 @@ def kind_of(m):
     return L.LIN_KIND_GEMV_BF16 if m.fmt == "bf16" else L.LIN_KIND_GEMV_Q4G64
 
 
-def autotune(mats):
-    """Load-time tuning: once per distinct (format, N, K), on that shape's first matrix."""
+def tune_key(m):
+    return (kind_of(m), 1, m.N, m.K)
+
+
+def autotune(mats, only=None):
+    """Load-time tuning: once per distinct (format, N, K), on that shape's first
+    matrix; returns {tune key: config}."""
     seen = {}
     for m in mats:
-        key = (m.fmt, m.N, m.K)
-        if key in seen:
+        key = tune_key(m)
+        if key in seen or (only is not None and key not in only):
             continue
         if m.fmt == "bf16":
             cfg = L.lin_autotune(L.LIN_KIND_GEMV_BF16, m.W, m.x, m.y)
@@ -99,6 +113,22 @@ def autotune(mats):
         seen[key] = cfg
         log("tuned %-5s %6d x %-6d -> %s" % (m.fmt, m.N, m.K, cfg))
     return seen
+
+
+def apply_tuning(mats, path, retune):
+    """Use the persisted tuning table (tuned once with lin_autotune on MI355X);
+    shapes it does not cover, or all shapes with retune, are tuned now."""
+    keys = {tune_key(m) for m in mats}
+    if retune or not os.path.exists(path):
+        entries = autotune(mats)
+        L.save_tuning(path, entries)
+        return "tuned now (%d shapes), saved to %s" % (len(entries), os.path.relpath(path, ROOT))
+    ok, stale = L.load_tuning(path)
+    missing = keys - set(ok)
+    if missing:
+        autotune(mats, only=missing)
+    return "loaded %s (%d shapes%s)" % (os.path.relpath(path, ROOT), len(keys - missing),
+                                        ", %d re-tuned" % len(missing) if missing else "")
 
 
 def capture(mats):
@@ -136,31 +166,66 @@ def time_graph(g, steps, warmup):
 
 def variant_key(m):
     c = L.lin_get_config(kind_of(m), 1, m.N, m.K)
-    return "%s R%d U%d S%d X%d" % (m.fmt, c["rows"], c["unroll"], c["split"], c["stage_x"])
+    return "%s R%d U%d S%d X%d" % ("gemv_bf16" if m.fmt == "bf16" else "gemv_q4g64",
+                                   c["rows"], c["unroll"], c["split"], c["stage_x"])
 
 
-def kernel_durations(mats, reps=3):
-    """Per-launch durations with HIP events on the launch stream (torch's current
-    stream, which the binding passes to the library), grouped by kernel variant."""
-    per = {}
-    stream = torch.cuda.current_stream()
-    for _ in range(reps):
-        evs = []
-        for m in mats:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            launch(m)
-            b.record(stream)
-            evs.append((m, a, b))
+def kernel_times(mats, reps):
+    """Average duration per launch of each kernel variant, measured live with HIP
+    events around graph replays that hold only that variant's launches (in step
+    order).  Queued kernels start as the previous one ends, so elapsed time /
+    launches is the kernel's own duration."""
+    by = {}
+    for m in mats:
+        by.setdefault(variant_key(m), []).append(m)
+    out = {}
+    for key, ms in by.items():
+        rep = max(1, -(-64 // len(ms)))   # at least 64 launches per replay
+        g = capture(ms * rep)
+        for _ in range(2):
+            g.replay()
         torch.cuda.synchronize()
-        for m, a, b in evs:
-            d = per.setdefault(variant_key(m), {"t": 0.0, "bytes": 0, "n": 0, "shapes": set()})
-            d["t"] += a.elapsed_time(b) / 1000.0
-            d["bytes"] += m.bytes
-            d["n"] += 1
-            d["shapes"].add("%dx%d" % (m.N, m.K))
-    return per
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_launch = e0.elapsed_time(e1) / 1000.0 / (reps * rep * len(ms))
+        nbytes = sum(m.bytes for m in ms)
+        mix = {}
+        for m in ms:
+            mix["%dx%d" % (m.N, m.K)] = mix.get("%dx%d" % (m.N, m.K), 0) + 1
+        out[key] = {"avg_s": per_launch, "launches": len(ms), "bytes_per_launch": nbytes / len(ms),
+                    "step_s": per_launch * len(ms), "shapes": sorted(mix), "mix": mix}
+    return out
+
+
+def measured_traffic(key, shapes_mix):
+    """HBM bytes per launch of kernel variant `key` over the step's shape mix,
+    from the counter table, or None if none was taken for the current source."""
+    import hashlib
+    path = os.path.join(L.TUNING_DIR, "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)["measured"]
+    for e in table:
+        if e["kernel"] != key:
+            continue
+        src = b"".join(open(os.path.join(os.path.dirname(L.__file__), p), "rb").read()
+                       for p in e["sources"])
+        if hashlib.sha256(src).hexdigest()[:16] != e["src_sha256_16"]:
+            return None
+        tot, n = 0, 0
+        for shape, count in shapes_mix.items():
+            if shape not in e["per_shape"]:
+                return None
+            tot += count * (e["per_shape"][shape]["fetch_bytes"] + e["per_shape"][shape]["write_bytes"])
+            n += count
+        return int(tot / n)
+    return None
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -211,9 +276,16 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyllama", choices=["tinyllama", "qwen7b"])
-    ap.add_argument("--no-tune", action="store_true")
+    ap.add_argument("--tune", action="store_true",
+                    help="re-run lin_autotune for every shape and rewrite the tuning table")
+    ap.add_argument("--tuning", default=None, help="tuning table path")
+    ap.add_argument("--no-fuse", action="store_true",
+                    help="one launch per matrix instead of q|k|v and gate|up concatenated")
     ap.add_argument("--cpu-layers", type=int, default=4)
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES three times (scales the HBM "
+                         "byte counters of a profiler run) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the decode-step linear layer is built and timed on a "
@@ -222,11 +294,23 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
     model = synth.TINYLLAMA if args.workload == "tinyllama" else synth.QWEN7B
     log("building %s weight sets on %s" % (model["name"], torch.cuda.get_device_name(dev)))
-    sets = {f: build_set(model, f, dev) for f in ("bf16", "q4")}
+    fused = not args.no_fuse
+    sets = {f: build_set(model, f, dev, fused) for f in ("bf16", "q4")}
     allm = sets["bf16"] + sets["q4"]
-    tuned = {} if args.no_tune else autotune(allm)
+    tfile = args.tuning or os.path.join(L.TUNING_DIR, "%s.json" % model["name"])
+    tuning = apply_tuning(allm, tfile, args.tune)
+    log("tuning: " + tuning)
 
     graphs = {f: capture(sets[f]) for f in sets}
     g_all = capture(allm)
@@ -244,27 +328,33 @@ def main():
     step_bytes = sum(m.bytes for m in allm)
     gbs = step_bytes / wall / 1e9
 
-    per = kernel_durations(allm)
-    dom_key = max(per, key=lambda k: per[k]["t"])
-    dom = per[dom_key]
-    achieved = dom["bytes"] / dom["t"] / 1e9
+    kt = kernel_times(allm, reps=max(5, args.steps // 2))
+    dom_key = max(kt, key=lambda k: kt[k]["step_s"])
+    dom = kt[dom_key]
+    achieved = dom["bytes_per_launch"] / dom["avg_s"] / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": dom_key, "launches": dom["n"], "shapes": sorted(dom["shapes"]),
-                "avg_launch_us": round(dom["t"] / dom["n"] * 1e6, 3),
-                "bytes_per_launch": int(dom["bytes"] / dom["n"])}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom_key, dom["mix"]),
+                "kernel": dom_key, "launches_per_step": dom["launches"], "shapes": dom["shapes"],
+                "avg_launch_us": round(dom["avg_s"] * 1e6, 3),
+                "bytes_per_launch": int(dom["bytes_per_launch"]),
+                "share_of_step": round(dom["step_s"] / gpu, 3)}
+    kernels = {k: {"avg_us": round(v["avg_s"] * 1e6, 3), "launches": v["launches"],
+                   "GB_s": round(v["bytes_per_launch"] / v["avg_s"] / 1e9, 1)}
+               for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["step_s"])}
 
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
            "dtype": "bf16 and int4-g64 weights, bf16 x, fp32 accumulate", "data": "synthetic",
-           "config": {"workload": "%s decode weight set, batch 1, bf16 + int4-g64 (%d matrices each)"
-                      % (model["name"], len(sets["bf16"])), "batch": 1,
-                      "matrices_per_step": len(allm), "bytes_per_step": step_bytes,
-                      "tuned": not args.no_tune},
+           "config": {"workload": "%s decode weight set, batch 1, bf16 + int4-g64 (%d matrices "
+                      "each%s)" % (model["name"], len(synth.decode_groups(model, False)),
+                                   ", q|k|v and gate|up concatenated at load" if fused else ""),
+                      "batch": 1, "launches_per_step": len(allm), "bytes_per_step": step_bytes,
+                      "fused_projections": fused, "tuning": tuning},
            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
            "gpu_ms_per_step": round(gpu * 1e3, 4),
-           "per_format": per_fmt, "roofline": roofline}
+           "per_format": per_fmt, "kernels": kernels, "roofline": roofline}
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline(model, args.cpu_layers, min(16, os.cpu_count() or 1))
     print(json.dumps(out), flush=True)

@@ -8,6 +8,7 @@ library must have been built (``__graft_entry__.build()`` or
 ``python memory_bound_weight_amd/build.py``); importing fails loudly otherwise.
 """
 import ctypes
+import json
 import os
 
 import torch
@@ -241,3 +242,34 @@ def lin_set_config(kind, M, N, K, cfg):
     """Pin cfg (a dict from lin_candidate) for this shape; None removes the entry."""
     p = ctypes.byref(LinConfig.from_dict(cfg)) if cfg is not None else None
     _check(_lib.lin_set_config(int(kind), M, N, K, p), "lin_set_config")
+
+
+# ---------------------------------------------------------------- tuning table files
+
+TUNING_DIR = os.path.join(_HERE, "tuning")
+
+
+def save_tuning(path, entries):
+    """Persist tuned configurations: entries = {(kind, M, N, K): cfg dict}."""
+    rows = [dict(kind=k[0], M=k[1], N=k[2], K=k[3], cfg={f: v[f] for f in
+            ("algo", "rows", "unroll", "split", "stage_x", "tile_m", "us")})
+            for k, v in sorted(entries.items())]
+    with open(path, "w") as f:
+        json.dump({"device": torch.cuda.get_device_name(0) if torch.cuda.is_available() else "",
+                   "version": lin_version(), "entries": rows}, f, indent=1)
+
+
+def load_tuning(path):
+    """Pin every configuration of a tuning file that this library still offers;
+    returns the keys applied and the keys that no longer match a candidate."""
+    with open(path) as f:
+        data = json.load(f)
+    ok, stale = [], []
+    for e in data["entries"]:
+        key = (e["kind"], e["M"], e["N"], e["K"])
+        try:
+            lin_set_config(*key, e["cfg"])
+            ok.append(key)
+        except LinError:
+            stale.append(key)
+    return ok, stale

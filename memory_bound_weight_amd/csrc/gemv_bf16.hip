@@ -7,12 +7,13 @@
 // rows; its 64 lanes read consecutive 16-byte chunks of each row (eight bf16),
 // so one wavefront load instruction covers 1 KiB of a row, and a lane keeps
 // U x R independent loads in flight (tinyinfer post, "v0.2": several rows per
-// warp keep more requests in flight).  With SPLIT > 1, SPLIT wavefronts share
-// the same rows, each taking a contiguous part of K, and combine through LDS;
-// this fills the chip when N is small.  x is read from the cache hierarchy, or
-// staged in LDS once per workgroup when STAGE is set.  Products use
-// v_dot2_f32_bf16 (two exact bf16 products per instruction, fp32 sums); each
-// lane sums K/512 chunks, then a permlane/DPP tree sums the 64 lanes.
+// warp keep more requests in flight).  The loop is software-pipelined: the
+// loads of step i+1 are issued before the products of step i.  With SPLIT > 1,
+// SPLIT wavefronts share the same rows, each taking a contiguous part of K, and
+// combine through LDS; this fills the chip when N is small.  x is read through
+// the cache hierarchy, or staged in LDS once per workgroup when STAGE is set.
+// Products use v_dot2_f32_bf16 (two exact bf16 products per instruction, fp32
+// sums); each lane sums K/512 chunks, then a permlane/DPP tree sums the lanes.
 #include "registry.h"
 
 namespace lin {
@@ -21,8 +22,9 @@ template <int MT, int R, int U, int SPLIT, bool STAGE>
 __global__ __launch_bounds__(kBlock) void gemv_bf16_valu(KArgs a) {
     constexpr int GROUPS = 4 / SPLIT;
     constexpr int V = R * MT;
+    constexpr int STEP = kWave * U;   // chunks per pipeline step
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int grp = wave / SPLIT;
     const int part = wave - grp * SPLIT;
     const int M = a.M, N = a.N, K = a.K;
@@ -36,22 +38,22 @@ __global__ __launch_bounds__(kBlock) void gemv_bf16_valu(KArgs a) {
             const int m = i / nch;
             const int c = i - m * nch;
             const int mm = m < M ? m : 0;
-            xs[i] = load_x16((const u32x4*)(X + (size_t)mm * K) + c);
+            xs[i] = load_x16((const uint8_t*)(X + (size_t)mm * K), (uint32_t)c * 16u);
         }
         __syncthreads();
     }
 
     const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * R;
-    const u32x4* wp[R];
+    const uint8_t* wb[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         int64_t row = row0 + r;
         row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
-        wp[r] = (const u32x4*)(W + row * (int64_t)K);
+        wb[r] = (const uint8_t*)(W + row * (int64_t)K);
     }
-    const u32x4* xp[MT];
+    const uint8_t* xb[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) xp[m] = (const u32x4*)(X + (size_t)(m < M ? m : 0) * K);
+    for (int m = 0; m < MT; ++m) xb[m] = (const uint8_t*)(X + (size_t)(m < M ? m : 0) * K);
 
     const int per = (nch + SPLIT - 1) / SPLIT;
     const int cbeg = part * per;
@@ -61,46 +63,69 @@ __global__ __launch_bounds__(kBlock) void gemv_bf16_valu(KArgs a) {
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
 
-    int cb = cbeg;
-    for (; cb + kWave * U <= cend; cb += kWave * U) {
+    struct Stage {
         u32x4 w[U][R];
-        u32x4 xv[U][MT];
+        u32x4 x[U][MT];
+    };
+    auto load = [&](Stage& s, int cb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t off = (uint32_t)(cb + kWave * u + lane) * 16u;
+#pragma unroll
+            for (int r = 0; r < R; ++r) s.w[u][r] = load_w16(wb[r], off);
+            if constexpr (!STAGE) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m) s.x[u][m] = load_x16(xb[m], off);
+            }
+        }
+    };
+    auto compute = [&](const Stage& s, int cb) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int r = 0; r < R; ++r) w[u][r] = load_w16(wp[r] + cb + kWave * u + lane);
+            for (int m = 0; m < MT; ++m) {
+                const u32x4 xv = STAGE ? xs[m * nch + cb + kWave * u + lane] : s.x[u][m];
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-                xv[u][m] = STAGE ? xs[m * nch + cb + kWave * u + lane]
-                                 : load_x16(xp[m] + cb + kWave * u + lane);
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[r * MT + m] = dot2(w[u][r][j], xv[u][m][j], acc[r * MT + m]);
+                        acc[r * MT + m] = dot2(s.w[u][r][j], xv[j], acc[r * MT + m]);
+            }
+    };
+
+    // full steps, two register stages in flight (unrolled by two: no copies)
+    const int nfull = (cend - cbeg) / STEP;
+    int cb = cbeg;
+    if (nfull > 0) {
+        Stage s0, s1;
+        load(s0, cb);
+        for (int it = 0;;) {
+            if (it + 1 < nfull) load(s1, cb + STEP);
+            compute(s0, cb);
+            cb += STEP;
+            if (++it >= nfull) break;
+            if (it + 1 < nfull) load(s0, cb + STEP);
+            compute(s1, cb);
+            cb += STEP;
+            if (++it >= nfull) break;
+        }
     }
     for (; cb < cend; cb += kWave) {   // ragged tail: one chunk per lane at most
         const int c = cb + lane;
         if (c < cend) {
+            const uint32_t off = (uint32_t)c * 16u;
             u32x4 w[R];
-            u32x4 xv[MT];
 #pragma unroll
-            for (int r = 0; r < R; ++r) w[r] = load_w16(wp[r] + c);
+            for (int r = 0; r < R; ++r) w[r] = load_w16(wb[r], off);
 #pragma unroll
-            for (int m = 0; m < MT; ++m) xv[m] = STAGE ? xs[m * nch + c] : load_x16(xp[m] + c);
+            for (int m = 0; m < MT; ++m) {
+                const u32x4 xv = STAGE ? xs[m * nch + c] : load_x16(xb[m], off);
 #pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
+                for (int r = 0; r < R; ++r)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[r * MT + m] = dot2(w[r][j], xv[m][j], acc[r * MT + m]);
+                        acc[r * MT + m] = dot2(w[r][j], xv[j], acc[r * MT + m]);
+            }
         }
     }
 
@@ -170,36 +195,34 @@ static void add_splits(std::vector<Variant>& out) {
 }
 
 void register_gemv_bf16(std::vector<Variant>& out) {
+    add_splits<1, 1, 2>(out);
     add_splits<1, 1, 4>(out);
-    add_splits<1, 1, 8>(out);
+    add_splits<1, 2, 1>(out);
     add_splits<1, 2, 2>(out);
     add_splits<1, 2, 4>(out);
     add_splits<1, 4, 1>(out);
     add_splits<1, 4, 2>(out);
     add_splits<1, 8, 1>(out);
 
-    add_splits<2, 1, 4>(out);
+    add_splits<2, 1, 2>(out);
+    add_splits<2, 2, 1>(out);
     add_splits<2, 2, 2>(out);
-    add_splits<2, 4, 2>(out);
-    add_splits<2, 8, 1>(out);
+    add_splits<2, 4, 1>(out);
 
-    add_splits<4, 1, 4>(out);
+    add_splits<4, 1, 2>(out);
+    add_splits<4, 2, 1>(out);
     add_splits<4, 2, 2>(out);
     add_splits<4, 4, 1>(out);
-    add_splits<4, 4, 2>(out);
 
+    add_splits<8, 1, 1>(out);
     add_splits<8, 1, 2>(out);
-    add_splits<8, 1, 4>(out);
-    add_splits<8, 2, 2>(out);
+    add_splits<8, 2, 1>(out);
     add_splits<8, 4, 1>(out);
 
-    add_splits<16, 1, 2>(out);
+    add_splits<16, 1, 1>(out);
     add_splits<16, 2, 1>(out);
-    add_splits<16, 4, 1>(out);
 
     add_splits<32, 1, 1>(out);
-    add_splits<32, 1, 2>(out);
-    add_splits<32, 2, 1>(out);
 }
 
 }  // namespace lin

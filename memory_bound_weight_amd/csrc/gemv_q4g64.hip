@@ -8,16 +8,16 @@
 // R rows, each lane reads consecutive 16-byte chunks = 32 codes = half a scale
 // group, so lanes 2i and 2i+1 share one scale.
 //
-// Unpacking without conversions.  After XOR 0x88888888 every nibble holds
-// n' = q + 8 in [0, 15].  (n' | 0x4300) read as bf16 is exactly 128 + n' =
-// q + 136, so one AND-OR per pair of nibbles yields two bf16 "codes" that go
-// straight into v_dot2_f32_bf16.  Masking 0x000F000F after shifting a dword by
+// Unpacking without conversions.  Flipping bit 3 of a nibble turns the two's
+// complement code q into n' = q + 8 in [0, 15], and (n' | 0x4300) read as bf16
+// is exactly 128 + n' = q + 136, so one 3-input bitwise operation per pair of
+// nibbles yields two bf16 "codes" that go straight into v_dot2_f32_bf16.  Masking 0x000F000F after shifting a dword by
 // 0, 4, 8, 12 pairs nibble i with nibble i+4, i.e. k = 8d+i with k = 8d+i+4,
 // so x is re-paired the same way (one v_perm per pair).  The offset is removed
 // per chunk: sum_k q x = dot(codes, x) - 136 * sum_k x, where sum_k x over the
 // chunk is shared by all rows; the dot chain starts from -136 * sum x.  Then
-// acc += s * chunk sum.  Per 32 weights and row: 4 XOR + 28 unpack + 16 dot2 +
-// 2 for the scale, about 1.6 vector operations per weight.
+// acc += s * chunk sum.  Per 32 weights and row: 28 unpack + 16 dot2 + 1 for
+// the scale, about 1.4 vector operations per weight.
 //
 // x handling: either re-paired from cached global loads per chunk (cost shared
 // by the R rows), or, with STAGE, re-paired once per workgroup into LDS as
@@ -52,15 +52,19 @@ __device__ __forceinline__ void pair_x(const u32x4 (&xd)[4], XChunk& out) {
 }
 
 // Sum over one chunk of 32 codes times re-paired x, minus the code offset.
+// ((w >> 4i) & 0x000F000F) ^ 0x43084308 equals ((w ^ 0x88888888) >> 4i &
+// 0x000F000F) | 0x43004300: the sign flip and the bf16 exponent bits go in with
+// one 3-input bitwise operation (v_bitop3_b32), plus one shift for i > 0.
 __device__ __forceinline__ float chunk_dot(const u32x4& wq, const XChunk& xc) {
+    constexpr uint32_t M = 0x000F000Fu, C = 0x43084308u;
     float acc = xc.negsum;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const uint32_t w = wq[d] ^ 0x88888888u;
-        acc = dot2((w & 0x000F000Fu) | 0x43004300u, xc.v[d][0], acc);
-        acc = dot2(((w >> 4) & 0x000F000Fu) | 0x43004300u, xc.v[d][1], acc);
-        acc = dot2(((w >> 8) & 0x000F000Fu) | 0x43004300u, xc.v[d][2], acc);
-        acc = dot2(((w >> 12) & 0x000F000Fu) | 0x43004300u, xc.v[d][3], acc);
+        const uint32_t w = wq[d];
+        acc = dot2((w & M) ^ C, xc.v[d][0], acc);
+        acc = dot2(((w >> 4) & M) ^ C, xc.v[d][1], acc);
+        acc = dot2(((w >> 8) & M) ^ C, xc.v[d][2], acc);
+        acc = dot2(((w >> 12) & M) ^ C, xc.v[d][3], acc);
     }
     return acc;
 }
@@ -73,8 +77,9 @@ template <int MT, int R, int U, int SPLIT, bool STAGE>
 __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
     constexpr int GROUPS = 4 / SPLIT;
     constexpr int V = R * MT;
+    constexpr int STEP = kWave * U;   // chunks per pipeline step
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const int grp = wave / SPLIT;
     const int part = wave - grp * SPLIT;
     const int M = a.M, N = a.N, K = a.K;
@@ -91,10 +96,10 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
             const int m = i / nch;
             const int c = i - m * nch;
             const int mm = m < M ? m : 0;
-            const u32x4* src = (const u32x4*)(X + (size_t)mm * K) + 4 * c;
+            const uint8_t* src = (const uint8_t*)(X + (size_t)mm * K);
             u32x4 xd[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) xd[t] = load_x16(src + t);
+            for (int t = 0; t < 4; ++t) xd[t] = load_x16(src, (uint32_t)(4 * c + t) * 16u);
             XChunk xc;
             pair_x(xd, xc);
 #pragma unroll
@@ -105,18 +110,18 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
     }
 
     const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * R;
-    const u32x4* wp[R];
-    const uint16_t* sp[R];
+    const uint8_t* wb[R];
+    const uint8_t* sb[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         int64_t row = row0 + r;
-        row = row < N ? row : N - 1;
-        wp[r] = (const u32x4*)(Wq + row * (int64_t)(K / 2));
-        sp[r] = S + row * (int64_t)G;
+        row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
+        wb[r] = Wq + row * (int64_t)(K / 2);
+        sb[r] = (const uint8_t*)(S + row * (int64_t)G);
     }
-    const u32x4* xp[MT];
+    const uint8_t* xb[MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) xp[m] = (const u32x4*)(X + (size_t)(m < M ? m : 0) * K);
+    for (int m = 0; m < MT; ++m) xb[m] = (const uint8_t*)(X + (size_t)(m < M ? m : 0) * K);
 
     const int per = (nch + SPLIT - 1) / SPLIT;
     const int cbeg = part * per;
@@ -126,58 +131,93 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
 
-    auto get_x = [&](int m, int c, XChunk& xc) {
+    struct Stage {
+        u32x4 w[U][R];
+        uint16_t sc[U][R];
+        u32x4 x[U][MT][STAGE ? 1 : 4];   // raw x of the chunk (unstaged x only)
+    };
+    auto load = [&](Stage& s, int cb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = (uint32_t)(cb + kWave * u + lane);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                s.w[u][r] = load_w16(wb[r], c * 16u);
+                s.sc[u][r] = load_w2(sb[r], (c >> 1) * 2u);
+            }
+            if constexpr (!STAGE) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) s.x[u][m][t] = load_x16(xb[m], (4 * c + t) * 16u);
+            }
+        }
+    };
+    auto get_x = [&](const Stage& s, int u, int m, int c, XChunk& xc) {
         if constexpr (STAGE) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) xc.v[t] = xs[(m * 4 + t) * nch + c];
             xc.negsum = xsum[m * nch + c];
         } else {
-            u32x4 xd[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xd[t] = load_x16(xp[m] + 4 * c + t);
-            pair_x(xd, xc);
+            pair_x(s.x[u][m], xc);
         }
     };
-
-    int cb = cbeg;
-    for (; cb + kWave * U <= cend; cb += kWave * U) {
-        u32x4 w[U][R];
-        uint16_t sc[U][R];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int c = cb + kWave * u + lane;
-                w[u][r] = load_w16(wp[r] + c);
-                sc[u][r] = __builtin_nontemporal_load(sp[r] + (c >> 1));
-            }
+    auto compute = [&](const Stage& s, int cb) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = cb + kWave * u + lane;
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 XChunk xc;
-                get_x(m, c, xc);
+                get_x(s, u, m, c, xc);
 #pragma unroll
                 for (int r = 0; r < R; ++r)
-                    acc[r * MT + m] = fmaf(half_to_float(sc[u][r]), chunk_dot(w[u][r], xc), acc[r * MT + m]);
+                    acc[r * MT + m] = fmaf(half_to_float(s.sc[u][r]), chunk_dot(s.w[u][r], xc),
+                                           acc[r * MT + m]);
             }
         }
+    };
+
+    // full steps, two register stages in flight (unrolled by two: no copies)
+    const int nfull = (cend - cbeg) / STEP;
+    int cb = cbeg;
+    if (nfull > 0) {
+        Stage s0, s1;
+        load(s0, cb);
+        for (int it = 0;;) {
+            if (it + 1 < nfull) load(s1, cb + STEP);
+            compute(s0, cb);
+            cb += STEP;
+            if (++it >= nfull) break;
+            if (it + 1 < nfull) load(s0, cb + STEP);
+            compute(s1, cb);
+            cb += STEP;
+            if (++it >= nfull) break;
+        }
     }
-    for (; cb < cend; cb += kWave) {
+    for (; cb < cend; cb += kWave) {   // ragged tail: one chunk per lane at most
         const int c = cb + lane;
         if (c < cend) {
             u32x4 w[R];
             uint16_t sc[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                w[r] = load_w16(wp[r] + c);
-                sc[r] = __builtin_nontemporal_load(sp[r] + (c >> 1));
+                w[r] = load_w16(wb[r], (uint32_t)c * 16u);
+                sc[r] = load_w2(sb[r], (uint32_t)(c >> 1) * 2u);
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 XChunk xc;
-                get_x(m, c, xc);
+                if constexpr (STAGE) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) xc.v[t] = xs[(m * 4 + t) * nch + c];
+                    xc.negsum = xsum[m * nch + c];
+                } else {
+                    u32x4 xd[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) xd[t] = load_x16(xb[m], (uint32_t)(4 * c + t) * 16u);
+                    pair_x(xd, xc);
+                }
 #pragma unroll
                 for (int r = 0; r < R; ++r)
                     acc[r * MT + m] = fmaf(half_to_float(sc[r]), chunk_dot(w[r], xc), acc[r * MT + m]);
@@ -245,25 +285,22 @@ static void add_splits(std::vector<Variant>& out) {
 }
 
 void register_gemv_q4g64(std::vector<Variant>& out) {
+    add_splits<1, 1, 1>(out);
     add_splits<1, 1, 2>(out);
-    add_splits<1, 1, 4>(out);
     add_splits<1, 2, 1>(out);
     add_splits<1, 2, 2>(out);
     add_splits<1, 4, 1>(out);
-    add_splits<1, 4, 2>(out);
     add_splits<1, 8, 1>(out);
 
-    add_splits<2, 1, 2>(out);
+    add_splits<2, 1, 1>(out);
     add_splits<2, 2, 1>(out);
     add_splits<2, 4, 1>(out);
 
-    add_splits<4, 1, 2>(out);
+    add_splits<4, 1, 1>(out);
     add_splits<4, 2, 1>(out);
-    add_splits<4, 4, 1>(out);
 
     add_splits<8, 1, 1>(out);
     add_splits<8, 2, 1>(out);
-    add_splits<8, 4, 1>(out);
 }
 
 }  // namespace lin

@@ -21,12 +21,25 @@ struct KArgs {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;   // four wavefronts per workgroup
 
+// Index of this wavefront in its workgroup, as a wave-uniform (scalar) value so
+// that row addresses derived from it live in SGPRs.
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 // Weights are read exactly once per call: a non-temporal 16-byte load keeps
 // them from displacing the activations, which every wavefront re-reads.
-__device__ __forceinline__ u32x4 load_w16(const u32x4* p) {
-    return __builtin_nontemporal_load(p);
+// Addresses are a wave-uniform base plus a 32-bit per-lane byte offset, which
+// maps to the scalar-base form of the global load (no 64-bit vector adds).
+__device__ __forceinline__ u32x4 load_w16(const uint8_t* base, uint32_t off) {
+    return __builtin_nontemporal_load((const u32x4*)(base + off));
 }
-__device__ __forceinline__ u32x4 load_x16(const u32x4* p) { return *p; }
+__device__ __forceinline__ u32x4 load_x16(const uint8_t* base, uint32_t off) {
+    return *(const u32x4*)(base + off);
+}
+__device__ __forceinline__ uint16_t load_w2(const uint8_t* base, uint32_t off) {
+    return __builtin_nontemporal_load((const uint16_t*)(base + off));
+}
 
 // acc + a.lo*b.lo + a.hi*b.hi on two bf16 pairs (v_dot2_f32_bf16); the
 // bf16 x bf16 products are exact in fp32.

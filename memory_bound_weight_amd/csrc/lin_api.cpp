@@ -85,9 +85,19 @@ int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
         want.split = N >= 4096 ? 1 : (N >= 1024 ? 2 : 4);
     } else {
         if (kind == LIN_KIND_SKINNY_BF16 && M > 16) {
-            // matrix cores, when a variant applies
-            for (int i : candidates(kind, M, N, K))
-                if (registry()[i].cfg.algo == LIN_ALGO_MFMA) return i;
+            // matrix cores: a token tile covering M (up to 128), two W fragments
+            // per wavefront for small tiles
+            lin_config mf{};
+            mf.algo = LIN_ALGO_MFMA;
+            mf.tile_m = mt < 32 ? 32 : (mt > 128 ? 128 : mt);
+            mf.rows = mf.tile_m >= 128 ? 64 : 128;
+            mf.unroll = 1;
+            mf.split = 1;
+            mf.stage_x = 1;
+            int i = find_variant(kind, M, N, K, mf);
+            if (i >= 0) return i;
+            for (int j : candidates(kind, M, N, K))
+                if (registry()[j].cfg.algo == LIN_ALGO_MFMA) return j;
         }
         want.rows = mt <= 1 ? (N >= 8192 ? 2 : 1) : (mt <= 8 ? 2 : 1);
         want.unroll = mt <= 1 ? (want.rows == 1 ? 4 : 2) : (mt <= 8 ? 2 : 1);

@@ -56,6 +56,25 @@ def decode_matrices(model):
     return out
 
 
+def decode_groups(model, fused=True):
+    """Launch groups of one decode step, in model order: [(layer, [(mat_idx, name,
+    N, K), ...])].  Fused: matrices that read the same input are concatenated
+    along N at load time (q|k|v and gate|up), as an engine does to cut launches;
+    unfused: one group per matrix."""
+    groups = []
+    for layer in range(model["layers"]):
+        mats = [(i, name, n, k) for i, (name, n, k) in enumerate(model["layer"])]
+        if fused:
+            by = {m[1]: m for m in mats}
+            for names in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",)):
+                groups.append((layer, [by[nm] for nm in names]))
+        else:
+            groups += [(layer, [m]) for m in mats]
+    name, n, k = model["head"]
+    groups.append((model["layers"], [(0, name, n, k)]))
+    return groups
+
+
 def seed_for(cfg_seed, layer, mat_idx, role):
     """A 63-bit seed unique to (workload, layer, matrix, role)."""
     ss = np.random.SeedSequence([int(cfg_seed), int(layer), int(mat_idx), int(role)])

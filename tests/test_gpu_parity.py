@@ -70,7 +70,10 @@ def test_gemv_q4g64_every_candidate(M, N, K):
             assert_within_bound(y, Y, B, "q4 %s" % cfg)
 
 
-SKINNY_CASES = [(1, 64, 2048), (9, 130, 1032), (16, 257, 520), (17, 64, 2048), (31, 100, 4096)]
+# VALU path (M <= 32) and matrix-core path (M > 16): ragged M, N and K tails
+SKINNY_CASES = [(1, 64, 2048), (9, 130, 1032), (16, 257, 520), (17, 64, 2048), (31, 100, 4096),
+                (33, 100, 4096), (48, 1000, 576), (64, 130, 1032), (100, 257, 520),
+                (256, 64, 2048), (256, 300, 4104)]
 
 
 @pytest.mark.parametrize("M,N,K", SKINNY_CASES)

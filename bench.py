@@ -1,7 +1,8 @@
 """Decode-step linear-layer benchmark on one MI355X.
 
 One step = one batch-1 decode pass over a model's linear weights: every matrix
-y = W . x once, in model order, captured as a HIP graph and replayed.  The
+y = W . x once, in model order (q|k|v and gate|up concatenated at load), each
+format's pass captured as a HIP graph and replayed.  The
 default workload is the TinyLlama-1.1B-shaped weight set (22 layers x {q, k,
 v, o, gate, up, down} + output head), run once in bf16 and once in int4-g64;
 the value is the achieved HBM rate over the algorithmic bytes of the step.
@@ -145,6 +146,24 @@ def capture(mats):
             launch(m)
     torch.cuda.synchronize()
     return g
+
+
+def time_runs(fns, steps, warmup):
+    """Wall and GPU (event) time per step of calling every fn in order."""
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        for f in fns:
+            f()
+    e1.record()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps, e0.elapsed_time(e1) / 1000.0 / steps
 
 
 def time_graph(g, steps, warmup):
@@ -312,20 +331,21 @@ def main():
     tuning = apply_tuning(allm, tfile, args.tune)
     log("tuning: " + tuning)
 
+    step_bytes = sum(m.bytes for m in allm)
+    fmt_bytes = {f: sum(m.bytes for m in sets[f]) for f in sets}
+
+    # one kernel per (fused) matrix, each format's step captured as one graph
     graphs = {f: capture(sets[f]) for f in sets}
-    g_all = capture(allm)
     per_fmt = {}
     for f in ("bf16", "q4"):
-        wall, gpu = time_graph(graphs[f], max(5, args.steps // 2), args.warmup)
-        b = sum(m.bytes for m in sets[f])
-        per_fmt[f] = {"ms_per_token": round(gpu * 1e3, 4), "equiv_tok_s": round(1.0 / gpu, 1),
-                      "GB_s": round(b / gpu / 1e9, 1), "bytes": b}
-        log("%s step: %.1f us, %.1f GB/s, %.0f tok/s" % (f, gpu * 1e6, b / gpu / 1e9, 1 / gpu))
-
-    # the timed region: K steps of the whole path (bf16 + int4 sets)
+        _, gpu_f = time_graph(graphs[f], max(5, args.steps // 2), args.warmup)
+        per_fmt[f] = {"ms_per_token": round(gpu_f * 1e3, 4), "equiv_tok_s": round(1.0 / gpu_f, 1),
+                      "GB_s": round(fmt_bytes[f] / gpu_f / 1e9, 1), "bytes": fmt_bytes[f]}
+        log("%s step: %.1f us, %.1f GB/s, %.0f tok/s" % (f, gpu_f * 1e6, fmt_bytes[f] / gpu_f / 1e9,
+                                                        1 / gpu_f))
+    # the timed region: K steps of the whole path (bf16 step, then int4 step)
     torch.cuda.synchronize()
-    wall, gpu = time_graph(g_all, args.steps, args.warmup)
-    step_bytes = sum(m.bytes for m in allm)
+    wall, gpu = time_runs([graphs["bf16"].replay, graphs["q4"].replay], args.steps, args.warmup)
     gbs = step_bytes / wall / 1e9
 
     kt = kernel_times(allm, reps=max(5, args.steps // 2))

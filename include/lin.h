@@ -72,10 +72,13 @@ typedef enum lin_algo {
 /* One launch configuration.  VALU: a wavefront owns `rows` consecutive rows and
  * streams them with 16-byte loads, `unroll` loads per lane and row in flight;
  * `split` wavefronts share a row group by splitting K and combine through LDS;
- * `stage_x` = 1 stages x in LDS once per workgroup.  MFMA: `rows` is the W rows
- * per workgroup, `tile_m` the tokens per workgroup tile; `split` = wavefronts per
- * workgroup splitting K.  `us` is filled by lin_autotune (median microseconds
- * per call, cold caches) and ignored on input. */
+ * `stage_x` = 1 stages x in LDS once per workgroup; `tile_m` = tokens per
+ * kernel instance.  MFMA: `rows` = W rows per workgroup, `tile_m` = tokens per
+ * workgroup tile, `unroll` = k-blocks of 64 in flight per workgroup, `split` =
+ * workgroups sharing one output tile by splitting K (their partial tiles go
+ * through a library-owned workspace and are added in a fixed order, so results
+ * stay deterministic).  `us` is filled by lin_autotune (median microseconds per
+ * call, cold caches) and ignored on input. */
 typedef struct lin_config {
     int32_t algo;
     int32_t rows;
@@ -117,8 +120,9 @@ int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y,
  * from cold caches.  The fastest configuration is stored in the per-device
  * table and used by later calls with the same (kind, M, N, K); if `out` is not
  * NULL it receives it, with `us` set.  Unlike the compute calls this one
- * allocates a cache-flush buffer on first use (kept until process exit),
- * synchronises `stream` and must not be called during graph capture. */
+ * allocates a cache-flush buffer on first use and the split-K workspace the
+ * candidates need (both kept until process exit), synchronises `stream` and
+ * must not be called during graph capture. */
 int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y,
                  int64_t M, int64_t N, int64_t K, void* stream, lin_config* out);
 
@@ -133,7 +137,13 @@ int lin_candidate(int kind, int64_t M, int64_t N, int64_t K, int index, lin_conf
 int lin_get_config(int kind, int64_t M, int64_t N, int64_t K, lin_config* out);
 
 /* Pin `cfg` for (kind, M, N, K) on the current device (it must be one of the
- * candidates), or remove the entry when cfg is NULL. */
+ * candidates), or remove the entry when cfg is NULL.  A load-time call: a
+ * split-K configuration makes the library grow its per-device workspace here
+ * (allocation and device synchronisation), never in the product calls; a
+ * product call whose pinned configuration lacks workspace returns
+ * LIN_ERR_UNSUPPORTED.  Product calls that use split-K share the device's
+ * workspace, so such calls on one device must not run concurrently on
+ * different streams. */
 int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg);
 
 /* Load-time weight preparation: quantise bf16 W [N][K] (K % 64 == 0) to the

@@ -13,9 +13,10 @@
 // Mapping.  A workgroup is four wavefronts and owns BN = 64 NF rows of W and
 // TM tokens.  Wavefront w owns NF fragments of 16 W rows.  W is the streamed
 // operand: each lane loads its B fragment straight from HBM (16 bytes; the 64
-// lanes cover 16 rows x 64 contiguous bytes), with the next k-block's
-// fragments prefetched into registers while the current block is multiplied;
-// every W byte is read once per workgroup and used against all TM tokens.
+// lanes cover 16 rows x 64 contiguous bytes); a ring of D register stages
+// keeps D k-blocks of W and X loads in flight per workgroup (one block of work
+// is far too short to cover HBM latency); every W byte is read once per
+// workgroup and used against all TM tokens.
 // X, re-read by every workgroup, goes through LDS: a TM x 64 tile per k-block,
 // double-buffered, with 16-byte chunk c of token row m stored at slot
 // c ^ (m mod 8) (XOR swizzle, no padding) so the A-fragment reads spread over
@@ -25,6 +26,15 @@
 // with its own L2.  When M needs several token tiles, the tiles of one W block
 // are given consecutive slots on the same XCD, so the W block comes from HBM
 // once and from that XCD's L2 for the other token tiles.
+//
+// Split-K.  A small N x M leaves too few output tiles to keep 256 CUs streaming
+// (each workgroup walks K serially), so SPLITS workgroups share a tile, each
+// taking a contiguous range of k-blocks.  Each writes its partial tile to the
+// workspace, then bumps the tile's counter (agent-scope acq_rel atomic).  The
+// workgroup that sees the last count adds the SPLITS partials in split order
+// 0, 1, ... (so the result does not depend on which one finishes last), writes
+// Y and resets the counter to zero for the next call.  No workgroup ever waits
+// for another.
 #include "registry.h"
 
 namespace lin {
@@ -39,27 +49,40 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int NF, int TM>
+template <int NF, int TM, int D>
 __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
     constexpr int BN = 64 * NF;
     constexpr int MT = TM / 16;                  // 16-token sub-tiles
     constexpr int XCH = TM * (kBK / 8) / kBlock;  // 16-byte X chunks per thread per block
     static_assert(XCH >= 1, "TM too small");
     const int M = a.M, N = a.N, K = a.K;
+    const int S = a.splits;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
     const int l16 = lane & 15, lg = lane >> 4;
 
-    // XCD-aware tile order (see above)
     const int m_tiles = (M + TM - 1) / TM;
     const int n_tiles = (N + BN - 1) / BN;
-    const int b = blockIdx.x;
-    const int xcd = b & 7, loc = b >> 3;
-    const int n_tile = (loc / m_tiles) * 8 + xcd;
-    const int m_tile = loc - (loc / m_tiles) * m_tiles;
-    if (n_tile >= n_tiles) return;   // padding slot: whole workgroup leaves together
+    int n_tile, m_tile, ks;
+    if (S == 1) {   // XCD-aware tile order (see above)
+        const int b = blockIdx.x;
+        const int xcd = b & 7, loc = b >> 3;
+        n_tile = (loc / m_tiles) * 8 + xcd;
+        m_tile = loc - (loc / m_tiles) * m_tiles;
+        ks = 0;
+        if (n_tile >= n_tiles) return;   // padding slot: whole workgroup leaves together
+    } else {        // splits of one tile are consecutive
+        const int t = blockIdx.x / S;
+        ks = blockIdx.x - t * S;
+        n_tile = t / m_tiles;
+        m_tile = t - n_tile * m_tiles;
+    }
     const int n0 = n_tile * BN + wave * 16 * NF;
     const int m0 = m_tile * TM;
+    const int nkb_all = (K + kBK - 1) / kBK;   // a partial last block is zero-filled
+    const int bps = (nkb_all + S - 1) / S;     // k-blocks per split
+    const int kb0 = ks * bps;
+    const int kb1 = min(nkb_all, kb0 + bps);
 
     __shared__ u32x4 xt[2][TM * (kBK / 8)];   // two X tiles, 16-byte chunks, swizzled
 
@@ -97,8 +120,7 @@ __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-            {
+            for (int s = 0; s < 2; ++s) {
                 const int k = kb * kBK + s * 32 + lg * 8;
                 wr[f][s] = k < K ? load_w16(wrow[f], (uint32_t)k * 2u) : u32x4{0, 0, 0, 0};
             }
@@ -123,87 +145,159 @@ __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
             }
     };
 
-    const int nkb = (K + kBK - 1) / kBK;   // a partial last block is zero-filled
-    u32x4 w0[NF][2], w1[NF][2];
-    u32x4 xr[XCH];
-    load_w(w0, 0);
-    load_x(xr, 0);
-    store_x(xr, 0);
-    __syncthreads();
-    // k-blocks, two register stages of W (unrolled by two: no copies)
-    for (int kb = 0;;) {
-        if (kb + 1 < nkb) {
-            load_w(w1, kb + 1);
-            load_x(xr, kb + 1);
+    // D-stage prefetch ring: the loads of block kb + D are issued as soon as
+    // block kb has been consumed, so D blocks of W (and of X) are in flight per
+    // workgroup.  The ring is unrolled by D so every stage index is static.
+    struct Stage {
+        u32x4 w[NF][2];
+        u32x4 x[XCH];
+    };
+    Stage st[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (kb0 + d < kb1) {
+            load_w(st[d].w, kb0 + d);
+            load_x(st[d].x, kb0 + d);
         }
-        compute(w0, kb & 1);
-        if (kb + 1 < nkb) store_x(xr, (kb + 1) & 1);
-        __syncthreads();
-        if (++kb >= nkb) break;
-        if (kb + 1 < nkb) {
-            load_w(w0, kb + 1);
-            load_x(xr, kb + 1);
+    for (int base = kb0; base < kb1; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int kb = base + d;
+            if (kb >= kb1) break;
+            const int buf = (kb - kb0) & 1;
+            store_x(st[d].x, buf);
+            __syncthreads();   // X tile complete; the buffer written next time is idle
+            compute(st[d].w, buf);
+            if (kb + D < kb1) {
+                load_w(st[d].w, kb + D);
+                load_x(st[d].x, kb + D);
+            }
         }
-        compute(w1, kb & 1);
-        if (kb + 1 < nkb) store_x(xr, (kb + 1) & 1);
-        __syncthreads();
-        if (++kb >= nkb) break;
     }
 
-    // epilogue: lane holds rows 4*lg + r of each 16-token sub-tile, column l16
+    // lane holds rows 4*lg + r of each 16-token sub-tile, column l16
+    if (S == 1) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int n = n0 + f * 16 + l16;
+            if (n >= N) continue;
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + t * 16 + lg * 4 + r;
+                    if (m < M) a.Y[(int64_t)m * N + n] = acc[f][t][r];
+                }
+        }
+        return;
+    }
+
+    // split-K: publish the partial tile, count, the last arriver reduces in order
+    const int tiles = m_tiles * n_tiles;
+    const int tile = n_tile * m_tiles + m_tile;
+    uint32_t* cnt = (uint32_t*)a.ws;
+    float* parts = (float*)((uint8_t*)a.ws + ws_counter_bytes(tiles));
+    const size_t tile_elems = (size_t)TM * BN;
+    float* mine = parts + ((size_t)ks * tiles + tile) * tile_elems;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                mine[(t * 16 + lg * 4 + r) * BN + wave * 16 * NF + f * 16 + l16] = acc[f][t][r];
+    __shared__ int last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_ACQ_REL,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        last = (old == (uint32_t)(S - 1));
+    }
+    __syncthreads();
+    if (!last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
         const int n = n0 + f * 16 + l16;
-        if (n >= N) continue;
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int m = m0 + t * 16 + lg * 4 + r;
-                if (m < M) a.Y[(int64_t)m * N + n] = acc[f][t][r];
+                const int ml = t * 16 + lg * 4 + r;
+                const size_t e = (size_t)ml * BN + wave * 16 * NF + f * 16 + l16;
+                float v = 0.f;
+                for (int j = 0; j < S; ++j) v += parts[((size_t)j * tiles + tile) * tile_elems + e];
+                const int m = m0 + ml;
+                if (m < M && n < N) a.Y[(int64_t)m * N + n] = v;
             }
     }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NF, int TM>
-static bool geom_mfma(const Variant&, int M, int N, int K, dim3* grid, size_t* lds) {
+template <int NF, int TM, int D>
+static bool geom_mfma(const Variant& v, int M, int N, int K, dim3* grid, size_t* lds) {
     if (K <= 0) return false;
     constexpr int BN = 64 * NF;
+    const int S = v.cfg.split;
     const int m_tiles = (M + TM - 1) / TM;
     if (TM > 16 && M <= TM / 2) return false;    // a smaller token tile fits
     const int n_tiles = (N + BN - 1) / BN;
-    const int n_pad = (n_tiles + 7) / 8 * 8;
-    *grid = dim3((unsigned)(n_pad * m_tiles));
+    const int nkb = (K + kBK - 1) / kBK;
+    if (S > 1 && nkb < 2 * S) return false;      // at least two k-blocks per split
+    if (S == 1) {
+        const int n_pad = (n_tiles + 7) / 8 * 8;
+        *grid = dim3((unsigned)(n_pad * m_tiles));
+    } else {
+        *grid = dim3((unsigned)(n_tiles * m_tiles * S));
+    }
     *lds = 0;
     return true;
 }
 
-template <int NF, int TM>
-static void add(std::vector<Variant>& out) {
+template <int NF, int TM, int D>
+static size_t ws_mfma(const Variant& v, int M, int N, int K) {
+    (void)K;
+    const int S = v.cfg.split;
+    if (S <= 1) return 0;
+    constexpr int BN = 64 * NF;
+    const size_t tiles = (size_t)((M + TM - 1) / TM) * ((N + BN - 1) / BN);
+    return ws_counter_bytes((int)tiles) + (size_t)S * tiles * TM * BN * sizeof(float);
+}
+
+template <int NF, int TM, int D>
+static void add(std::vector<Variant>& out, int S) {
     Variant v{};
     v.kind = LIN_KIND_SKINNY_BF16;
     v.cfg.algo = LIN_ALGO_MFMA;
     v.cfg.rows = 64 * NF;
-    v.cfg.unroll = 1;
-    v.cfg.split = 1;
+    v.cfg.unroll = D;
+    v.cfg.split = S;
     v.cfg.stage_x = 1;
     v.cfg.tile_m = TM;
     v.mt = 0;
     v.min_m = 16;
-    v.func = (const void*)&gemm_mfma_kernel<NF, TM>;
-    v.geometry = &geom_mfma<NF, TM>;
+    v.func = (const void*)&gemm_mfma_kernel<NF, TM, D>;
+    v.geometry = &geom_mfma<NF, TM, D>;
+    v.workspace = &ws_mfma<NF, TM, D>;
     out.push_back(v);
 }
 
+template <int NF, int TM, int D>
+static void add_splits(std::vector<Variant>& out) {
+    for (int S : {1, 2, 4, 8, 16}) add<NF, TM, D>(out, S);
+}
+
 void register_gemm_mfma(std::vector<Variant>& out) {
-    add<1, 32>(out);
-    add<1, 64>(out);
-    add<2, 64>(out);
-    add<4, 64>(out);
-    add<1, 128>(out);
-    add<2, 128>(out);
-    add<1, 256>(out);
-    add<2, 256>(out);
+    add_splits<1, 32, 4>(out);
+    add_splits<1, 32, 8>(out);
+    add_splits<1, 64, 2>(out);
+    add_splits<1, 64, 4>(out);
+    add_splits<2, 64, 4>(out);
+    add_splits<1, 128, 2>(out);
+    add_splits<1, 128, 4>(out);
+    add_splits<2, 128, 2>(out);
+    add_splits<2, 256, 2>(out);
 }
 
 }  // namespace lin

@@ -1,250 +1,13 @@
-// int4-g64 streaming product on the vector ALUs: w[n][k] = q[n][k] * s[n][k/64],
-// y[m][n] = sum_k w[n][k] x[m][k], for M <= 8 tokens.  4-bit weights with one
-// fp16 scale per 64 (tinyinfer post, TL;DR) cut the streamed bytes to 0.53 B
-// per weight; unpacking must then cost almost nothing, since it is no longer
-// hidden behind the memory traffic (llm-rs benchmark post, section 6).
-//
-// Mapping.  As the bf16 kernel: four wavefronts per workgroup, a wavefront owns
-// R rows, each lane reads consecutive 16-byte chunks = 32 codes = half a scale
-// group, so lanes 2i and 2i+1 share one scale.
-//
-// Unpacking without conversions.  Flipping bit 3 of a nibble turns the two's
-// complement code q into n' = q + 8 in [0, 15], and (n' | 0x4300) read as bf16
-// is exactly 128 + n' = q + 136, so one 3-input bitwise operation per pair of
-// nibbles yields two bf16 "codes" that go straight into v_dot2_f32_bf16.  Masking 0x000F000F after shifting a dword by
-// 0, 4, 8, 12 pairs nibble i with nibble i+4, i.e. k = 8d+i with k = 8d+i+4,
-// so x is re-paired the same way (one v_perm per pair).  The offset is removed
-// per chunk: sum_k q x = dot(codes, x) - 136 * sum_k x, where sum_k x over the
-// chunk is shared by all rows; the dot chain starts from -136 * sum x.  Then
-// acc += s * chunk sum.  Per 32 weights and row: 28 unpack + 16 dot2 + 1 for
-// the scale, about 1.4 vector operations per weight.
-//
-// x handling: either re-paired from cached global loads per chunk (cost shared
-// by the R rows), or, with STAGE, re-paired once per workgroup into LDS as
-// [MT][4][chunks] 16-byte words (bank-conflict-free reads) plus the chunk sums.
+// Standalone kernels, launch geometry and the candidate list of the product in
+// gemv_q4g64_impl.h.
+#include "gemv_q4g64_impl.h"
 #include "registry.h"
 
 namespace lin {
 
-// 16 re-paired x dwords of one 32-k chunk: pair (x[8d+i], x[8d+i+4]) at 4d+i.
-struct XChunk {
-    u32x4 v[4];
-    float negsum;   // -136 * sum of the 32 x values
-};
-
-__device__ __forceinline__ void pair_x(const u32x4 (&xd)[4], XChunk& out) {
-    // xd[t/4][t%4] = natural dword t = (x[2t], x[2t+1]); dword d of the weights
-    // covers k = 8d .. 8d+7, i.e. natural dwords 4d .. 4d+3.
-    float s = 0.f;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t a0 = xd[d][0], a1 = xd[d][1], a2 = xd[d][2], a3 = xd[d][3];
-        out.v[d][0] = __builtin_amdgcn_perm(a2, a0, 0x05040100u);   // x0, x4
-        out.v[d][1] = __builtin_amdgcn_perm(a2, a0, 0x07060302u);   // x1, x5
-        out.v[d][2] = __builtin_amdgcn_perm(a3, a1, 0x05040100u);   // x2, x6
-        out.v[d][3] = __builtin_amdgcn_perm(a3, a1, 0x07060302u);   // x3, x7
-        s = dot2(a0, 0x3F803F80u, s);   // bf16 (1.0, 1.0)
-        s = dot2(a1, 0x3F803F80u, s);
-        s = dot2(a2, 0x3F803F80u, s);
-        s = dot2(a3, 0x3F803F80u, s);
-    }
-    out.negsum = -136.f * s;
-}
-
-// Sum over one chunk of 32 codes times re-paired x, minus the code offset.
-// ((w >> 4i) & 0x000F000F) ^ 0x43084308 equals ((w ^ 0x88888888) >> 4i &
-// 0x000F000F) | 0x43004300: the sign flip and the bf16 exponent bits go in with
-// one 3-input bitwise operation (v_bitop3_b32), plus one shift for i > 0.
-__device__ __forceinline__ float chunk_dot(const u32x4& wq, const XChunk& xc) {
-    constexpr uint32_t M = 0x000F000Fu, C = 0x43084308u;
-    float acc = xc.negsum;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t w = wq[d];
-        acc = dot2((w & M) ^ C, xc.v[d][0], acc);
-        acc = dot2(((w >> 4) & M) ^ C, xc.v[d][1], acc);
-        acc = dot2(((w >> 8) & M) ^ C, xc.v[d][2], acc);
-        acc = dot2(((w >> 12) & M) ^ C, xc.v[d][3], acc);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ float half_to_float(uint16_t h) {
-    return (float)__builtin_bit_cast(_Float16, h);
-}
-
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
-    constexpr int GROUPS = 4 / SPLIT;
-    constexpr int V = R * MT;
-    constexpr int STEP = kWave * U;   // chunks per pipeline step
-    const int lane = threadIdx.x & 63;
-    const int wave = wave_id();
-    const int grp = wave / SPLIT;
-    const int part = wave - grp * SPLIT;
-    const int M = a.M, N = a.N, K = a.K;
-    const int nch = K >> 5;   // 16-byte chunks (32 codes) per row
-    const int G = K >> 6;     // scale groups per row
-    const uint8_t* __restrict__ Wq = (const uint8_t*)a.W;
-    const uint16_t* __restrict__ S = (const uint16_t*)a.S;
-    const uint16_t* __restrict__ X = (const uint16_t*)a.X;
-
-    extern __shared__ u32x4 xs[];   // STAGE: [MT][4][nch] words, then [MT][nch] floats
-    float* xsum = (float*)(xs + (size_t)MT * 4 * nch);
-    if constexpr (STAGE) {
-        for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
-            const int m = i / nch;
-            const int c = i - m * nch;
-            const int mm = m < M ? m : 0;
-            const uint8_t* src = (const uint8_t*)(X + (size_t)mm * K);
-            u32x4 xd[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xd[t] = load_x16(src, (uint32_t)(4 * c + t) * 16u);
-            XChunk xc;
-            pair_x(xd, xc);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xs[(m * 4 + t) * nch + c] = xc.v[t];
-            xsum[m * nch + c] = xc.negsum;
-        }
-        __syncthreads();
-    }
-
-    const int64_t row0 = ((int64_t)blockIdx.x * GROUPS + grp) * R;
-    const uint8_t* wb[R];
-    const uint8_t* sb[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        int64_t row = row0 + r;
-        row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
-        wb[r] = Wq + row * (int64_t)(K / 2);
-        sb[r] = (const uint8_t*)(S + row * (int64_t)G);
-    }
-    const uint8_t* xb[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) xb[m] = (const uint8_t*)(X + (size_t)(m < M ? m : 0) * K);
-
-    const int per = (nch + SPLIT - 1) / SPLIT;
-    const int cbeg = part * per;
-    const int cend = min(nch, cbeg + per);
-
-    float acc[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.f;
-
-    struct Stage {
-        u32x4 w[U][R];
-        uint16_t sc[U][R];
-        u32x4 x[U][MT][STAGE ? 1 : 4];   // raw x of the chunk (unstaged x only)
-    };
-    auto load = [&](Stage& s, int cb) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t c = (uint32_t)(cb + kWave * u + lane);
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                s.w[u][r] = load_w16(wb[r], c * 16u);
-                s.sc[u][r] = load_w2(sb[r], (c >> 1) * 2u);
-            }
-            if constexpr (!STAGE) {
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) s.x[u][m][t] = load_x16(xb[m], (4 * c + t) * 16u);
-            }
-        }
-    };
-    auto get_x = [&](const Stage& s, int u, int m, int c, XChunk& xc) {
-        if constexpr (STAGE) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xc.v[t] = xs[(m * 4 + t) * nch + c];
-            xc.negsum = xsum[m * nch + c];
-        } else {
-            pair_x(s.x[u][m], xc);
-        }
-    };
-    auto compute = [&](const Stage& s, int cb) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int c = cb + kWave * u + lane;
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                XChunk xc;
-                get_x(s, u, m, c, xc);
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    acc[r * MT + m] = fmaf(half_to_float(s.sc[u][r]), chunk_dot(s.w[u][r], xc),
-                                           acc[r * MT + m]);
-            }
-        }
-    };
-
-    // full steps, two register stages in flight (unrolled by two: no copies)
-    const int nfull = (cend - cbeg) / STEP;
-    int cb = cbeg;
-    if (nfull > 0) {
-        Stage s0, s1;
-        load(s0, cb);
-        for (int it = 0;;) {
-            if (it + 1 < nfull) load(s1, cb + STEP);
-            compute(s0, cb);
-            cb += STEP;
-            if (++it >= nfull) break;
-            if (it + 1 < nfull) load(s0, cb + STEP);
-            compute(s1, cb);
-            cb += STEP;
-            if (++it >= nfull) break;
-        }
-    }
-    for (; cb < cend; cb += kWave) {   // ragged tail: one chunk per lane at most
-        const int c = cb + lane;
-        if (c < cend) {
-            u32x4 w[R];
-            uint16_t sc[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                w[r] = load_w16(wb[r], (uint32_t)c * 16u);
-                sc[r] = load_w2(sb[r], (uint32_t)(c >> 1) * 2u);
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                XChunk xc;
-                if constexpr (STAGE) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) xc.v[t] = xs[(m * 4 + t) * nch + c];
-                    xc.negsum = xsum[m * nch + c];
-                } else {
-                    u32x4 xd[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) xd[t] = load_x16(xb[m], (uint32_t)(4 * c + t) * 16u);
-                    pair_x(xd, xc);
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    acc[r * MT + m] = fmaf(half_to_float(sc[r]), chunk_dot(w[r], xc), acc[r * MT + m]);
-            }
-        }
-    }
-
-    wave_reduce<V>(acc);
-    if constexpr (SPLIT == 1) {
-        for_each_reduced<V>(acc, lane, [&](int idx, float val) {
-            const int r = idx / MT, m = idx - (idx / MT) * MT;
-            if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = val;
-        });
-    } else {
-        __shared__ float red[4][V];
-        for_each_reduced<V>(acc, lane, [&](int idx, float val) { red[wave][idx] = val; });
-        __syncthreads();
-        if (part == 0) {
-            for_each_reduced<V>(acc, lane, [&](int idx, float) {
-                const int r = idx / MT, m = idx - (idx / MT) * MT;
-                float s = red[wave][idx];
-#pragma unroll
-                for (int p = 1; p < SPLIT; ++p) s += red[wave + p][idx];
-                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = s;
-            });
-        }
-    }
+    gemv_q4_valu_block<MT, R, U, SPLIT, STAGE>(a, blockIdx.x);
 }
 
 template <int MT, int R, int U, int SPLIT, bool STAGE>

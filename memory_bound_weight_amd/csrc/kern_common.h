@@ -16,6 +16,8 @@ struct KArgs {
     const void* X;   // bf16 [M][K]
     float* Y;        // fp32 [M][N]
     int M, N, K;
+    int splits;      // split-K factor (matrix-core path), 1 otherwise
+    void* ws;        // split-K workspace: tile counters, then partial tiles
 };
 
 constexpr int kWave = 64;
@@ -128,6 +130,12 @@ __device__ __forceinline__ void for_each_reduced(const float (&v)[V], int lane, 
 #pragma unroll
     for (int s = 0; s < S; ++s)
         if (reduce_writer<V>(s, lane)) f(reduce_index<V>(s, lane), v[s]);
+}
+
+// Split-K workspace: one 32-bit counter per output tile, padded to 256 bytes,
+// followed by the partial tiles.
+__host__ __device__ inline size_t ws_counter_bytes(int tiles) {
+    return ((size_t)tiles * 4 + 255) / 256 * 256;
 }
 
 }  // namespace lin

@@ -141,6 +141,42 @@ int lookup(int kind, int64_t M, int64_t N, int64_t K) {
     return vi;
 }
 
+// Split-K workspace per device.  Grown only by the load-time calls
+// (lin_autotune, lin_set_config), after a device synchronisation, and zeroed so
+// that every tile counter starts at 0; kernels leave the counters at 0.
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::map<int, Workspace>& workspaces() {
+    static auto* w = new std::map<int, Workspace>();
+    return *w;
+}
+
+size_t workspace_need(const Variant& v, int64_t M, int64_t N, int64_t K) {
+    return v.workspace ? v.workspace(v, (int)M, (int)N, (int)K) : 0;
+}
+
+int ensure_workspace(int dev, size_t bytes) {
+    if (bytes == 0) return LIN_OK;
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace& w = workspaces()[dev];
+    if (w.bytes >= bytes) return LIN_OK;
+    if (hipDeviceSynchronize() != hipSuccess) return LIN_ERR_HIP;
+    if (w.ptr) (void)hipFree(w.ptr);
+    w.ptr = nullptr;
+    w.bytes = 0;
+    const size_t want = bytes + (bytes >> 2);   // headroom for nearby shapes
+    if (hipMalloc(&w.ptr, want) != hipSuccess) {
+        w.ptr = nullptr;
+        return LIN_ERR_HIP;
+    }
+    if (hipMemset(w.ptr, 0, want) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+        return LIN_ERR_HIP;
+    w.bytes = want;
+    return LIN_OK;
+}
+
 int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
                    hipEvent_t ev1 = nullptr) {
     const Variant& v = registry()[vi];
@@ -148,6 +184,17 @@ int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = 
     size_t lds = 0;
     if (!v.geometry(v, a.M, a.N, a.K, &grid, &lds)) return LIN_ERR_UNSUPPORTED;
     KArgs args = a;
+    args.splits = v.cfg.algo == LIN_ALGO_MFMA ? v.cfg.split : 1;
+    args.ws = nullptr;
+    const size_t need = workspace_need(v, a.M, a.N, a.K);
+    if (need) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return LIN_ERR_HIP;
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = workspaces().find(dev);
+        if (it == workspaces().end() || it->second.bytes < need) return LIN_ERR_UNSUPPORTED;
+        args.ws = it->second.ptr;
+    }
     void* params[] = {(void*)&args};
     hipError_t e;
     if (ev0 || ev1)
@@ -184,7 +231,7 @@ int run(int kind, const void* W, const void* S, const void* x, float* y, int64_t
     if (st != LIN_OK) return st > 0 ? LIN_OK : st;
     const int vi = lookup(kind, M, N, K);
     if (vi < 0) return LIN_ERR_UNSUPPORTED;
-    KArgs a{W, S, x, y, (int)M, (int)N, (int)K};
+    KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr};
     return launch_variant(vi, a, (hipStream_t)stream);
 }
 
@@ -264,7 +311,7 @@ int lin_get_config(int kind, int64_t M, int64_t N, int64_t K, lin_config* out) {
     return LIN_OK;
 }
 
-int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg) {
+static int set_config_table(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg) {
     int n = lin_num_candidates(kind, M, N, K);
     if (n < 0) return n;
     const int dev = current_device();
@@ -278,6 +325,34 @@ int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* 
     if (vi < 0) return LIN_ERR_UNSUPPORTED;
     table()[Key(dev, kind, M, N, K)] = vi;
     return LIN_OK;
+}
+
+}  // extern "C"
+
+namespace lin {
+namespace {
+int set_config_reserving(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg) {
+    if (cfg) {
+        int n = lin_num_candidates(kind, M, N, K);
+        if (n < 0) return n;
+        const int vi = find_variant(kind, M, N, K, *cfg);
+        if (vi < 0) return LIN_ERR_UNSUPPORTED;
+        const int dev = current_device();
+        if (dev < 0) return LIN_ERR_HIP;
+        int rc = ensure_workspace(dev, workspace_need(registry()[vi], M, N, K));
+        if (rc != LIN_OK) return rc;
+    }
+    return LIN_OK;
+}
+}  // namespace
+}  // namespace lin
+
+extern "C" {
+
+int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg) {
+    int rc = set_config_reserving(kind, M, N, K, cfg);
+    if (rc != LIN_OK) return rc;
+    return set_config_table(kind, M, N, K, cfg);
 }
 
 int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, void* stream) {
@@ -316,13 +391,16 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
             fl->bytes = flush_bytes;
         }
     }
+    size_t ws_max = 0;
+    for (int vi : cand) ws_max = std::max(ws_max, workspace_need(registry()[vi], M, N, K));
+    if (int rc0 = ensure_workspace(dev, ws_max)) return rc0;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return LIN_ERR_HIP;
     if (hipEventCreate(&e1) != hipSuccess) {
         (void)hipEventDestroy(e0);
         return LIN_ERR_HIP;
     }
-    KArgs a{W, S, x, y, (int)M, (int)N, (int)K};
+    KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr};
     const int reps = 7;
     int best = -1;
     float best_us = 0.f;

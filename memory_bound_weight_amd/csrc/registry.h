@@ -22,6 +22,8 @@ struct Variant {
     // Workgroups and dynamic LDS bytes for a shape; returns false if the shape
     // does not fit this variant (for example LDS too small for K).
     bool (*geometry)(const Variant&, int M, int N, int K, dim3* grid, size_t* lds);
+    // Split-K workspace bytes this variant needs for a shape (0: none).
+    size_t (*workspace)(const Variant&, int M, int N, int K);
 };
 
 void register_gemv_bf16(std::vector<Variant>& out);

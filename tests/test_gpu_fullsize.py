@@ -1,0 +1,110 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (its tuning tables), on sampled outputs the oracle computes one by one.
+
+Weights are drawn on the GPU by the seeded generator; the sampled rows (and x)
+are copied back and handed to the oracle, so both sides see the same inputs.
+int4 weights come from the GPU quantiser; the sampled rows of its output must
+equal the oracle quantiser's output for the same bf16 rows, bit for bit."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_weight_amd as L
+import oracle
+import synth
+from gpu_util import assert_within_bound, u16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _sample_rows(N, k=40, seed=0):
+    rng = np.random.default_rng(seed + N)
+    rows = set([0, 1, N // 2, N - 2, N - 1]) | set(rng.integers(0, N, k).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N))
+
+
+def _tuned(model_name):
+    path = os.path.join(L.TUNING_DIR, "%s.json" % model_name)
+    if os.path.exists(path):
+        L.load_tuning(path)
+
+
+def _shapes(model):
+    seen = []
+    for layer, parts in synth.decode_groups(model, fused=True):
+        N = sum(p[2] for p in parts)
+        K = parts[0][3]
+        if (N, K) not in seen:
+            seen.append((N, K))
+    return seen
+
+
+@pytest.mark.parametrize("model", [synth.TINYLLAMA, synth.QWEN7B], ids=lambda m: m["name"])
+def test_decode_shapes_bf16_and_int4_sampled(model):
+    _tuned(model["name"])
+    for N, K in _shapes(model):
+        print("case fullsize %s %dx%d" % (model["name"], N, K), flush=True)
+        W = synth.weight(model["seed"], 0, 99, N, K, device=DEV)
+        x = synth.activation(model["seed"], 0, 99, 1, K, device=DEV)
+        rows = _sample_rows(N)
+        Wr = u16(W[torch.from_numpy(rows).to(DEV)])
+        xb = u16(x)
+        # bf16
+        y = L.lin_gemv_bf16(W, x)
+        torch.cuda.synchronize()
+        Y, B = oracle.gemm_dense(Wr, xb)
+        assert_within_bound(y[:, torch.from_numpy(rows).to(DEV)], Y, B, "bf16 %dx%d" % (N, K))
+        # int4-g64: GPU quantiser, checked against the oracle's on the sampled rows
+        Wq, S = L.lin_quantize_q4g64(W)
+        y4 = L.lin_gemv_q4g64(Wq, S, x)
+        torch.cuda.synchronize()
+        idx = torch.from_numpy(rows).to(DEV)
+        Wq_o, S_o = oracle.quantize_q4g64(Wr)
+        assert np.array_equal(Wq[idx].cpu().numpy(), Wq_o)
+        assert np.array_equal(u16(S[idx]), S_o)
+        Y4, B4 = oracle.gemm_q4g64(Wq_o, S_o, xb)
+        assert_within_bound(y4[:, idx], Y4, B4, "int4 %dx%d" % (N, K))
+        del W, Wq, S
+
+
+def test_single_gemv_full_oracle():
+    N, K = synth.SINGLE_SHAPE
+    W = synth.weight(synth.SINGLE_SEED, 0, 0, N, K, device=DEV)
+    x = synth.activation(synth.SINGLE_SEED, 0, 0, 1, K, device=DEV)
+    y = L.lin_gemv_bf16(W, x)
+    torch.cuda.synchronize()
+    Y, B = oracle.gemm_dense(u16(W), u16(x))
+    assert_within_bound(y, Y, B, "single 2048x2048")
+
+
+@pytest.mark.parametrize("M", list(synth.MISTRAL_M))
+def test_mistral_skinny_sampled(M):
+    for N, K in synth.MISTRAL_SHAPES:
+        print("case skinny full M=%d %dx%d" % (M, N, K), flush=True)
+        W = synth.weight(synth.MISTRAL_SEED, 0, N, N, K, device=DEV)
+        X = synth.activation(synth.MISTRAL_SEED, 0, N, M, K, device=DEV)
+        Y = L.lin_gemm_skinny_bf16(W, X)
+        torch.cuda.synchronize()
+        rows = _sample_rows(N, k=12 if M == 256 else 24)
+        idx = torch.from_numpy(rows).to(DEV)
+        Yo, Bo = oracle.gemm_dense(u16(W[idx]), u16(X))
+        assert_within_bound(Y[:, idx], Yo, Bo, "skinny M=%d %dx%d" % (M, N, K))
+
+
+def test_maximum_k():
+    K = 1 << 22   # LIN_MAX_K
+    for N in (3,):
+        W = synth.weight(8000, 0, 0, N, K, device=DEV)
+        x = synth.activation(8000, 0, 0, 2, K, device=DEV)
+        y = L.lin_gemv_bf16(W, x)
+        Wq, S = L.lin_quantize_q4g64(W)
+        y4 = L.lin_gemv_q4g64(Wq, S, x)
+        torch.cuda.synchronize()
+        Y, B = oracle.gemm_dense(u16(W), u16(x))
+        assert_within_bound(y, Y, B, "bf16 K=2^22")
+        Wq_o, S_o = oracle.quantize_q4g64(u16(W))
+        Y4, B4 = oracle.gemm_q4g64(Wq_o, S_o, u16(x))
+        assert_within_bound(y4, Y4, B4, "int4 K=2^22")

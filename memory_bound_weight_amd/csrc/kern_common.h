@@ -132,10 +132,10 @@ __device__ __forceinline__ void for_each_reduced(const float (&v)[V], int lane, 
         if (reduce_writer<V>(s, lane)) f(reduce_index<V>(s, lane), v[s]);
 }
 
-// Split-K workspace: one 32-bit counter per output tile, padded to 256 bytes,
-// followed by the partial tiles.
-__host__ __device__ inline size_t ws_counter_bytes(int tiles) {
-    return ((size_t)tiles * 4 + 255) / 256 * 256;
-}
+// Split-K workspace: a fixed region of 32-bit tile counters (zero whenever no
+// kernel runs) followed by the partial tiles.  The counter region never holds
+// partial data, so shapes with different tile counts can share the workspace.
+constexpr int kMaxTileCounters = 1 << 16;
+__host__ __device__ inline size_t ws_counter_bytes(int) { return (size_t)kMaxTileCounters * 4; }
 
 }  // namespace lin

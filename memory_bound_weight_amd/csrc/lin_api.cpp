@@ -73,6 +73,8 @@ int find_variant(int kind, int64_t M, int64_t N, int64_t K, const lin_config& cf
     return -1;
 }
 
+size_t workspace_need(const Variant& v, int64_t M, int64_t N, int64_t K);
+
 // Built-in choice for shapes that were neither tuned nor pinned.
 int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
     lin_config want{};
@@ -85,19 +87,20 @@ int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
         want.split = N >= 4096 ? 1 : (N >= 1024 ? 2 : 4);
     } else {
         if (kind == LIN_KIND_SKINNY_BF16 && M > 16) {
-            // matrix cores: a token tile covering M (up to 128), two W fragments
-            // per wavefront for small tiles
-            lin_config mf{};
-            mf.algo = LIN_ALGO_MFMA;
-            mf.tile_m = mt < 32 ? 32 : (mt > 128 ? 128 : mt);
-            mf.rows = mf.tile_m >= 128 ? 64 : 128;
-            mf.unroll = 1;
-            mf.split = 1;
-            mf.stage_x = 1;
-            int i = find_variant(kind, M, N, K, mf);
-            if (i >= 0) return i;
-            for (int j : candidates(kind, M, N, K))
-                if (registry()[j].cfg.algo == LIN_ALGO_MFMA) return j;
+            // matrix cores without split-K (the default never needs the
+            // workspace): the k-block variant whose token tile covers M best
+            const int tm = mt < 32 ? 32 : (mt > 128 ? 128 : mt);
+            int best = -1;
+            for (int i : candidates(kind, M, N, K)) {
+                const Variant& v = registry()[i];
+                if (v.cfg.algo != LIN_ALGO_MFMA || v.cfg.stage_x != 1 || v.cfg.split != 1) continue;
+                if (v.cfg.tile_m != tm || v.cfg.rows != 64) continue;
+                if (best < 0 || v.cfg.unroll == 4) best = i;
+            }
+            if (best >= 0) return best;
+            for (int i : candidates(kind, M, N, K))
+                if (registry()[i].cfg.algo == LIN_ALGO_MFMA && workspace_need(registry()[i], M, N, K) == 0)
+                    return i;
         }
         want.rows = mt <= 1 ? (N >= 8192 ? 2 : 1) : (mt <= 8 ? 2 : 1);
         want.unroll = mt <= 1 ? (want.rows == 1 ? 4 : 2) : (mt <= 8 ? 2 : 1);

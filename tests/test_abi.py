@@ -109,3 +109,13 @@ def test_candidate_enumeration():
         L.lin_candidate(0, 1, 8, 8, 10 ** 6)
     assert L._lib.lin_num_candidates(0, 1, 8, 12) == L.LIN_ERR_SHAPE
     assert L._lib.lin_num_candidates(5, 1, 8, 8) == L.LIN_ERR_ARG
+
+
+def test_default_skinny_config_needs_no_workspace():
+    """Without tuning or pinning, a product call must never need the split-K
+    workspace (it is only created by the load-time calls)."""
+    for M in (17, 32, 33, 64, 100, 128, 200, 256):
+        for N, K in ((1024, 4096), (14336, 4096), (4096, 14336), (300, 4104)):
+            c = L.lin_get_config(L.LIN_KIND_SKINNY_BF16, M, N, K)
+            if c["algo"] == L.LIN_ALGO_MFMA:
+                assert c["split"] == 1 and c["stage_x"] == 1, (M, N, K, c)

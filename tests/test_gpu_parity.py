@@ -249,3 +249,24 @@ def test_output_rows_past_n_untouched():
                     L.lin_gemv_q4g64(Wq, S, X.to(DEV), y)
                 torch.cuda.synchronize()
                 assert torch.all(buf[M * N:] == 12345.0), cfg
+
+
+def test_split_k_workspace_shared_across_shapes():
+    """Split-K configurations of shapes with few and with many output tiles run
+    one after another on the shared workspace; each must stay exact to the
+    bound (the tile counters live in a region partial tiles never touch)."""
+    cases = [(64, 130, 4096), (64, 4096, 4096), (40, 200, 2048), (64, 2000, 4096)]
+    data = []
+    for M, N, K in cases:
+        W, X = _inputs(9300 + N, M, N, K)
+        data.append((M, N, K, W.to(DEV), X.to(DEV), oracle.gemm_dense(u16(W), u16(X))))
+    for rep in range(2):
+        for M, N, K, Wd, Xd, (Y, B) in data:
+            splits = [c for c in L.lin_candidates(L.LIN_KIND_SKINNY_BF16, M, N, K)
+                      if c["algo"] == L.LIN_ALGO_MFMA and (c["split"] != 1 or c["stage_x"] == 2)]
+            assert splits
+            for cfg in splits:
+                with pinned(L.LIN_KIND_SKINNY_BF16, M, N, K, cfg):
+                    y = L.lin_gemm_skinny_bf16(Wd, Xd)
+                    torch.cuda.synchronize()
+                    assert_within_bound(y, Y, B, "split-K %dx%dx%d %s" % (M, N, K, cfg))

@@ -247,6 +247,127 @@ def measured_traffic(key, shapes_mix):
     return None
 
 
+# ---------------------------------------------------------------- batched tokens
+
+MFMA_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix-core peak
+
+
+class SkinnyCase:
+    """One batched-token product Y = X . W^T of a Mistral-7B-shaped matrix."""
+
+    def __init__(self, M, N, K):
+        self.M, self.N, self.K = M, N, K
+        self.bytes = bytes_bf16(N, K, M)
+        self.flop = 2 * M * N * K
+        self.key = (L.LIN_KIND_SKINNY_BF16, M, N, K)
+
+    @property
+    def name(self):
+        return "M%d %dx%d" % (self.M, self.N, self.K)
+
+
+def skinny_variant(c):
+    cfg = L.lin_get_config(L.LIN_KIND_SKINNY_BF16, c.M, c.N, c.K)
+    if cfg["algo"] == L.LIN_ALGO_MFMA:
+        return "mfma rows%d tm%d D%d S%d X%d" % (cfg["rows"], cfg["tile_m"], cfg["unroll"],
+                                                cfg["split"], cfg["stage_x"])
+    return "valu R%d U%d S%d X%d tm%d" % (cfg["rows"], cfg["unroll"], cfg["split"],
+                                         cfg["stage_x"], cfg["tile_m"])
+
+
+def run_skinny(args, dev):
+    """Every (shape, M) product of the batched-decode workload: per case, a graph
+    of back-to-back launches cycling over enough distinct weight copies to
+    exceed the 256 MB last-level cache (so each launch streams W from HBM);
+    the step is one launch of every case."""
+    cases = [SkinnyCase(M, N, K) for M in synth.MISTRAL_M for N, K in synth.MISTRAL_SHAPES]
+    tfile = args.tuning or os.path.join(L.TUNING_DIR, "mistral-7b-skinny.json")
+    ok, stale = L.load_tuning(tfile) if (os.path.exists(tfile) and not args.tune) else ([], [])
+    weights = {}
+    for N, K in synth.MISTRAL_SHAPES:
+        copies = max(2, -(-(600 << 20) // (2 * N * K)))
+        weights[(N, K)] = [synth.weight(synth.MISTRAL_SEED, 0, N + i, N, K, device=dev)
+                           for i in range(copies)]
+    X = {(M, K): synth.activation(synth.MISTRAL_SEED, 0, 0, M, K, device=dev)
+         for M in synth.MISTRAL_M for K in {k for _, k in synth.MISTRAL_SHAPES}}
+    Y = {c.key: torch.empty((c.M, c.N), dtype=torch.float32, device=dev) for c in cases}
+    tuned = {}
+    for c in cases:
+        if c.key in ok:
+            continue
+        cfg = L.lin_autotune(L.LIN_KIND_SKINNY_BF16, weights[(c.N, c.K)][0], X[(c.M, c.K)],
+                             Y[c.key])
+        tuned[c.key] = cfg
+        log("tuned skinny %-16s -> %s" % (c.name, cfg))
+    if tuned:
+        entries = {k: L.lin_get_config(*k) for k in (c.key for c in cases)}
+        L.save_tuning(tfile, entries)
+    tuning = "%s (%d cases, %d tuned now)" % (os.path.relpath(tfile, ROOT), len(cases), len(tuned))
+
+    def graph_of(fn_list):
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for f in fn_list:
+                f()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for f in fn_list:
+                f()
+        torch.cuda.synchronize()
+        return g
+
+    def call(c, i):
+        Wc = weights[(c.N, c.K)]
+        return lambda: L.lin_gemm_skinny_bf16(Wc[i % len(Wc)], X[(c.M, c.K)], Y[c.key])
+
+    reps = max(5, args.steps // 2)
+    per_case = {}
+    for c in cases:
+        n = max(32, 2 * len(weights[(c.N, c.K)]))
+        g = graph_of([call(c, i) for i in range(n)])
+        _, gpu = time_graph(g, reps, 2)
+        us = gpu / n * 1e6
+        floor_us = max(c.bytes / (HBM_PEAK_GBS * 1e3), c.flop / (MFMA_PEAK_TFS * 1e6))
+        per_case[c.name] = {"variant": skinny_variant(c), "us": round(us, 3),
+                            "GB_s": round(c.bytes / us / 1e3, 1),
+                            "TFLOP_s": round(c.flop / us / 1e6, 1),
+                            "hbm_frac": round(c.bytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                            "mfma_frac": round(c.flop / us / 1e6 / MFMA_PEAK_TFS, 4),
+                            "roofline_time_frac": round(floor_us / us, 4),
+                            "tok_s": round(c.M / us * 1e6, 1)}
+        log("skinny %-16s %-34s %8.2f us %7.1f GB/s %6.1f TFLOP/s  %.0f%% of roofline time"
+            % (c.name, per_case[c.name]["variant"], us, c.bytes / us / 1e3, c.flop / us / 1e6,
+               100 * floor_us / us))
+        del g
+    step = graph_of([call(c, 0) for c in cases])
+    wall, gpu = time_runs([step.replay], args.steps, args.warmup)
+    step_bytes = sum(c.bytes for c in cases)
+    dom = max(cases, key=lambda c: per_case[c.name]["us"])
+    d = per_case[dom.name]
+    roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": d["hbm_frac"], "traffic": None, "kernel": d["variant"], "case": dom.name,
+                "avg_launch_us": d["us"], "bytes_per_launch": dom.bytes,
+                "mfma": {"achieved": d["TFLOP_s"], "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": d["mfma_frac"]}}
+    out = {"metric": METRIC, "value": round(step_bytes / wall / 1e9, 1), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16 weights and tokens, fp32 accumulate",
+           "data": "synthetic",
+           "config": {"workload": "mistral-7b-shaped batched-decode products, M in %s tokens x %d "
+                      "shapes, one launch each per step" % (list(synth.MISTRAL_M),
+                                                          len(synth.MISTRAL_SHAPES)),
+                      "bytes_per_step": step_bytes, "tuning": tuning},
+           "pct_of_hbm_peak": round(100.0 * step_bytes / wall / 1e9 / HBM_PEAK_GBS, 2),
+           "gpu_ms_per_step": round(gpu * 1e3, 4), "cases": per_case, "roofline": roofline}
+    if not args.skip_cpu:
+        out["cpu_baseline"] = cpu_baseline_skinny(min(16, os.cpu_count() or 1))
+    print(json.dumps(out), flush=True)
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(model, layers, threads):
@@ -287,6 +408,28 @@ def cpu_baseline(model, layers, threads):
                       % (model["name"], layers - 1, len(work) // 2, total_bytes / 1e6, dt)}
 
 
+def cpu_baseline_skinny(threads, rows=96):
+    """The oracle on a bounded sample of the batched workload: the first `rows`
+    rows of every shape against all M tokens, for every M."""
+    import oracle
+    work = []
+    for M in synth.MISTRAL_M:
+        for N, K in synth.MISTRAL_SHAPES:
+            W = synth.bits(synth.weight(synth.MISTRAL_SEED, 0, N, N, K)[:rows])
+            Xb = synth.bits(synth.activation(synth.MISTRAL_SEED, 0, 0, M, K))
+            work.append((W, Xb, bytes_bf16(rows, K, M)))
+    total = sum(w[2] for w in work)
+    jobs = [(W[lo:lo + 8], Xb) for W, Xb, _ in work for lo in range(0, W.shape[0], 8)]
+    t0 = time.perf_counter()
+    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda j: oracle.gemm_dense(*j), jobs))
+    dt = time.perf_counter() - t0
+    return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "first %d rows of each of the %d shapes x M in %s, fp64 sequential sums, "
+                      "%.2f s wall" % (rows, len(synth.MISTRAL_SHAPES), list(synth.MISTRAL_M), dt)}
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -294,7 +437,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="tinyllama", choices=["tinyllama", "qwen7b"])
+    ap.add_argument("--workload", default="tinyllama", choices=["tinyllama", "qwen7b", "mistral-skinny"])
     ap.add_argument("--tune", action="store_true",
                     help="re-run lin_autotune for every shape and rewrite the tuning table")
     ap.add_argument("--tuning", default=None, help="tuning table path")
@@ -321,6 +464,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
+        return
+    if args.workload == "mistral-skinny":
+        run_skinny(args, dev)
         return
     model = synth.TINYLLAMA if args.workload == "tinyllama" else synth.QWEN7B
     log("building %s weight sets on %s" % (model["name"], torch.cuda.get_device_name(dev)))

@@ -200,10 +200,12 @@ def test_results_are_deterministic():
             b = L.lin_gemv_bf16(Wd, Xd)
             torch.cuda.synchronize()
             assert torch.equal(a, b)
-    a = L.lin_gemv_q4g64(Wq, S, Xd)
-    b = L.lin_gemv_q4g64(Wq, S, Xd)
-    torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    for cfg in L.lin_candidates(L.LIN_KIND_GEMV_Q4G64, 1, N, K)[::3]:
+        with pinned(L.LIN_KIND_GEMV_Q4G64, 1, N, K, cfg):
+            a = L.lin_gemv_q4g64(Wq, S, Xd)
+            b = L.lin_gemv_q4g64(Wq, S, Xd)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), cfg
 
 
 def test_empty_and_degenerate_shapes():
@@ -235,8 +237,8 @@ def test_empty_and_degenerate_shapes():
 
 def test_output_rows_past_n_untouched():
     """The kernels never write outside y: a guard band after y keeps its values."""
-    for kind, N, K in [(L.LIN_KIND_GEMV_BF16, 37, 1032), (L.LIN_KIND_GEMV_Q4G64, 37, 1088)]:
-        M = 3
+    for kind, N, K, M in [(L.LIN_KIND_GEMV_BF16, 37, 1032, 3), (L.LIN_KIND_GEMV_Q4G64, 37, 1088, 3),
+                          (L.LIN_KIND_GEMV_Q4G64, 37, 1088, 1), (L.LIN_KIND_GEMV_Q4G64, 300, 3584, 1)]:
         W, X = _inputs(7000 + N, M, N, K)
         buf = torch.full((M * N + 256,), 12345.0, device=DEV)
         y = buf[:M * N].view(M, N)

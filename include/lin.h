@@ -77,9 +77,10 @@ typedef enum lin_algo {
  * workgroup tile, `unroll` = k-blocks of 64 in flight per workgroup, `split` =
  * workgroups sharing one output tile by splitting K (their partial tiles go
  * through a library-owned workspace and are added in a fixed order, so results
- * stay deterministic); `stage_x` = 1 stages a 64-k block of X per step, 2
- * stages a whole K-slice of X once (then `split` is 0: the number of slices
- * follows from K and the tile).  `us` is filled by lin_autotune (median microseconds per
+ * stay deterministic); `stage_x` = 1: W streams through registers and a
+ * 64-k block of X is staged in LDS per step; `stage_x` = 3: W and X blocks
+ * both stream through an LDS ring of `unroll` stages filled by direct
+ * global-to-LDS loads.  `us` is filled by lin_autotune (median microseconds per
  * call, cold caches) and ignored on input. */
 typedef struct lin_config {
     int32_t algo;

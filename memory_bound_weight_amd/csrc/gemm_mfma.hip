@@ -260,162 +260,6 @@ __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
     finish_tile<NF, TM>(a, acc, S, ks, n_tile, m_tile, m_tiles, n_tiles, n0, m0);
 }
 
-// K-slice variant for small token counts (HBM-bound regime).  A workgroup
-// stages its tokens' X over a whole K-slice into LDS once (64 KB: TM x KS
-// with TM * KS = 32768; 16-byte chunk c of token row m at slot c ^ (m mod 16),
-// so the 16 rows an A-fragment read touches hit 16 different bank groups),
-// then each wavefront streams its W rows through a ring of D register stages
-// with no further barrier.  The K-slices of a tile are added by the split-K
-// reduction; the partial tiles cost 2 TM / KS of the W bytes.
-template <int NF, int TM, int D>
-__global__ __launch_bounds__(kBlock) void gemm_mfma_xs_kernel(KArgs a) {
-    constexpr int BN = 64 * NF;
-    constexpr int MT = TM / 16;
-    constexpr int KS = 32768 / TM;   // k per slice
-    constexpr int KC = KS / 8;       // 16-byte chunks per staged row
-    constexpr int BLOCKS = KS / 64;  // 64-k blocks (two MFMA steps) per slice
-    static_assert(KC >= 16, "slice too short for the swizzle");
-    const int M = a.M, N = a.N, K = a.K;
-    const int S = (K + KS - 1) / KS;
-    const int lane = threadIdx.x & 63;
-    const int wave = wave_id();
-    const int l16 = lane & 15, lg = lane >> 4;
-
-    const int m_tiles = (M + TM - 1) / TM;
-    const int n_tiles = (N + BN - 1) / BN;
-    const int t = blockIdx.x / S;
-    const int ks = blockIdx.x - t * S;
-    const int n_tile = t / m_tiles;
-    const int m_tile = t - n_tile * m_tiles;
-    const int n0 = n_tile * BN + wave * 16 * NF;
-    const int m0 = m_tile * TM;
-    const int k0 = ks * KS;
-    const int blocks = min(BLOCKS, (K - k0 + 63) / 64);
-
-    __shared__ u32x4 xs[TM * KC];
-
-    const uint16_t* __restrict__ W = (const uint16_t*)a.W;
-    const uint16_t* __restrict__ X = (const uint16_t*)a.X;
-    const uint8_t* wrow[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        int n = n0 + f * 16 + l16;
-        n = n < N ? n : N - 1;   // rows past N are computed, never stored
-        wrow[f] = (const uint8_t*)(W + (int64_t)n * K);
-    }
-    // k order inside a 64-k block: MFMA step h of lane group lg covers
-    // k = 64 b + 16 lg + 8 h, so a lane's two loads are 32 contiguous bytes and
-    // the four lane groups read each row's 128-byte line in one go.  A and B
-    // use the same order, which leaves every product sum unchanged.
-    auto load_w = [&](u32x4 (&wr)[NF][2], int b) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int k = k0 + b * 64 + lg * 16 + h * 8;
-                wr[f][h] = k < K ? load_w16(wrow[f], (uint32_t)k * 2u) : u32x4{0, 0, 0, 0};
-            }
-    };
-
-    // W ring first, so its loads are in flight while X is staged
-    u32x4 ring[D][NF][2];
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-        if (d < blocks) load_w(ring[d], d);
-
-    constexpr int XCH = TM * KC / kBlock;   // X chunks per thread
-    constexpr int XB = 8;                   // staged in batches of 8 loads
-    static_assert(XCH % XB == 0, "chunk count");
-#pragma unroll
-    for (int b = 0; b < XCH; b += XB) {
-        u32x4 xr[XB];
-#pragma unroll
-        for (int i = 0; i < XB; ++i) {
-            const int q = threadIdx.x + kBlock * (b + i);
-            const int m = q / KC, c = q - (q / KC) * KC;
-            const int gm = m0 + m, k = k0 + c * 8;
-            xr[i] = (gm < M && k < K) ? load_x16((const uint8_t*)(X + (int64_t)gm * K), (uint32_t)k * 2u)
-                                      : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < XB; ++i) {
-            const int q = threadIdx.x + kBlock * (b + i);
-            const int m = q / KC, c = q - (q / KC) * KC;
-            xs[m * KC + (c ^ (m & 15))] = xr[i];
-        }
-    }
-    __syncthreads();
-
-    f32x4 acc[NF][MT];
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int u = 0; u < MT; ++u) acc[f][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int base = 0; base < blocks; base += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int b = base + d;
-            if (b >= blocks) break;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int c = b * 8 + lg * 2 + h;   // chunk of k = 64 b + 16 lg + 8 h
-#pragma unroll
-                for (int u = 0; u < MT; ++u) {
-                    const int m = u * 16 + l16;
-                    const u32x4 av = xs[m * KC + (c ^ (m & 15))];
-#pragma unroll
-                    for (int f = 0; f < NF; ++f) acc[f][u] = mfma16(av, ring[d][f][h], acc[f][u]);
-                }
-            }
-            if (b + D < blocks) load_w(ring[d], b + D);
-        }
-    }
-    finish_tile<NF, TM>(a, acc, S, ks, n_tile, m_tile, m_tiles, n_tiles, n0, m0);
-}
-
-template <int NF, int TM, int D>
-static bool geom_mfma_xs(const Variant&, int M, int N, int K, dim3* grid, size_t* lds) {
-    if (K <= 0) return false;
-    if (TM > 16 && M <= TM / 2) return false;    // a smaller token tile fits
-    constexpr int BN = 64 * NF;
-    constexpr int KS = 32768 / TM;
-    const int S = (K + KS - 1) / KS;
-    const int tiles = ((M + TM - 1) / TM) * ((N + BN - 1) / BN);
-    if (S > 1 && tiles > kMaxTileCounters) return false;
-    *grid = dim3((unsigned)(tiles * S));
-    *lds = 0;
-    return true;
-}
-
-template <int NF, int TM, int D>
-static size_t ws_mfma_xs(const Variant&, int M, int N, int K) {
-    constexpr int BN = 64 * NF;
-    constexpr int KS = 32768 / TM;
-    const int S = (K + KS - 1) / KS;
-    if (S <= 1) return 0;
-    const size_t tiles = (size_t)((M + TM - 1) / TM) * ((N + BN - 1) / BN);
-    return ws_counter_bytes((int)tiles) + (size_t)S * tiles * TM * BN * sizeof(float);
-}
-
-template <int NF, int TM, int D>
-static void add_xs(std::vector<Variant>& out) {
-    Variant v{};
-    v.kind = LIN_KIND_SKINNY_BF16;
-    v.cfg.algo = LIN_ALGO_MFMA;
-    v.cfg.rows = 64 * NF;
-    v.cfg.unroll = D;
-    v.cfg.split = 0;     // K / (32768 / tile_m) slices, fixed by the shape
-    v.cfg.stage_x = 2;   // K-slice of X staged once
-    v.cfg.tile_m = TM;
-    v.mt = 0;
-    v.min_m = 16;
-    v.func = (const void*)&gemm_mfma_xs_kernel<NF, TM, D>;
-    v.geometry = &geom_mfma_xs<NF, TM, D>;
-    v.workspace = &ws_mfma_xs<NF, TM, D>;
-    out.push_back(v);
-}
-
 template <int NF, int TM, int D>
 static bool geom_mfma(const Variant& v, int M, int N, int K, dim3* grid, size_t* lds) {
     if (K <= 0) return false;
@@ -471,10 +315,6 @@ static void add_splits(std::vector<Variant>& out) {
 }
 
 void register_gemm_mfma(std::vector<Variant>& out) {
-    add_xs<1, 32, 4>(out);
-    add_xs<2, 32, 4>(out);
-    add_xs<1, 64, 4>(out);
-    add_xs<2, 64, 2>(out);
     add_splits<1, 32, 4>(out);
     add_splits<1, 32, 8>(out);
     add_splits<1, 64, 2>(out);

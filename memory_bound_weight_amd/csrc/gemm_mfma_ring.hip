@@ -1,0 +1,317 @@
+// Matrix-core product Y = X . W^T with both operands streamed through an LDS
+// ring filled by direct-to-LDS loads (gfx950 global_load_lds_dwordx4).
+//
+// Why.  Batched decode keeps the product memory-bound up to a few hundred
+// tokens (llm-rs benchmark post, section 3), so what matters is how many
+// weight bytes each compute unit keeps in flight: under full load HBM
+// latency is several microseconds, and a register ring of a few k-blocks per
+// workgroup leaves the chip latency-bound.  A direct-to-LDS load moves 16
+// bytes per lane from memory into LDS without passing through registers, so
+// the ring depth is bounded by the 160 KB of LDS instead of the register
+// file, and the loads of D k-blocks are in flight at once.  Pipelining and
+// bank-conflict-free staging follow section 5 of the same post; the data
+// path is CDNA4's own.
+//
+// Ring.  A stage holds one 64-k block: BN/16 x 2 W fragments and TM/16 x 2 X
+// fragments, each fragment 1 KB in the order v_mfma_f32_16x16x32_bf16 reads
+// its operands (lane l: row l mod 16, k 8 (l / 16) .. + 7 of a 32-k half), so
+// that a wavefront loads a fragment with one instruction (64 lanes x 16 B,
+// placed in lane order) and reads it back with one conflict-free
+// ds_read_b128.  The four wavefronts share the loads of a stage.  Iteration i
+// waits (vmcnt) until its own loads of stage i have landed, meets the others
+// at one s_barrier (their loads have landed too, and everyone has finished
+// reading stage i - 1), refills the slot of stage i - 1 with stage i + D - 1,
+// then multiplies stage i.  k past K reads from a zero word, rows past N or
+// M re-read the last row (never stored).
+//
+// Wave tile.  The workgroup tile BN x TM is split 2 x 2 (or 1 x 4 when TM is
+// 256) among the four wavefronts; each keeps its NF x MT 16x16 fp32
+// accumulators in registers and writes them directly, or as a split-K partial
+// that the last workgroup of the tile adds in split order (deterministic).
+#include "registry.h"
+
+namespace lin {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// One direct-to-LDS load: 16 bytes per lane from `g` into LDS at the
+// wavefront-uniform address `lds` + 16 * lane (ordinary cache policy: a
+// non-temporal hint on the weights measured slower).  Written as inline assembly so
+// that the compiler does not treat every later LDS read as waiting on it
+// (it would wait for all outstanding loads, which empties the ring); the
+// kernel orders the ring itself with vmcnt waits and barriers.  M0 is only
+// set here: nothing else in these kernels uses it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved: set here, used by nothing else
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS const void*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// k >= K lanes load these zeros instead of reading past a row.
+__device__ __attribute__((aligned(16))) const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
+
+// s_waitcnt with vmcnt <= N (N < 64) and lgkmcnt = 0; expcnt not waited on.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+template <int L, int D, int J = 0>
+__device__ __forceinline__ void wait_stages(int after) {
+    if constexpr (J <= D - 2) {
+        if (after == J) {
+            wait_vm_lgkm0<J * L>();
+            return;
+        }
+        wait_stages<L, D, J + 1>(after);
+    } else {
+        wait_vm_lgkm0<0>();
+    }
+}
+
+// Wave tile of a workgroup tile: NW wavefronts as WR x WC; KB k per stage
+// (eight wavefronts and 128-k stages measured no faster than 4 and 64).
+template <int BN, int TM, int NW, int KB>
+struct Shape {
+    static constexpr int WR = NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4);
+    static constexpr int WC = NW / WR;
+    static constexpr int WN = BN / WR, WM = TM / WC;
+    static constexpr int NF = WN / 16, MT = WM / 16;
+    static constexpr int H = KB / 32;                  // 32-k halves per stage
+    static constexpr int FW = BN / 16 * H, FX = TM / 16 * H, F = FW + FX;
+    static constexpr int L = F / NW;                   // fragment loads per wavefront and stage
+    static_assert(NF >= 1 && MT >= 1 && F % NW == 0, "tile shape");
+};
+
+template <int BN, int TM, int D, int NW, int KB>
+__global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
+    using SH = Shape<BN, TM, NW, KB>;
+    constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, F = SH::F, L = SH::L, H = SH::H;
+    const int M = a.M, N = a.N, K = a.K;
+    const int S = a.splits;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    const int m_tiles = (M + TM - 1) / TM;
+    const int n_tiles = (N + BN - 1) / BN;
+    int n_tile, m_tile, ks;
+    if (S == 1) {   // XCD-aware: the token tiles of one W block run on one XCD
+        const int b = blockIdx.x;
+        const int xcd = b & 7, loc = b >> 3;
+        n_tile = (loc / m_tiles) * 8 + xcd;
+        m_tile = loc - (loc / m_tiles) * m_tiles;
+        ks = 0;
+        if (n_tile >= n_tiles) return;   // padding slot: whole workgroup leaves together
+    } else {        // the splits of one tile are consecutive
+        const int t = blockIdx.x / S;
+        ks = blockIdx.x - t * S;
+        n_tile = t / m_tiles;
+        m_tile = t - n_tile * m_tiles;
+    }
+    const int nkb_all = (K + KB - 1) / KB;
+    const int bps = (nkb_all + S - 1) / S;
+    const int kb0 = ks * bps;
+    const int nkb = max(0, min(nkb_all, kb0 + bps) - kb0);
+
+    __shared__ u32x4 ring[D][F][64];
+
+    // Fragments this wavefront loads per stage: f = wave * L + i.  Per lane a
+    // fixed row pointer; the k offset moves with the stage.
+    const uint8_t* src[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int f = wave * L + i;
+        if (f < FW) {
+            int n = n_tile * BN + (f / H) * 16 + l16;
+            n = n < N ? n : N - 1;
+            src[i] = (const uint8_t*)a.W + (int64_t)n * K * 2;
+        } else {
+            int m = m_tile * TM + ((f - FW) / H) * 16 + l16;
+            m = m < M ? m : M - 1;
+            src[i] = (const uint8_t*)a.X + (int64_t)m * K * 2;
+        }
+    }
+    auto issue = [&](int kb, int slot) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int f = wave * L + i;
+            const int k = kb * KB + (f % H) * 32 + lg * 8;
+            const void* p = k < K ? (const void*)(src[i] + (size_t)k * 2) : (const void*)&g_zero16;
+            dma16(p, &ring[slot][f][0]);
+        }
+    };
+
+    f32x4 acc[NF][MT];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int wr = wave / SH::WC, wc = wave - (wave / SH::WC) * SH::WC;
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (d < nkb) issue(kb0 + d, d);
+    for (int i = 0; i < nkb; ++i) {
+        wait_stages<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();                  // everyone's loads of stage i landed
+        asm volatile("" ::: "memory");
+        if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
+        const int slot = i % D;
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+            u32x4 bw[NF], ax[MT];
+#pragma unroll
+            for (int f = 0; f < NF; ++f) bw[f] = ring[slot][(wr * NF + f) * H + h][lane];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) ax[t] = ring[slot][FW + (wc * MT + t) * H + h][lane];
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int t = 0; t < MT; ++t) acc[f][t] = mfma16(ax[t], bw[f], acc[f][t]);
+        }
+    }
+
+    // Output: lane holds W row n0 + 16 f + l16, tokens m0 + 16 t + 4 lg + r.
+    const int n0 = n_tile * BN + wr * SH::WN;
+    const int m0 = m_tile * TM + wc * SH::WM;
+    if (S == 1) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const int n = n0 + f * 16 + l16;
+            if (n >= N) continue;
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m0 + t * 16 + lg * 4 + r;
+                    if (m < M) a.Y[(int64_t)m * N + n] = acc[f][t][r];
+                }
+        }
+        return;
+    }
+    // Split-K: publish the partial tile with coherent (agent-scope) stores, count
+    // the tile, and let the workgroup that completes the count add the S
+    // partials in split order.  Partial element (m, n) of a tile sits at
+    // m * BN + n (tile-local indices).
+    const int tiles = m_tiles * n_tiles;
+    const int tile = n_tile * m_tiles + m_tile;
+    uint32_t* cnt = (uint32_t*)a.ws;
+    float* parts = (float*)((uint8_t*)a.ws + ws_counter_bytes(tiles));
+    const size_t tile_elems = (size_t)TM * BN;
+    float* mine = parts + ((size_t)ks * tiles + tile) * tile_elems;
+    const int nl0 = wr * SH::WN, ml0 = wc * SH::WM;
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                __hip_atomic_store(&mine[(size_t)(ml0 + t * 16 + lg * 4 + r) * BN + nl0 + f * 16 + l16],
+                                   acc[f][t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);   // the partial stores are complete
+    __shared__ int last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        last = (old == (uint32_t)(S - 1));
+    }
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        const int n = n0 + f * 16 + l16;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const size_t e = (size_t)(ml0 + t * 16 + lg * 4 + r) * BN + nl0 + f * 16 + l16;
+                float v = 0.f;
+                for (int j = 0; j < S; ++j)
+                    v += __hip_atomic_load(&parts[((size_t)j * tiles + tile) * tile_elems + e],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int m = m0 + t * 16 + lg * 4 + r;
+                if (m < M && n < N) a.Y[(int64_t)m * N + n] = v;
+            }
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int BN, int TM, int D, int NW, int KB>
+bool geom_ring(const Variant& v, int M, int N, int K, dim3* grid, size_t* lds) {
+    if (K <= 0) return false;
+    if (TM > 32 && M <= TM / 2) return false;   // a smaller token tile fits
+    const int S = v.cfg.split;
+    const int m_tiles = (M + TM - 1) / TM;
+    const int n_tiles = (N + BN - 1) / BN;
+    const int nkb = (K + KB - 1) / KB;
+    if (S > 1 && nkb < 2 * S) return false;      // at least two k-blocks per split
+    if (S > 1 && m_tiles * n_tiles > kMaxTileCounters) return false;
+    if (S == 1)
+        *grid = dim3((unsigned)((n_tiles + 7) / 8 * 8 * m_tiles));
+    else
+        *grid = dim3((unsigned)(n_tiles * m_tiles * S));
+    *lds = 0;
+    return true;
+}
+
+template <int BN, int TM, int D, int NW, int KB>
+size_t ws_ring(const Variant& v, int M, int N, int K) {
+    (void)K;
+    const int S = v.cfg.split;
+    if (S <= 1) return 0;
+    const size_t tiles = (size_t)((M + TM - 1) / TM) * ((N + BN - 1) / BN);
+    return ws_counter_bytes((int)tiles) + (size_t)S * tiles * TM * BN * sizeof(float);
+}
+
+template <int BN, int TM, int D, int NW = 4, int KB = 64>
+void add_ring(std::vector<Variant>& out, int S) {
+    static_assert(D * Shape<BN, TM, NW, KB>::F * 1024 <= 160 * 1024, "LDS ring too large");
+    Variant v{};
+    v.kind = LIN_KIND_SKINNY_BF16;
+    v.cfg.algo = LIN_ALGO_MFMA;
+    v.cfg.rows = BN;
+    v.cfg.unroll = D;
+    v.cfg.split = S;
+    v.cfg.stage_x = 3;   // W and X blocks through an LDS ring of direct loads
+    v.cfg.tile_m = TM;
+    v.mt = 0;
+    v.min_m = 16;
+    v.func = (const void*)&gemm_mfma_ring_kernel<BN, TM, D, NW, KB>;
+    v.geometry = &geom_ring<BN, TM, D, NW, KB>;
+    v.workspace = &ws_ring<BN, TM, D, NW, KB>;
+    v.block = 64 * NW;
+    out.push_back(v);
+}
+
+}  // namespace
+
+void register_gemm_mfma_ring(std::vector<Variant>& out) {
+    for (int S : {1, 2, 4, 8}) {
+        add_ring<32, 32, 8>(out, S);
+        add_ring<32, 64, 6>(out, S);
+        add_ring<64, 32, 8>(out, S);
+        add_ring<64, 64, 4>(out, S);
+        add_ring<64, 128, 4>(out, S);
+        add_ring<128, 64, 4>(out, S);
+        add_ring<64, 256, 3>(out, S);
+        add_ring<128, 128, 4>(out, S);
+    }
+}
+
+}  // namespace lin

@@ -23,6 +23,7 @@ const std::vector<Variant>& registry() {
         register_gemv_bf16(*r);
         register_gemv_q4g64(*r);
         register_gemm_mfma(*r);
+        register_gemm_mfma_ring(*r);
         return r;
     }();
     return *reg;
@@ -88,16 +89,15 @@ int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
     } else {
         if (kind == LIN_KIND_SKINNY_BF16 && M > 16) {
             // matrix cores without split-K (the default never needs the
-            // workspace): the k-block variant whose token tile covers M best
-            const int tm = mt < 32 ? 32 : (mt > 128 ? 128 : mt);
-            int best = -1;
+            // workspace): the LDS-ring variant whose token tile covers M best
+            const int tm = mt < 32 ? 32 : (mt > 256 ? 256 : mt);
+            const int bn = tm == 32 ? 32 : (tm == 256 ? 128 : 64);
+            const int tm_pick = tm == 256 ? 128 : tm;
             for (int i : candidates(kind, M, N, K)) {
                 const Variant& v = registry()[i];
-                if (v.cfg.algo != LIN_ALGO_MFMA || v.cfg.stage_x != 1 || v.cfg.split != 1) continue;
-                if (v.cfg.tile_m != tm || v.cfg.rows != 64) continue;
-                if (best < 0 || v.cfg.unroll == 4) best = i;
+                if (v.cfg.algo != LIN_ALGO_MFMA || v.cfg.stage_x != 3 || v.cfg.split != 1) continue;
+                if (v.cfg.tile_m == tm_pick && v.cfg.rows == bn) return i;
             }
-            if (best >= 0) return best;
             for (int i : candidates(kind, M, N, K))
                 if (registry()[i].cfg.algo == LIN_ALGO_MFMA && workspace_need(registry()[i], M, N, K) == 0)
                     return i;
@@ -199,11 +199,12 @@ int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = 
         args.ws = it->second.ptr;
     }
     void* params[] = {(void*)&args};
+    const dim3 block(v.block ? v.block : kBlock);
     hipError_t e;
     if (ev0 || ev1)
-        e = hipExtLaunchKernel(v.func, grid, dim3(kBlock), params, lds, stream, ev0, ev1, 0);
+        e = hipExtLaunchKernel(v.func, grid, block, params, lds, stream, ev0, ev1, 0);
     else
-        e = hipLaunchKernel(v.func, grid, dim3(kBlock), params, lds, stream);
+        e = hipLaunchKernel(v.func, grid, block, params, lds, stream);
     return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
 }
 

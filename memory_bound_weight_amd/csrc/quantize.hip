@@ -1,6 +1,6 @@
 // Load-time weight preparation for the int4-g64 format (tinyinfer post, TL;DR:
 // 4-bit weights plus one fp16 scale per 64), and the cache-flush kernel used
-// while tuning.
+// while tuning (a read sweep over a buffer larger than the caches).
 //
 // One thread per (row, group of 64): a = max |w|; s = fp16 nearest to a/7
 // (ties to even, saturated at 65504); q = s > 0 ? clamp(rint(w/s), -8, 7) : 0
@@ -111,12 +111,17 @@ hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K,
     return hipLaunchKernel((const void*)&quantize_q4g64_kernel, grid, dim3(256), args, 0, stream);
 }
 
+// Reads (does not write) the buffer: the caches end up full of clean lines, as
+// after other kernels' reads, with no dirty data whose write-back would slow
+// the timed call.  The store below only keeps the loads alive.
 __global__ __launch_bounds__(256) void flush_kernel(u32x4* buf, size_t n16, uint32_t salt) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
-         i += (size_t)gridDim.x * blockDim.x) {
-        const uint32_t v = (uint32_t)i ^ salt;
-        buf[i] = u32x4{v, v, v, v};
+    const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (size_t i = i0; i < n16; i += (size_t)gridDim.x * blockDim.x) {
+        const u32x4 v = buf[i];
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
     }
+    if (acc == salt && i0 < n16) buf[i0] = u32x4{acc, acc, acc, acc};
 }
 
 hipError_t launch_flush(void* buf, size_t n16, uint32_t salt, hipStream_t stream) {

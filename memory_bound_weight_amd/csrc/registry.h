@@ -24,11 +24,13 @@ struct Variant {
     bool (*geometry)(const Variant&, int M, int N, int K, dim3* grid, size_t* lds);
     // Split-K workspace bytes this variant needs for a shape (0: none).
     size_t (*workspace)(const Variant&, int M, int N, int K);
+    int block = 0;     // threads per workgroup (0: kBlock)
 };
 
 void register_gemv_bf16(std::vector<Variant>& out);
 void register_gemv_q4g64(std::vector<Variant>& out);
 void register_gemm_mfma(std::vector<Variant>& out);
+void register_gemm_mfma_ring(std::vector<Variant>& out);
 
 // Quantiser launch (int4-g64 weight preparation).
 hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream);

@@ -146,19 +146,8 @@ __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
     const int m_tiles = (M + TM - 1) / TM;
     const int n_tiles = (N + BN - 1) / BN;
     int n_tile, m_tile, ks;
-    if (S == 1) {   // XCD-aware tile order (see above)
-        const int b = blockIdx.x;
-        const int xcd = b & 7, loc = b >> 3;
-        n_tile = (loc / m_tiles) * 8 + xcd;
-        m_tile = loc - (loc / m_tiles) * m_tiles;
-        ks = 0;
-        if (n_tile >= n_tiles) return;   // padding slot: whole workgroup leaves together
-    } else {        // splits of one tile are consecutive
-        const int t = blockIdx.x / S;
-        ks = blockIdx.x - t * S;
-        n_tile = t / m_tiles;
-        m_tile = t - n_tile * m_tiles;
-    }
+    if (!tile_of(blockIdx.x, n_tiles, m_tiles, S, n_tile, ks, m_tile))
+        return;   // padding slot: the whole workgroup leaves together
     const int n0 = n_tile * BN + wave * 16 * NF;
     const int m0 = m_tile * TM;
     const int nkb_all = (K + kBK - 1) / kBK;   // a partial last block is zero-filled
@@ -271,12 +260,7 @@ static bool geom_mfma(const Variant& v, int M, int N, int K, dim3* grid, size_t*
     const int nkb = (K + kBK - 1) / kBK;
     if (S > 1 && nkb < 2 * S) return false;      // at least two k-blocks per split
     if (S > 1 && m_tiles * n_tiles > kMaxTileCounters) return false;
-    if (S == 1) {
-        const int n_pad = (n_tiles + 7) / 8 * 8;
-        *grid = dim3((unsigned)(n_pad * m_tiles));
-    } else {
-        *grid = dim3((unsigned)(n_tiles * m_tiles * S));
-    }
+    *grid = dim3(tile_grid(n_tiles, m_tiles, S));
     *lds = 0;
     return true;
 }

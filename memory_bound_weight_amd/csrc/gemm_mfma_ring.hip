@@ -108,19 +108,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
     const int m_tiles = (M + TM - 1) / TM;
     const int n_tiles = (N + BN - 1) / BN;
     int n_tile, m_tile, ks;
-    if (S == 1) {   // XCD-aware: the token tiles of one W block run on one XCD
-        const int b = blockIdx.x;
-        const int xcd = b & 7, loc = b >> 3;
-        n_tile = (loc / m_tiles) * 8 + xcd;
-        m_tile = loc - (loc / m_tiles) * m_tiles;
-        ks = 0;
-        if (n_tile >= n_tiles) return;   // padding slot: whole workgroup leaves together
-    } else {        // the splits of one tile are consecutive
-        const int t = blockIdx.x / S;
-        ks = blockIdx.x - t * S;
-        n_tile = t / m_tiles;
-        m_tile = t - n_tile * m_tiles;
-    }
+    if (!tile_of(blockIdx.x, n_tiles, m_tiles, S, n_tile, ks, m_tile))
+        return;   // padding slot: the whole workgroup leaves together
     const int nkb_all = (K + KB - 1) / KB;
     const int bps = (nkb_all + S - 1) / S;
     const int kb0 = ks * bps;
@@ -262,10 +251,7 @@ bool geom_ring(const Variant& v, int M, int N, int K, dim3* grid, size_t* lds) {
     const int nkb = (K + KB - 1) / KB;
     if (S > 1 && nkb < 2 * S) return false;      // at least two k-blocks per split
     if (S > 1 && m_tiles * n_tiles > kMaxTileCounters) return false;
-    if (S == 1)
-        *grid = dim3((unsigned)((n_tiles + 7) / 8 * 8 * m_tiles));
-    else
-        *grid = dim3((unsigned)(n_tiles * m_tiles * S));
+    *grid = dim3(tile_grid(n_tiles, m_tiles, S));
     *lds = 0;
     return true;
 }

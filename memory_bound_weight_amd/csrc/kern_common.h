@@ -132,6 +132,25 @@ __device__ __forceinline__ void for_each_reduced(const float (&v)[V], int lane, 
         if (reduce_writer<V>(s, lane)) f(reduce_index<V>(s, lane), v[s]);
 }
 
+// Matrix-core tile order.  Workgroups are dispatched round-robin over the
+// eight XCDs, each with its own L2.  The workgroups that read the same W block
+// (one n tile and k split, every token tile m) get consecutive slots on one
+// XCD, so the block comes from HBM once and from that XCD's L2 for the other
+// token tiles.  Grid: ceil(n_tiles * S / 8) * 8 * m_tiles; false for a padding
+// slot (the whole workgroup leaves).
+__device__ __forceinline__ bool tile_of(int b, int n_tiles, int m_tiles, int S, int& n_tile,
+                                        int& ks, int& m_tile) {
+    const int xcd = b & 7, loc = b >> 3;
+    const int grp = (loc / m_tiles) * 8 + xcd;   // n_tile * S + ks
+    m_tile = loc - (loc / m_tiles) * m_tiles;
+    n_tile = grp / S;
+    ks = grp - n_tile * S;
+    return n_tile < n_tiles;
+}
+__host__ __device__ inline unsigned tile_grid(int n_tiles, int m_tiles, int S) {
+    return (unsigned)(((n_tiles * S + 7) / 8) * 8 * m_tiles);
+}
+
 // Split-K workspace: a fixed region of 32-bit tile counters (zero whenever no
 // kernel runs) followed by the partial tiles.  The counter region never holds
 // partial data, so shapes with different tile counts can share the workspace.

@@ -20,8 +20,7 @@
 
 namespace lin {
 
-// One row block (R x 4/SPLIT rows) of the product; the standalone kernel runs
-// one per workgroup, the persistent decode-step kernel loops over them.
+// One row block (R x 4/SPLIT rows) of the product, one per workgroup.
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t block) {
     constexpr int GROUPS = 4 / SPLIT;
@@ -152,7 +151,7 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
                 if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = s;
             });
         }
-        __syncthreads();   // red[] is reused by the next block of a persistent loop
+        __syncthreads();
     }
 }
 

@@ -16,8 +16,8 @@
 // so x is re-paired the same way (one v_perm per pair).  The offset is removed
 // per chunk: sum_k q x = dot(codes, x) - 136 * sum_k x, where sum_k x over the
 // chunk is shared by all rows; the dot chain starts from -136 * sum x.  Then
-// acc += s * chunk sum.  Per 32 weights and row: 28 unpack + 16 dot2 + 1 for
-// the scale, about 1.4 vector operations per weight.
+// acc += s * chunk sum.  Per 32 weights and row: 22 unpack + 16 dot2 + 1 for
+// the scale, about 1.2 vector operations per weight.
 //
 // x handling: either re-paired from cached global loads per chunk (cost shared
 // by the R rows), or, with STAGE, re-paired once per workgroup into LDS as
@@ -56,17 +56,32 @@ __device__ __forceinline__ void pair_x(const u32x4 (&xd)[4], XChunk& out) {
 // Sum over one chunk of 32 codes times re-paired x, minus the code offset.
 // ((w >> 4i) & 0x000F000F) ^ 0x43084308 equals ((w ^ 0x88888888) >> 4i &
 // 0x000F000F) | 0x43004300: the sign flip and the bf16 exponent bits go in with
-// one 3-input bitwise operation (v_bitop3_b32), plus one shift for i > 0.
+// one 3-input bitwise operation (v_bitop3_b32).  The shifts are done on two
+// dwords at once with one v_lshrrev_b64 (bits that cross from the high dword
+// land in bits 20..31 of the low one, outside the mask), which halves them:
+// per 32 codes 6 shifts + 16 bitwise operations + 16 dot products.
+template <int S>
+__device__ __forceinline__ uint64_t shr64(uint64_t v) {
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "I"(S), "v"(v));
+    return r;
+}
+
 __device__ __forceinline__ float chunk_dot(const u32x4& wq, const XChunk& xc) {
     constexpr uint32_t M = 0x000F000Fu, C = 0x43084308u;
     float acc = xc.negsum;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t w = wq[d];
-        acc = dot2((w & M) ^ C, xc.v[d][0], acc);
-        acc = dot2(((w >> 4) & M) ^ C, xc.v[d][1], acc);
-        acc = dot2(((w >> 8) & M) ^ C, xc.v[d][2], acc);
-        acc = dot2(((w >> 12) & M) ^ C, xc.v[d][3], acc);
+    for (int d = 0; d < 4; d += 2) {
+        const uint64_t w = (uint64_t)wq[d] | ((uint64_t)wq[d + 1] << 32);
+        const uint64_t t1 = shr64<4>(w), t2 = shr64<8>(w), t3 = shr64<12>(w);
+        acc = dot2(((uint32_t)w & M) ^ C, xc.v[d][0], acc);
+        acc = dot2(((uint32_t)t1 & M) ^ C, xc.v[d][1], acc);
+        acc = dot2(((uint32_t)t2 & M) ^ C, xc.v[d][2], acc);
+        acc = dot2(((uint32_t)t3 & M) ^ C, xc.v[d][3], acc);
+        acc = dot2(((uint32_t)(w >> 32) & M) ^ C, xc.v[d + 1][0], acc);
+        acc = dot2(((uint32_t)(t1 >> 32) & M) ^ C, xc.v[d + 1][1], acc);
+        acc = dot2(((uint32_t)(t2 >> 32) & M) ^ C, xc.v[d + 1][2], acc);
+        acc = dot2(((uint32_t)(t3 >> 32) & M) ^ C, xc.v[d + 1][3], acc);
     }
     return acc;
 }
@@ -75,8 +90,7 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// One row block (R x 4/SPLIT rows) of the product; the standalone kernel runs
-// one per workgroup, the persistent decode-step kernel loops over them.
+// One row block (R x 4/SPLIT rows) of the product, one per workgroup.
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block) {
     constexpr int GROUPS = 4 / SPLIT;
@@ -248,7 +262,6 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
                 if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = s;
             });
         }
-        __syncthreads();   // red[] is reused by the next block of a persistent loop
     }
 }
 

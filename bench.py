@@ -443,7 +443,7 @@ def main():
     ap.add_argument("--tuning", default=None, help="tuning table path")
     ap.add_argument("--no-fuse", action="store_true",
                     help="one launch per matrix instead of q|k|v and gate|up concatenated")
-    ap.add_argument("--cpu-layers", type=int, default=4)
+    ap.add_argument("--cpu-layers", type=int, default=16)
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES three times (scales the HBM "

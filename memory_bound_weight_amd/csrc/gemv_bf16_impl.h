@@ -16,6 +16,8 @@
 // sums); each lane sums K/512 chunks, then a permlane/DPP tree sums the lanes.
 #pragma once
 
+#include <type_traits>
+
 #include "kern_common.h"
 
 namespace lin {
@@ -70,10 +72,15 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
         u32x4 w[U][R];
         u32x4 x[U][MT];
     };
+    // Every step, the last one included, loads U x 64 chunks per row; in a
+    // partial last step the lanes past cend re-load chunk cend - 1 (in bounds)
+    // and drop its product, so the ragged end rides the same two-stage
+    // pipeline instead of a serial tail.
     auto load = [&](Stage& s, int cb) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t off = (uint32_t)(cb + kWave * u + lane) * 16u;
+            const int c = min(cb + kWave * u + lane, cend - 1);
+            const uint32_t off = (uint32_t)c * 16u;
 #pragma unroll
             for (int r = 0; r < R; ++r) s.w[u][r] = load_w16(wb[r], off);
             if constexpr (!STAGE) {
@@ -82,53 +89,53 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
             }
         }
     };
-    auto compute = [&](const Stage& s, int cb) {
+    auto compute = [&](const Stage& s, int cb, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < U; ++u) {
+            const int c = cb + kWave * u + lane;
+            const int cc = min(c, cend - 1);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const u32x4 xv = STAGE ? xs[m * nch + cb + kWave * u + lane] : s.x[u][m];
+                const u32x4 xv = STAGE ? xs[m * nch + cc] : s.x[u][m];
 #pragma unroll
-                for (int r = 0; r < R; ++r)
+                for (int r = 0; r < R; ++r) {
+                    if constexpr (MASK) {
+                        float t = 0.f;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[r * MT + m] = dot2(s.w[u][r][j], xv[j], acc[r * MT + m]);
+                        for (int j = 0; j < 4; ++j) t = dot2(s.w[u][r][j], xv[j], t);
+                        acc[r * MT + m] += c < cend ? t : 0.f;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            acc[r * MT + m] = dot2(s.w[u][r][j], xv[j], acc[r * MT + m]);
+                    }
+                }
             }
+        }
+    };
+    auto step = [&](const Stage& s, int cb) {
+        if (cb + STEP > cend)
+            compute(s, cb, std::true_type{});
+        else
+            compute(s, cb, std::false_type{});
     };
 
-    // full steps, two register stages in flight (unrolled by two: no copies)
-    const int nfull = (cend - cbeg) / STEP;
+    // two register stages in flight (unrolled by two: no copies)
+    const int nsteps = (cend - cbeg + STEP - 1) / STEP;
     int cb = cbeg;
-    if (nfull > 0) {
+    if (nsteps > 0) {
         Stage s0, s1;
         load(s0, cb);
         for (int it = 0;;) {
-            if (it + 1 < nfull) load(s1, cb + STEP);
-            compute(s0, cb);
+            if (it + 1 < nsteps) load(s1, cb + STEP);
+            step(s0, cb);
             cb += STEP;
-            if (++it >= nfull) break;
-            if (it + 1 < nfull) load(s0, cb + STEP);
-            compute(s1, cb);
+            if (++it >= nsteps) break;
+            if (it + 1 < nsteps) load(s0, cb + STEP);
+            step(s1, cb);
             cb += STEP;
-            if (++it >= nfull) break;
-        }
-    }
-    for (; cb < cend; cb += kWave) {   // ragged tail: one chunk per lane at most
-        const int c = cb + lane;
-        if (c < cend) {
-            const uint32_t off = (uint32_t)c * 16u;
-            u32x4 w[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) w[r] = load_w16(wb[r], off);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                const u32x4 xv = STAGE ? xs[m * nch + c] : load_x16(xb[m], off);
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[r * MT + m] = dot2(w[r][j], xv[j], acc[r * MT + m]);
-            }
+            if (++it >= nsteps) break;
         }
     }
 

@@ -24,6 +24,8 @@
 // [MT][4][chunks] 16-byte words (bank-conflict-free reads) plus the chunk sums.
 #pragma once
 
+#include <type_traits>
+
 #include "kern_common.h"
 
 namespace lin {
@@ -154,10 +156,14 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
         uint16_t sc[U][R];
         u32x4 x[U][MT][STAGE ? 1 : 4];   // raw x of the chunk (unstaged x only)
     };
+    // Every step, the last one included, loads U x 64 chunks per row; in a
+    // partial last step the lanes past cend re-load chunk cend - 1 (in bounds)
+    // and drop its product, so the ragged end rides the same two-stage
+    // pipeline instead of a serial tail.
     auto load = [&](Stage& s, int cb) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t c = (uint32_t)(cb + kWave * u + lane);
+            const uint32_t c = (uint32_t)min(cb + kWave * u + lane, cend - 1);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 s.w[u][r] = load_w16(wb[r], c * 16u);
@@ -180,66 +186,50 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
             pair_x(s.x[u][m], xc);
         }
     };
-    auto compute = [&](const Stage& s, int cb) {
+    auto compute = [&](const Stage& s, int cb, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int c = cb + kWave * u + lane;
+            const int cc = min(c, cend - 1);
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
                 XChunk xc;
-                get_x(s, u, m, c, xc);
+                get_x(s, u, m, cc, xc);
 #pragma unroll
-                for (int r = 0; r < R; ++r)
-                    acc[r * MT + m] = fmaf(half_to_float(s.sc[u][r]), chunk_dot(s.w[u][r], xc),
-                                           acc[r * MT + m]);
+                for (int r = 0; r < R; ++r) {
+                    const float v = fmaf(half_to_float(s.sc[u][r]), chunk_dot(s.w[u][r], xc),
+                                         acc[r * MT + m]);
+                    if constexpr (MASK)
+                        acc[r * MT + m] = c < cend ? v : acc[r * MT + m];
+                    else
+                        acc[r * MT + m] = v;
+                }
             }
         }
     };
+    auto step = [&](const Stage& s, int cb) {
+        if (cb + STEP > cend)
+            compute(s, cb, std::true_type{});
+        else
+            compute(s, cb, std::false_type{});
+    };
 
-    // full steps, two register stages in flight (unrolled by two: no copies)
-    const int nfull = (cend - cbeg) / STEP;
+    // two register stages in flight (unrolled by two: no copies)
+    const int nsteps = (cend - cbeg + STEP - 1) / STEP;
     int cb = cbeg;
-    if (nfull > 0) {
+    if (nsteps > 0) {
         Stage s0, s1;
         load(s0, cb);
         for (int it = 0;;) {
-            if (it + 1 < nfull) load(s1, cb + STEP);
-            compute(s0, cb);
+            if (it + 1 < nsteps) load(s1, cb + STEP);
+            step(s0, cb);
             cb += STEP;
-            if (++it >= nfull) break;
-            if (it + 1 < nfull) load(s0, cb + STEP);
-            compute(s1, cb);
+            if (++it >= nsteps) break;
+            if (it + 1 < nsteps) load(s0, cb + STEP);
+            step(s1, cb);
             cb += STEP;
-            if (++it >= nfull) break;
-        }
-    }
-    for (; cb < cend; cb += kWave) {   // ragged tail: one chunk per lane at most
-        const int c = cb + lane;
-        if (c < cend) {
-            u32x4 w[R];
-            uint16_t sc[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                w[r] = load_w16(wb[r], (uint32_t)c * 16u);
-                sc[r] = load_w2(sb[r], (uint32_t)(c >> 1) * 2u);
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                XChunk xc;
-                if constexpr (STAGE) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) xc.v[t] = xs[(m * 4 + t) * nch + c];
-                    xc.negsum = xsum[m * nch + c];
-                } else {
-                    u32x4 xd[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) xd[t] = load_x16(xb[m], (uint32_t)(4 * c + t) * 16u);
-                    pair_x(xd, xc);
-                }
-#pragma unroll
-                for (int r = 0; r < R; ++r)
-                    acc[r * MT + m] = fmaf(half_to_float(sc[r]), chunk_dot(w[r], xc), acc[r * MT + m]);
-            }
+            if (++it >= nsteps) break;
         }
     }
 

@@ -190,15 +190,15 @@ def variant_key(m):
 
 
 def kernel_times(mats, reps):
-    """Average duration per launch of each kernel variant, measured live with HIP
-    events around graph replays that hold only that variant's launches (in step
-    order).  Queued kernels start as the previous one ends, so elapsed time /
-    launches is the kernel's own duration."""
+    """Average duration per launch of each kernel (variant and shape), measured
+    live with HIP events around graph replays that hold only that kernel's
+    launches (at least 64, in step order).  Queued kernels start as the
+    previous one ends, so elapsed time / launches is the kernel's own duration."""
     by = {}
     for m in mats:
-        by.setdefault(variant_key(m), []).append(m)
+        by.setdefault((variant_key(m), "%dx%d" % (m.N, m.K)), []).append(m)
     out = {}
-    for key, ms in by.items():
+    for (variant, shape), ms in by.items():
         rep = max(1, -(-64 // len(ms)))   # at least 64 launches per replay
         g = capture(ms * rep)
         for _ in range(2):
@@ -212,12 +212,10 @@ def kernel_times(mats, reps):
         e1.record()
         torch.cuda.synchronize()
         per_launch = e0.elapsed_time(e1) / 1000.0 / (reps * rep * len(ms))
-        nbytes = sum(m.bytes for m in ms)
-        mix = {}
-        for m in ms:
-            mix["%dx%d" % (m.N, m.K)] = mix.get("%dx%d" % (m.N, m.K), 0) + 1
-        out[key] = {"avg_s": per_launch, "launches": len(ms), "bytes_per_launch": nbytes / len(ms),
-                    "step_s": per_launch * len(ms), "shapes": sorted(mix), "mix": mix}
+        out["%s %s" % (variant, shape)] = {
+            "variant": variant, "shape": shape, "avg_s": per_launch, "launches": len(ms),
+            "bytes_per_launch": ms[0].bytes, "step_s": per_launch * len(ms)}
+        del g
     return out
 
 
@@ -500,8 +498,9 @@ def main():
     achieved = dom["bytes_per_launch"] / dom["avg_s"] / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom_key, dom["mix"]),
-                "kernel": dom_key, "launches_per_step": dom["launches"], "shapes": dom["shapes"],
+                "traffic": measured_traffic(dom["variant"], {dom["shape"]: 1}),
+                "kernel": dom["variant"], "shape": dom["shape"],
+                "launches_per_step": dom["launches"],
                 "avg_launch_us": round(dom["avg_s"] * 1e6, 3),
                 "bytes_per_launch": int(dom["bytes_per_launch"]),
                 "share_of_step": round(dom["step_s"] / gpu, 3)}

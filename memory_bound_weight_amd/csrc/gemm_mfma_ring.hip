@@ -82,17 +82,21 @@ __device__ __forceinline__ void wait_stages(int after) {
 }
 
 // Wave tile of a workgroup tile: NW wavefronts as WR x WC; KB k per stage
-// (eight wavefronts and 128-k stages measured no faster than 4 and 64).
+// (eight wavefronts and 128-k stages measured no faster than 4 and 64).  A
+// 16-token tile stacks the wavefronts along W (4 x 1).  The fragment loads of
+// a stage are spread evenly over the wavefronts; when their number does not
+// divide, the stage is padded with fragments that load the zero word.
 template <int BN, int TM, int NW, int KB>
 struct Shape {
-    static constexpr int WR = NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4);
+    static constexpr int WR = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4));
     static constexpr int WC = NW / WR;
     static constexpr int WN = BN / WR, WM = TM / WC;
     static constexpr int NF = WN / 16, MT = WM / 16;
     static constexpr int H = KB / 32;                  // 32-k halves per stage
-    static constexpr int FW = BN / 16 * H, FX = TM / 16 * H, F = FW + FX;
+    static constexpr int FW = BN / 16 * H, FX = TM / 16 * H;
+    static constexpr int F = (FW + FX + NW - 1) / NW * NW;   // fragments per stage, padded
     static constexpr int L = F / NW;                   // fragment loads per wavefront and stage
-    static_assert(NF >= 1 && MT >= 1 && F % NW == 0, "tile shape");
+    static_assert(NF >= 1 && MT >= 1 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
 };
 
 template <int BN, int TM, int D, int NW, int KB>
@@ -123,7 +127,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int f = wave * L + i;
-        if (f < FW) {
+        if (f >= FW + SH::FX) {
+            src[i] = nullptr;   // padding fragment: loads the zero word
+        } else if (f < FW) {
             int n = n_tile * BN + (f / H) * 16 + l16;
             n = n < N ? n : N - 1;
             src[i] = (const uint8_t*)a.W + (int64_t)n * K * 2;
@@ -138,7 +144,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
         for (int i = 0; i < L; ++i) {
             const int f = wave * L + i;
             const int k = kb * KB + (f % H) * 32 + lg * 8;
-            const void* p = k < K ? (const void*)(src[i] + (size_t)k * 2) : (const void*)&g_zero16;
+            const void* p = (src[i] && k < K) ? (const void*)(src[i] + (size_t)k * 2) : (const void*)&g_zero16;
             dma16(p, &ring[slot][f][0]);
         }
     };
@@ -277,7 +283,7 @@ void add_ring(std::vector<Variant>& out, int S) {
     v.cfg.stage_x = 3;   // W and X blocks through an LDS ring of direct loads
     v.cfg.tile_m = TM;
     v.mt = 0;
-    v.min_m = 16;
+    v.min_m = TM <= 16 ? 1 : 16;
     v.func = (const void*)&gemm_mfma_ring_kernel<BN, TM, D, NW, KB>;
     v.geometry = &geom_ring<BN, TM, D, NW, KB>;
     v.workspace = &ws_ring<BN, TM, D, NW, KB>;
@@ -289,6 +295,8 @@ void add_ring(std::vector<Variant>& out, int S) {
 
 void register_gemm_mfma_ring(std::vector<Variant>& out) {
     for (int S : {1, 2, 4, 8}) {
+        add_ring<64, 16, 8>(out, S);
+        add_ring<128, 16, 6>(out, S);
         add_ring<32, 32, 8>(out, S);
         add_ring<32, 64, 6>(out, S);
         add_ring<64, 32, 8>(out, S);

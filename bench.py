@@ -219,6 +219,31 @@ def kernel_times(mats, reps):
     return out
 
 
+def read_ceiling(nbytes, dev, reps):
+    """What one kernel moving `nbytes` can reach here: lin_stream_read over a
+    buffer of that size (a read-only pass with the products' launch shape),
+    cycled over copies larger than the last-level cache and replayed
+    back-to-back in a graph, like the products.  GB/s."""
+    nbytes = max(16, nbytes // 16 * 16)
+    copies = max(2, -(-(600 << 20) // nbytes))
+    bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+    n = max(32, 2 * copies)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n):
+            L.lin_stream_read(bufs[i % copies])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            L.lin_stream_read(bufs[i % copies])
+    _, gpu = time_graph(g, reps, 2)
+    del g, bufs
+    return nbytes / (gpu / n) / 1e9
+
+
 def measured_traffic(key, shapes_mix):
     """HBM bytes per launch of kernel variant `key` over the step's shape mix,
     from the counter table, or None if none was taken for the current source."""
@@ -345,8 +370,11 @@ def run_skinny(args, dev):
     step_bytes = sum(c.bytes for c in cases)
     dom = max(cases, key=lambda c: per_case[c.name]["us"])
     d = per_case[dom.name]
+    ceil = read_ceiling(dom.bytes, dev, reps)
     roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": d["hbm_frac"], "traffic": None, "kernel": d["variant"], "case": dom.name,
+                "frac": d["hbm_frac"], "traffic": None,
+                "read_ceiling_GB_s": round(ceil, 1), "frac_of_read_ceiling": round(d["GB_s"] / ceil, 4),
+                "kernel": d["variant"], "case": dom.name,
                 "avg_launch_us": d["us"], "bytes_per_launch": dom.bytes,
                 "mfma": {"achieved": d["TFLOP_s"], "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": d["mfma_frac"]}}
@@ -496,16 +524,20 @@ def main():
     dom_key = max(kt, key=lambda k: kt[k]["step_s"])
     dom = kt[dom_key]
     achieved = dom["bytes_per_launch"] / dom["avg_s"] / 1e9
+    ceil = {k: read_ceiling(v["bytes_per_launch"], dev, max(5, args.steps // 2)) for k, v in kt.items()}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom["variant"], {dom["shape"]: 1}),
+                "read_ceiling_GB_s": round(ceil[dom_key], 1),
+                "frac_of_read_ceiling": round(achieved / ceil[dom_key], 4),
                 "kernel": dom["variant"], "shape": dom["shape"],
                 "launches_per_step": dom["launches"],
                 "avg_launch_us": round(dom["avg_s"] * 1e6, 3),
                 "bytes_per_launch": int(dom["bytes_per_launch"]),
                 "share_of_step": round(dom["step_s"] / gpu, 3)}
     kernels = {k: {"avg_us": round(v["avg_s"] * 1e6, 3), "launches": v["launches"],
-                   "GB_s": round(v["bytes_per_launch"] / v["avg_s"] / 1e9, 1)}
+                   "GB_s": round(v["bytes_per_launch"] / v["avg_s"] / 1e9, 1),
+                   "read_ceiling_GB_s": round(ceil[k], 1)}
                for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["step_s"])}
 
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,

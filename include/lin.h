@@ -156,6 +156,14 @@ int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* 
  * Writes Wq [N][K/2] and S [N][K/64].  W must hold finite values. */
 int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, void* stream);
 
+/* Measurement: read every byte of `buf` (device, 16-byte aligned, `bytes` a
+ * multiple of 16) once and discard it.  This is the ceiling a product is
+ * measured against (llm-rs design post, section 6: track the share of a
+ * ceiling): the same bytes, streamed by a kernel that does nothing else, with
+ * the launch shape the products use at their best (short wavefronts of four
+ * 16-byte loads per lane).  Enqueued on `stream`; allocates nothing. */
+int lin_stream_read(const void* buf, int64_t bytes, void* stream);
+
 /* Static description of a status code. */
 const char* lin_status_string(int status);
 

@@ -37,7 +37,7 @@ LIN_SKINNY_MAX_M = 256
 # Every symbol include/lin.h declares.
 EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemm_skinny_bf16", "lin_autotune",
            "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
-           "lin_quantize_q4g64", "lin_status_string", "lin_version")
+           "lin_quantize_q4g64", "lin_stream_read", "lin_status_string", "lin_version")
 
 
 class LinConfig(ctypes.Structure):
@@ -79,6 +79,7 @@ def _load():
         "lin_get_config": [I, I64, I64, I64, ctypes.POINTER(LinConfig)],
         "lin_set_config": [I, I64, I64, I64, ctypes.POINTER(LinConfig)],
         "lin_quantize_q4g64": [P, P, P, I64, I64, P],
+        "lin_stream_read": [P, I64, P],
         "lin_status_string": [I],
         "lin_version": [],
     }
@@ -195,6 +196,15 @@ def lin_quantize_q4g64(W, Wq=None, S=None):
     _check(_lib.lin_quantize_q4g64(W.data_ptr(), Wq.data_ptr(), S.data_ptr(), N, K, _stream(W)),
            "lin_quantize_q4g64")
     return Wq, S
+
+
+def lin_stream_read(buf):
+    """Read every byte of a contiguous device tensor once (the bandwidth ceiling
+    a product is compared with); returns nothing."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("lin_stream_read: buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    _check(_lib.lin_stream_read(buf.data_ptr(), nbytes, _stream(buf)), "lin_stream_read")
 
 
 def _shape_args(kind, W, S, x):

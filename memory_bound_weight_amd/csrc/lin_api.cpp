@@ -359,6 +359,15 @@ int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* 
     return set_config_table(kind, M, N, K, cfg);
 }
 
+int lin_stream_read(const void* buf, int64_t bytes, void* stream) {
+    if (bytes < 0 || bytes % 16) return LIN_ERR_SHAPE;
+    if (bytes == 0) return LIN_OK;
+    if (!buf) return LIN_ERR_NULL;
+    if (!aligned(buf, 16)) return LIN_ERR_ALIGN;
+    hipError_t e = launch_stream_read(buf, (size_t)bytes, (hipStream_t)stream);
+    return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
+}
+
 int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, void* stream) {
     if (N < 0 || K < 0 || N > 0x7FFFFFFF || K > LIN_MAX_K || K % 64) return LIN_ERR_SHAPE;
     if (N == 0 || K == 0) return LIN_OK;

@@ -35,8 +35,11 @@ void register_gemm_mfma_ring(std::vector<Variant>& out);
 // Quantiser launch (int4-g64 weight preparation).
 hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream);
 
-// Cache-flush kernel used while tuning: writes n 16-byte words.
+// Cache sweep used while tuning: reads n 16-byte words.
 hipError_t launch_flush(void* buf, size_t n16, uint32_t salt, hipStream_t stream);
+
+// Read-only streaming pass (achievable-bandwidth ceiling).
+hipError_t launch_stream_read(const void* buf, size_t bytes, hipStream_t stream);
 
 constexpr size_t kMaxDynLds = 64 * 1024;
 

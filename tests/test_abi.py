@@ -79,6 +79,15 @@ def test_quantizer_validation():
     assert q(P, P, P + 1, 4, 64, None) == L.LIN_ERR_ALIGN
 
 
+def test_stream_read_validation():
+    r = L._lib.lin_stream_read
+    assert r(None, 0, None) == L.LIN_OK
+    assert r(P, -16, None) == L.LIN_ERR_SHAPE
+    assert r(P, 24, None) == L.LIN_ERR_SHAPE
+    assert r(None, 16, None) == L.LIN_ERR_NULL
+    assert r(P + 8, 16, None) == L.LIN_ERR_ALIGN
+
+
 def test_autotune_validation():
     cfg = L.LinConfig()
     t = L._lib.lin_autotune

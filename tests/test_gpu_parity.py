@@ -272,3 +272,15 @@ def test_split_k_workspace_shared_across_shapes():
                     y = L.lin_gemm_skinny_bf16(Wd, Xd)
                     torch.cuda.synchronize()
                     assert_within_bound(y, Y, B, "split-K %dx%dx%d %s" % (M, N, K, cfg))
+
+
+def test_stream_read_runs_on_ragged_sizes():
+    """The read-only pass used as the bandwidth ceiling: any multiple of 16
+    bytes, including sizes that leave a partial workgroup, completes without
+    error and leaves the buffer unchanged."""
+    for nbytes in (16, 4096 + 16, (1 << 20) + 48, 3 << 20):
+        buf = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device=DEV)
+        ref = buf.clone()
+        L.lin_stream_read(buf)
+        torch.cuda.synchronize()
+        assert torch.equal(buf, ref)

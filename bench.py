@@ -100,19 +100,24 @@ def tune_key(m):
 
 
 def autotune(mats, only=None):
-    """Load-time tuning: once per distinct (format, N, K), on that shape's first
-    matrix; returns {tune key: config}."""
-    seen = {}
+    """Load-time tuning: once per distinct (format, N, K), with lin_autotune_set
+    over all of that shape's matrices (the layers), timed back to back the way
+    the step runs them; returns {tune key: config}."""
+    groups = {}
     for m in mats:
         key = tune_key(m)
-        if key in seen or (only is not None and key not in only):
-            continue
+        if only is None or key in only:
+            groups.setdefault(key, []).append(m)
+    seen = {}
+    for key, ms in groups.items():
+        m = ms[0]
         if m.fmt == "bf16":
-            cfg = L.lin_autotune(L.LIN_KIND_GEMV_BF16, m.W, m.x, m.y)
+            cfg = L.lin_autotune_set(L.LIN_KIND_GEMV_BF16, [g.W for g in ms], m.x, m.y)
         else:
-            cfg = L.lin_autotune(L.LIN_KIND_GEMV_Q4G64, m.Wq, m.x, m.y, S=m.S)
+            cfg = L.lin_autotune_set(L.LIN_KIND_GEMV_Q4G64, [g.Wq for g in ms], m.x, m.y,
+                                     Ss=[g.S for g in ms])
         seen[key] = cfg
-        log("tuned %-5s %6d x %-6d -> %s" % (m.fmt, m.N, m.K, cfg))
+        log("tuned %-5s %6d x %-6d over %d matrices -> %s" % (m.fmt, m.N, m.K, len(ms), cfg))
     return seen
 
 
@@ -318,8 +323,8 @@ def run_skinny(args, dev):
     for c in cases:
         if c.key in ok:
             continue
-        cfg = L.lin_autotune(L.LIN_KIND_SKINNY_BF16, weights[(c.N, c.K)][0], X[(c.M, c.K)],
-                             Y[c.key])
+        cfg = L.lin_autotune_set(L.LIN_KIND_SKINNY_BF16, weights[(c.N, c.K)], X[(c.M, c.K)],
+                                 Y[c.key])
         tuned[c.key] = cfg
         log("tuned skinny %-16s -> %s" % (c.name, cfg))
     if tuned:

@@ -78,10 +78,11 @@ typedef enum lin_algo {
  * workgroups sharing one output tile by splitting K (their partial tiles go
  * through a library-owned workspace and are added in a fixed order, so results
  * stay deterministic); `stage_x` = 1: W streams through registers and a
- * 64-k block of X is staged in LDS per step; `stage_x` = 3: W and X blocks
- * both stream through an LDS ring of `unroll` stages filled by direct
- * global-to-LDS loads.  `us` is filled by lin_autotune (median microseconds per
- * call, cold caches) and ignored on input. */
+ * 64-k block of X is staged in LDS per step; `stage_x` = 3 or 4: W and X
+ * blocks both stream through an LDS ring of `unroll` stages filled by direct
+ * global-to-LDS loads, in the matrix-core operand order (3) or in whole
+ * 128-byte lines with a swizzled layout (4).  `us` is filled by lin_autotune
+ * (median microseconds per call, cold caches) and ignored on input. */
 typedef struct lin_config {
     int32_t algo;
     int32_t rows;
@@ -128,6 +129,19 @@ int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y,
  * must not be called during graph capture. */
 int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y,
                  int64_t M, int64_t N, int64_t K, void* stream, lin_config* out);
+
+/* The same load-time tuning timed the way a decode step runs the layer: every
+ * candidate is captured as one graph of back-to-back calls cycling over the
+ * `count` >= 1 weight matrices W[0..count-1] (and S[0..count-1] for
+ * LIN_KIND_GEMV_Q4G64; S may be NULL otherwise) of the same shape, e.g. the
+ * layers of a model, and the graph is replayed; `us` is the mean time per
+ * call.  W and S are host arrays of device pointers, owned by the caller and
+ * only read during the call.  Stores the fastest configuration like
+ * lin_autotune and has the same allocation, synchronisation and
+ * no-capture rules; it runs the candidates on a stream of its own. */
+int lin_autotune_set(int kind, const void* const* W, const void* const* S, int count,
+                     const void* x, float* y, int64_t M, int64_t N, int64_t K, void* stream,
+                     lin_config* out);
 
 /* Candidate configurations for (kind, M, N, K), in a fixed order: returns how
  * many there are (>= 0) or a negative status.  lin_candidate writes number

@@ -36,7 +36,7 @@ LIN_SKINNY_MAX_M = 256
 
 # Every symbol include/lin.h declares.
 EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemm_skinny_bf16", "lin_autotune",
-           "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
+           "lin_autotune_set", "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
            "lin_quantize_q4g64", "lin_stream_read", "lin_status_string", "lin_version")
 
 
@@ -74,6 +74,8 @@ def _load():
         "lin_gemv_q4g64": [P, P, P, P, I64, I64, I64, P],
         "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
         "lin_autotune": [I, P, P, P, P, I64, I64, I64, P, ctypes.POINTER(LinConfig)],
+        "lin_autotune_set": [I, ctypes.POINTER(P), ctypes.POINTER(P), I, P, P, I64, I64, I64, P,
+                             ctypes.POINTER(LinConfig)],
         "lin_num_candidates": [I, I64, I64, I64],
         "lin_candidate": [I, I64, I64, I64, I, ctypes.POINTER(LinConfig)],
         "lin_get_config": [I, I64, I64, I64, ctypes.POINTER(LinConfig)],
@@ -222,6 +224,31 @@ def lin_autotune(kind, W, x, y, S=None):
     _check(_lib.lin_autotune(int(kind), W.data_ptr(), S.data_ptr() if S is not None else None,
                              x.data_ptr(), y.data_ptr(), M, N, K, _stream(W), ctypes.byref(cfg)),
            "lin_autotune")
+    return cfg.as_dict()
+
+
+def lin_autotune_set(kind, Ws, x, y, Ss=None):
+    """Time every candidate as a graph of back-to-back calls cycling over the
+    same-shaped weights Ws (and scales Ss for int4), keep the fastest for later
+    calls; returns it as a dict with 'us' (mean per call)."""
+    Ws = list(Ws)
+    if not Ws:
+        raise ValueError("lin_autotune_set needs at least one weight matrix")
+    x, M, N, K = _shape_args(kind, Ws[0], Ss[0] if Ss else None, x)
+    for W in Ws:
+        if tuple(W.shape) != tuple(Ws[0].shape) or W.dtype != Ws[0].dtype:
+            raise ValueError("lin_autotune_set: every matrix must have the same shape and dtype")
+    wp = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
+    sp = None
+    if Ss is not None:
+        Ss = list(Ss)
+        if len(Ss) != len(Ws):
+            raise ValueError("lin_autotune_set: one scale tensor per weight matrix")
+        sp = (ctypes.c_void_p * len(Ss))(*[S.data_ptr() for S in Ss])
+    cfg = LinConfig()
+    _check(_lib.lin_autotune_set(int(kind), wp, sp, len(Ws), x.data_ptr(), y.data_ptr(), M, N, K,
+                                 _stream(Ws[0]), ctypes.byref(cfg)),
+           "lin_autotune_set")
     return cfg.as_dict()
 
 

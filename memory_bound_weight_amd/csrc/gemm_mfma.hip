@@ -237,7 +237,11 @@ __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
             if (kb >= kb1) break;
             const int buf = (kb - kb0) & 1;
             store_x(st[d].x, buf);
-            __syncthreads();   // X tile complete; the buffer written next time is idle
+            // X tile complete (LDS writes done; later stages' loads stay in
+            // flight, which __syncthreads would drain); the buffer written
+            // next time is idle.
+            wait_cnt<63, 0>();
+            barrier_only();
             compute(st[d].w, buf);
             if (kb + D < kb1) {
                 load_w(st[d].w, kb + D);

@@ -12,17 +12,23 @@
 // bank-conflict-free staging follow section 5 of the same post; the data
 // path is CDNA4's own.
 //
-// Ring.  A stage holds one 64-k block: BN/16 x 2 W fragments and TM/16 x 2 X
-// fragments, each fragment 1 KB in the order v_mfma_f32_16x16x32_bf16 reads
-// its operands (lane l: row l mod 16, k 8 (l / 16) .. + 7 of a 32-k half), so
-// that a wavefront loads a fragment with one instruction (64 lanes x 16 B,
-// placed in lane order) and reads it back with one conflict-free
-// ds_read_b128.  The four wavefronts share the loads of a stage.  Iteration i
-// waits (vmcnt) until its own loads of stage i have landed, meets the others
-// at one s_barrier (their loads have landed too, and everyone has finished
-// reading stage i - 1), refills the slot of stage i - 1 with stage i + D - 1,
-// then multiplies stage i.  k past K reads from a zero word, rows past N or
-// M re-read the last row (never stored).
+// Ring.  A stage holds one 64-k block of BN W rows and TM X rows in 1 KB
+// load units, one wavefront instruction (64 lanes x 16 B, placed in lane
+// order) each.  Two unit layouts:
+//  - fragment order: a unit is 16 rows x 64 B (32 k), in the order
+//    v_mfma_f32_16x16x32_bf16 reads its operands (lane l: row l mod 16, k
+//    8 (l / 16) .. + 7), read back with one lane-linear ds_read_b128;
+//  - line order: a unit is 8 rows x 128 B, whole cache lines, with the 16-byte
+//    chunks of a row XOR-swizzled so that the operand reads of a 16-row group
+//    (two units) are still one ds_read_b128 spread over the banks.  Half as
+//    many cache lines per load instruction: X, which every workgroup re-reads
+//    from L2, streams faster (measured 40 %), at a small cost in LDS reads.
+// The four wavefronts share the loads of a stage.  Iteration i waits (vmcnt)
+// until its own loads of stage i have landed, meets the others at one
+// s_barrier (their loads have landed too, and everyone has finished reading
+// stage i - 1), refills the slot of stage i - 1 with stage i + D - 1, then
+// multiplies stage i.  k past K reads from a zero word, rows past N or M
+// re-read the last row (never stored).
 //
 // Wave tile.  The workgroup tile BN x TM is split 2 x 2 (or 1 x 4 when TM is
 // 256) among the four wavefronts; each keeps its NF x MT 16x16 fp32
@@ -35,31 +41,22 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-#define LDS_AS __attribute__((address_space(3)))
-
 __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// One direct-to-LDS load: 16 bytes per lane from `g` into LDS at the
-// wavefront-uniform address `lds` + 16 * lane (ordinary cache policy: a
-// non-temporal hint on the weights measured slower).  Written as inline assembly so
-// that the compiler does not treat every later LDS read as waiting on it
-// (it would wait for all outstanding loads, which empties the ring); the
-// kernel orders the ring itself with vmcnt waits and barriers.  M0 is only
-// set here: nothing else in these kernels uses it.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved: set here, used by nothing else
-__device__ __forceinline__ void dma16(const void* g, const void* lds) {
-    const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS const void*)lds;
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
+// Position of k-chunk c (8 k, 16 bytes) in row r of a ring group is
+// c ^ ring_swz(r).  The 16 rows of a group are 128 bytes apart, so unswizzled
+// the 16 lanes reading one chunk of 16 rows would hit the same banks; with
+// this swizzle any 8 consecutive rows, and the 8 even and the 8 odd rows of
+// a group, use 8 different 16-byte positions, which spreads them over the
+// banks whether the LDS serves 128 or 256 bytes per clock.
+__device__ __forceinline__ int ring_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// k >= K lanes load these zeros instead of reading past a row.
-__device__ __attribute__((aligned(16))) const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
+// The ring's direct-to-LDS loads use dma16 (ordinary cache policy: a
+// non-temporal hint on the weights measured slower); k >= K lanes load
+// g_zero16 instead of reading past a row.
 
 // s_waitcnt with vmcnt <= N (N < 64) and lgkmcnt = 0; expcnt not waited on.
 template <int N>
@@ -97,9 +94,10 @@ struct Shape {
     static constexpr int F = (FW + FX + NW - 1) / NW * NW;   // fragments per stage, padded
     static constexpr int L = F / NW;                   // fragment loads per wavefront and stage
     static_assert(NF >= 1 && MT >= 1 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
+    static_assert(KB == 64, "a ring group is 16 rows x 128 bytes");
 };
 
-template <int BN, int TM, int D, int NW, int KB>
+template <int BN, int TM, int D, int NW, int KB, bool LINE>
 __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
     using SH = Shape<BN, TM, NW, KB>;
     constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, F = SH::F, L = SH::L, H = SH::H;
@@ -121,20 +119,27 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
 
     __shared__ u32x4 ring[D][F][64];
 
-    // Fragments this wavefront loads per stage: f = wave * L + i.  Per lane a
-    // fixed row pointer; the k offset moves with the stage.
+    // Load units this wavefront issues per stage: u = wave * L + i.  Per lane
+    // a fixed row pointer and k offset within the stage.  Fragment order:
+    // unit u is half u % 2 of 16-row group u / 2, lane l takes row l % 16 and
+    // k 32 (u % 2) + 8 (l / 16).  Line order: unit u is rows 8 (u % 2) .. + 7
+    // of group u / 2, lane l takes row 8 (u % 2) + l / 8 and stores, at
+    // position l % 8 of that row, k-chunk (l % 8) ^ swz(row).
     const uint8_t* src[L];
+    int koff[L];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-        const int f = wave * L + i;
-        if (f >= FW + SH::FX) {
-            src[i] = nullptr;   // padding fragment: loads the zero word
-        } else if (f < FW) {
-            int n = n_tile * BN + (f / H) * 16 + l16;
+        const int u = wave * L + i;
+        const int r = LINE ? (u & 1) * 8 + (lane >> 3) : l16;   // row within the group
+        koff[i] = LINE ? ((lane & 7) ^ ring_swz(r)) * 8 : (u & 1) * 32 + lg * 8;
+        if (u >= FW + SH::FX) {
+            src[i] = nullptr;   // padding unit: loads the zero word
+        } else if (u < FW) {
+            int n = n_tile * BN + (u >> 1) * 16 + r;
             n = n < N ? n : N - 1;
             src[i] = (const uint8_t*)a.W + (int64_t)n * K * 2;
         } else {
-            int m = m_tile * TM + ((f - FW) / H) * 16 + l16;
+            int m = m_tile * TM + ((u - FW) >> 1) * 16 + r;
             m = m < M ? m : M - 1;
             src[i] = (const uint8_t*)a.X + (int64_t)m * K * 2;
         }
@@ -142,10 +147,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
     auto issue = [&](int kb, int slot) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
-            const int f = wave * L + i;
-            const int k = kb * KB + (f % H) * 32 + lg * 8;
+            const int u = wave * L + i;
+            const int k = kb * KB + koff[i];   // K % 8 == 0: a chunk is wholly in or out
             const void* p = (src[i] && k < K) ? (const void*)(src[i] + (size_t)k * 2) : (const void*)&g_zero16;
-            dma16(p, &ring[slot][f][0]);
+            dma16(p, &ring[slot][u][0]);
         }
     };
 
@@ -159,6 +164,17 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
 #pragma unroll
     for (int d = 0; d < D - 1; ++d)
         if (d < nkb) issue(kb0 + d, d);
+
+    // Operand of lane l for half h of a 16-row group: fragment order, entry l
+    // of unit 2 g + h; line order, row l % 16 of the group at position
+    // (4 h + l / 16) ^ swz(row) (the two units of the group are contiguous).
+    const int rsw = ring_swz(l16);
+    auto operand = [&](int slot, int unit0, int h) -> u32x4 {
+        if constexpr (LINE)
+            return (&ring[slot][unit0][0])[l16 * 8 + ((4 * h + lg) ^ rsw)];
+        else
+            return ring[slot][unit0 + h][lane];
+    };
     for (int i = 0; i < nkb; ++i) {
         wait_stages<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
         asm volatile("" ::: "memory");
@@ -170,9 +186,9 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
         for (int h = 0; h < H; ++h) {
             u32x4 bw[NF], ax[MT];
 #pragma unroll
-            for (int f = 0; f < NF; ++f) bw[f] = ring[slot][(wr * NF + f) * H + h][lane];
+            for (int f = 0; f < NF; ++f) bw[f] = operand(slot, 2 * (wr * NF + f), h);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) ax[t] = ring[slot][FW + (wc * MT + t) * H + h][lane];
+            for (int t = 0; t < MT; ++t) ax[t] = operand(slot, FW + 2 * (wc * MT + t), h);
 #pragma unroll
             for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -271,8 +287,8 @@ size_t ws_ring(const Variant& v, int M, int N, int K) {
     return ws_counter_bytes((int)tiles) + (size_t)S * tiles * TM * BN * sizeof(float);
 }
 
-template <int BN, int TM, int D, int NW = 4, int KB = 64>
-void add_ring(std::vector<Variant>& out, int S) {
+template <int BN, int TM, int D, bool LINE, int NW = 4, int KB = 64>
+void add_ring1(std::vector<Variant>& out, int S) {
     static_assert(D * Shape<BN, TM, NW, KB>::F * 1024 <= 160 * 1024, "LDS ring too large");
     Variant v{};
     v.kind = LIN_KIND_SKINNY_BF16;
@@ -280,15 +296,23 @@ void add_ring(std::vector<Variant>& out, int S) {
     v.cfg.rows = BN;
     v.cfg.unroll = D;
     v.cfg.split = S;
-    v.cfg.stage_x = 3;   // W and X blocks through an LDS ring of direct loads
+    // W and X blocks through an LDS ring of direct loads: 3 fragment order,
+    // 4 line order
+    v.cfg.stage_x = LINE ? 4 : 3;
     v.cfg.tile_m = TM;
     v.mt = 0;
     v.min_m = TM <= 16 ? 1 : 16;
-    v.func = (const void*)&gemm_mfma_ring_kernel<BN, TM, D, NW, KB>;
+    v.func = (const void*)&gemm_mfma_ring_kernel<BN, TM, D, NW, KB, LINE>;
     v.geometry = &geom_ring<BN, TM, D, NW, KB>;
     v.workspace = &ws_ring<BN, TM, D, NW, KB>;
     v.block = 64 * NW;
     out.push_back(v);
+}
+
+template <int BN, int TM, int D>
+void add_ring(std::vector<Variant>& out, int S) {
+    add_ring1<BN, TM, D, false>(out, S);
+    add_ring1<BN, TM, D, true>(out, S);
 }
 
 }  // namespace

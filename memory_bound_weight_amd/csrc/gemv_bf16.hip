@@ -13,7 +13,7 @@ __global__ __launch_bounds__(kBlock) void gemv_bf16_valu(KArgs a) {
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 static bool geom_bf16(const Variant&, int M, int N, int K, dim3* grid, size_t* lds) {
     constexpr int rows_per_block = R * (4 / SPLIT);
-    size_t bytes = STAGE ? (size_t)MT * (size_t)(K / 8) * 16 : 0;
+    size_t bytes = STAGE ? 16 * stage_x_units(MT, K) : 0;
     if (bytes > kMaxDynLds) return false;
     (void)M;
     *grid = dim3((unsigned)((N + rows_per_block - 1) / rows_per_block));
@@ -47,10 +47,9 @@ static void add_splits(std::vector<Variant>& out) {
     add<MT, R, U, 1, false>(out);
     add<MT, R, U, 2, false>(out);
     add<MT, R, U, 4, false>(out);
-    if constexpr (MT >= 2) {
-        add<MT, R, U, 1, true>(out);
-        add<MT, R, U, 4, true>(out);
-    }
+    add<MT, R, U, 1, true>(out);
+    add<MT, R, U, 2, true>(out);
+    add<MT, R, U, 4, true>(out);
 }
 
 void register_gemv_bf16(std::vector<Variant>& out) {

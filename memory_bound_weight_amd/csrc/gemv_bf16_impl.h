@@ -11,7 +11,10 @@
 // loads of step i+1 are issued before the products of step i.  With SPLIT > 1,
 // SPLIT wavefronts share the same rows, each taking a contiguous part of K, and
 // combine through LDS; this fills the chip when N is small.  x is read through
-// the cache hierarchy, or staged in LDS once per workgroup when STAGE is set.
+// the cache hierarchy, or, when STAGE is set, copied into LDS once per
+// workgroup with coalesced direct-to-LDS loads issued before the first weight
+// loads (only those copies are waited for, so the copy overlaps the latency
+// of the first weight stage).
 // Products use v_dot2_f32_bf16 (two exact bf16 products per instruction, fp32
 // sums); each lane sums K/512 chunks, then a permlane/DPP tree sums the lanes.
 #pragma once
@@ -38,15 +41,7 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
     const uint16_t* __restrict__ X = (const uint16_t*)a.X;
 
     extern __shared__ u32x4 xs[];   // STAGE: [MT][nch] chunks of x
-    if constexpr (STAGE) {
-        for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
-            const int m = i / nch;
-            const int c = i - m * nch;
-            const int mm = m < M ? m : 0;
-            xs[i] = load_x16((const uint8_t*)(X + (size_t)mm * K), (uint32_t)c * 16u);
-        }
-        __syncthreads();
-    }
+    if constexpr (STAGE) stage_x_dma(X, M, MT, K, xs);
 
     const int64_t row0 = (block * GROUPS + grp) * R;
     const uint8_t* wb[R];
@@ -122,11 +117,21 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
     };
 
     // two register stages in flight (unrolled by two: no copies)
-    const int nsteps = (cend - cbeg + STEP - 1) / STEP;
+    const int nsteps = cend > cbeg ? (cend - cbeg + STEP - 1) / STEP : 0;
     int cb = cbeg;
+    Stage s0, s1;
+    if (nsteps > 0) load(s0, cb);
+    if constexpr (STAGE) {
+        // The x copies were issued before the U R loads of stage 0, and loads
+        // complete in order: waiting down to U R leaves stage 0 in flight.
+        // The barrier makes every wavefront's copies visible.
+        if (nsteps > 0)
+            wait_cnt<U * R, 15>();
+        else
+            wait_cnt<0, 15>();
+        barrier_only();
+    }
     if (nsteps > 0) {
-        Stage s0, s1;
-        load(s0, cb);
         for (int it = 0;;) {
             if (it + 1 < nsteps) load(s1, cb + STEP);
             step(s0, cb);

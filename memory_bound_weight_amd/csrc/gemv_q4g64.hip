@@ -13,7 +13,7 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 static bool geom_q4(const Variant&, int M, int N, int K, dim3* grid, size_t* lds) {
     constexpr int rows_per_block = R * (4 / SPLIT);
-    size_t bytes = STAGE ? (size_t)MT * (size_t)(K / 32) * (64 + 4) : 0;
+    size_t bytes = STAGE ? q4_stage_bytes(MT, K) : 0;
     if (bytes > kMaxDynLds) return false;
     (void)M;
     *grid = dim3((unsigned)((N + rows_per_block - 1) / rows_per_block));
@@ -44,6 +44,7 @@ static void add_splits(std::vector<Variant>& out) {
     add<MT, R, U, 2, false>(out);
     add<MT, R, U, 4, false>(out);
     add<MT, R, U, 1, true>(out);
+    add<MT, R, U, 2, true>(out);
     add<MT, R, U, 4, true>(out);
 }
 
@@ -53,6 +54,7 @@ void register_gemv_q4g64(std::vector<Variant>& out) {
     add_splits<1, 2, 1>(out);
     add_splits<1, 2, 2>(out);
     add_splits<1, 4, 1>(out);
+    add_splits<1, 4, 2>(out);
     add_splits<1, 8, 1>(out);
 
     add_splits<2, 1, 1>(out);

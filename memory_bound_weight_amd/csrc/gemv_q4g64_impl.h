@@ -20,8 +20,15 @@
 // the scale, about 1.2 vector operations per weight.
 //
 // x handling: either re-paired from cached global loads per chunk (cost shared
-// by the R rows), or, with STAGE, re-paired once per workgroup into LDS as
-// [MT][4][chunks] 16-byte words (bank-conflict-free reads) plus the chunk sums.
+// by the R rows), or, with STAGE, staged once per workgroup.  Per chunk a lane
+// needs 64 bytes of x for 16 bytes of weights, and those per-lane x loads
+// touch four times as many cache lines as the weight loads; they cost more of
+// the compute unit's load bandwidth than the weights themselves.  STAGE
+// copies x into LDS with coalesced direct-to-LDS loads issued before the
+// first weight loads, waits for those copies only, re-pairs x cooperatively
+// into [MT][4][chunks] 16-byte words (bank-conflict-free reads) plus the
+// chunk sums, and then reads x from LDS; all of this overlaps the latency of
+// the first weight stage.
 #pragma once
 
 #include <type_traits>
@@ -92,6 +99,16 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
     return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// LDS layout of the staged x (16-byte units): re-paired words MT * 4 * nch,
+// chunk sums MT * nch floats rounded up to whole units, then the raw copy.
+__host__ __device__ inline size_t q4_stage_raw_offset(int MT, int K) {
+    const size_t nch = (size_t)(K / 32);
+    return (size_t)MT * 4 * nch + ((size_t)MT * nch + 3) / 4;
+}
+__host__ __device__ inline size_t q4_stage_bytes(int MT, int K) {
+    return 16 * (q4_stage_raw_offset(MT, K) + stage_x_units(MT, K));
+}
+
 // One row block (R x 4/SPLIT rows) of the product, one per workgroup.
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block) {
@@ -109,25 +126,12 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
     const uint16_t* __restrict__ S = (const uint16_t*)a.S;
     const uint16_t* __restrict__ X = (const uint16_t*)a.X;
 
-    extern __shared__ u32x4 xs[];   // STAGE: [MT][4][nch] words, then [MT][nch] floats
+    // STAGE: [MT][4][nch] re-paired words, [MT][nch] chunk sums (padded to
+    // 16 bytes), then the raw copy of x (q4_stage_raw_offset).
+    extern __shared__ u32x4 xs[];
     float* xsum = (float*)(xs + (size_t)MT * 4 * nch);
-    if constexpr (STAGE) {
-        for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
-            const int m = i / nch;
-            const int c = i - m * nch;
-            const int mm = m < M ? m : 0;
-            const uint8_t* src = (const uint8_t*)(X + (size_t)mm * K);
-            u32x4 xd[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xd[t] = load_x16(src, (uint32_t)(4 * c + t) * 16u);
-            XChunk xc;
-            pair_x(xd, xc);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xs[(m * 4 + t) * nch + c] = xc.v[t];
-            xsum[m * nch + c] = xc.negsum;
-        }
-        __syncthreads();
-    }
+    u32x4* xraw = xs + q4_stage_raw_offset(MT, K);
+    if constexpr (STAGE) stage_x_dma(X, M, MT, K, xraw);
 
     const int64_t row0 = (block * GROUPS + grp) * R;
     const uint8_t* wb[R];
@@ -216,11 +220,34 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
     };
 
     // two register stages in flight (unrolled by two: no copies)
-    const int nsteps = (cend - cbeg + STEP - 1) / STEP;
+    const int nsteps = cend > cbeg ? (cend - cbeg + STEP - 1) / STEP : 0;
     int cb = cbeg;
+    Stage s0, s1;
+    if (nsteps > 0) load(s0, cb);
+    if constexpr (STAGE) {
+        // The x copies were issued before the 2 U R loads of stage 0, and
+        // loads complete in order: waiting down to 2 U R leaves stage 0 in
+        // flight.  The barrier makes every wavefront's copies visible.
+        if (nsteps > 0)
+            wait_cnt<2 * U * R, 15>();
+        else
+            wait_cnt<0, 15>();
+        barrier_only();
+        for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
+            const int m = i / nch;
+            const int c = i - m * nch;
+            const u32x4* src = xraw + (size_t)m * (K >> 3) + 4 * c;
+            const u32x4 xd[4] = {src[0], src[1], src[2], src[3]};
+            XChunk xc;
+            pair_x(xd, xc);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) xs[(m * 4 + t) * nch + c] = xc.v[t];
+            xsum[m * nch + c] = xc.negsum;
+        }
+        wait_cnt<63, 0>();   // LDS writes done, weight loads still in flight
+        barrier_only();
+    }
     if (nsteps > 0) {
-        Stage s0, s1;
-        load(s0, cb);
         for (int it = 0;;) {
             if (it + 1 < nsteps) load(s1, cb + STEP);
             step(s0, cb);

@@ -43,6 +43,74 @@ __device__ __forceinline__ uint16_t load_w2(const uint8_t* base, uint32_t off) {
     return __builtin_nontemporal_load((const uint16_t*)(base + off));
 }
 
+// s_waitcnt with vmcnt <= VM and lgkmcnt <= LGKM (expcnt not waited on).
+// The empty asm statements keep memory accesses from moving across it.
+template <int VM, int LGKM>
+__device__ __forceinline__ void wait_cnt() {
+    static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+    asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier without the vmcnt(0) that __syncthreads adds: loads still
+// in flight stay in flight.  Callers wait for what the barrier must cover.
+__device__ __forceinline__ void barrier_only() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+#define LDS_AS __attribute__((address_space(3)))
+
+// One direct-to-LDS load (gfx950 global_load_lds_dwordx4): 16 bytes per lane
+// from `g` into LDS at the wavefront-uniform address `lds` + 16 * lane.
+// Written as inline assembly so that the compiler does not make later LDS
+// reads wait for every outstanding load; callers order it with wait_cnt and
+// barriers.  M0 is set here and used by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved: set here, used by nothing else
+__device__ __forceinline__ void dma16(const void* g, const void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS const void*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+namespace {
+// Lanes with nothing to load read these zeros (a valid address).
+__device__ __attribute__((aligned(16))) const u32x4 g_zero16 = {0u, 0u, 0u, 0u};
+}  // namespace
+
+// 16-byte units of LDS that stage_x_dma fills for MT token rows of K bf16:
+// MT * K / 8, rounded up to whole wavefront loads (64 units).
+__host__ __device__ inline size_t stage_x_units(int MT, int K) {
+    return ((size_t)MT * (size_t)(K / 8) + 63) / 64 * 64;
+}
+
+// Issue the direct-to-LDS loads of MT token rows of x (bf16 [M][K], K a
+// multiple of 8) into `dst` in natural order, dst[m * K / 8 + j] = 16-byte
+// unit j of row m.  Rows m >= M load row 0 (finite values, never stored).
+// Wavefront loads are dealt round-robin to the four wavefronts; units past
+// the end land in the padding of stage_x_units.  Returns without waiting:
+// the loads complete in issue order with the wavefront's other loads.
+__device__ __forceinline__ void stage_x_dma(const void* X, int M, int MT, int K, u32x4* dst) {
+    const int nch = K >> 3;
+    const int total = MT * nch;
+    const int nload = (total + 63) >> 6;
+    const int lane = threadIdx.x & 63;
+    const u32x4* src = (const u32x4*)X;
+    for (int i = wave_id(); i < nload; i += 4) {
+        const int u = i * 64 + lane;
+        const u32x4* p = &g_zero16;
+        if (u < total) {
+            const int m = u / nch;
+            p = src + (m < M ? u : u - m * nch);
+        }
+        dma16(p, dst + i * 64);
+    }
+}
+
 // acc + a.lo*b.lo + a.hi*b.hi on two bf16 pairs (v_dot2_f32_bf16); the
 // bf16 x bf16 products are exact in fp32.
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {

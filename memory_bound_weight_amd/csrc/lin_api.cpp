@@ -180,12 +180,28 @@ int ensure_workspace(int dev, size_t bytes) {
     return LIN_OK;
 }
 
+// Dynamic LDS above the default 64 KB per workgroup must be allowed per
+// kernel first; the largest size allowed so far is kept per variant.
+bool allow_lds(int vi, size_t lds) {
+    if (lds <= 64 * 1024) return true;
+    static auto* allowed = new std::vector<size_t>(registry().size(), 64 * 1024);
+    std::lock_guard<std::mutex> lk(g_mu);
+    size_t& cur = (*allowed)[vi];
+    if (lds <= cur) return true;
+    if (hipFuncSetAttribute(registry()[vi].func, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)lds) != hipSuccess)
+        return false;
+    cur = lds;
+    return true;
+}
+
 int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
                    hipEvent_t ev1 = nullptr) {
     const Variant& v = registry()[vi];
     dim3 grid;
     size_t lds = 0;
     if (!v.geometry(v, a.M, a.N, a.K, &grid, &lds)) return LIN_ERR_UNSUPPORTED;
+    if (!allow_lds(vi, lds)) return LIN_ERR_HIP;
     KArgs args = a;
     args.splits = v.cfg.algo == LIN_ALGO_MFMA ? v.cfg.split : 1;
     args.ws = nullptr;
@@ -449,6 +465,93 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
     }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
+    if (rc != LIN_OK) return rc;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        table()[Key(dev, kind, M, N, K)] = best;
+    }
+    if (out) {
+        *out = registry()[best].cfg;
+        out->us = best_us;
+    }
+    return LIN_OK;
+}
+
+int lin_autotune_set(int kind, const void* const* W, const void* const* S, int count,
+                     const void* x, float* y, int64_t M, int64_t N, int64_t K, void* stream,
+                     lin_config* out) {
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_BF16) return LIN_ERR_ARG;
+    if (count < 1) return LIN_ERR_ARG;
+    if (!W || (kind == LIN_KIND_GEMV_Q4G64 && !S)) return LIN_ERR_NULL;
+    for (int j = 0; j < count; ++j) {
+        const int st = check(kind, W[j], S ? S[j] : nullptr, x, y, M, N, K);
+        if (st < 0) return st;
+        if (st > 0) return LIN_OK;
+    }
+    const auto cand = candidates(kind, M, N, K);
+    if (cand.empty()) return LIN_ERR_UNSUPPORTED;
+    const int dev = current_device();
+    if (dev < 0) return LIN_ERR_HIP;
+    size_t ws_max = 0;
+    for (int vi : cand) ws_max = std::max(ws_max, workspace_need(registry()[vi], M, N, K));
+    if (int rc0 = ensure_workspace(dev, ws_max)) return rc0;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return LIN_ERR_HIP;
+
+    // Candidates run on a private stream (default priority), captured as one
+    // graph of n launches cycling over the matrices, as a decode step runs them.
+    hipStream_t ts = nullptr;
+    if (hipStreamCreateWithFlags(&ts, hipStreamNonBlocking) != hipSuccess) return LIN_ERR_HIP;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    int rc = LIN_OK;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) rc = LIN_ERR_HIP;
+    const int n = count * std::max(1, (32 + count - 1) / count);
+    const int reps = 5;
+    int best = -1;
+    float best_us = 0.f;
+    for (size_t ci = 0; ci < cand.size() && rc == LIN_OK; ++ci) {
+        const int vi = cand[ci];
+        auto args = [&](int j) {
+            return KArgs{W[j % count], S ? S[j % count] : nullptr, x, y,
+                         (int)M, (int)N, (int)K, 1, nullptr};
+        };
+        // warm-up outside the capture (code load, LDS attribute)
+        if ((rc = launch_variant(vi, args(0), ts)) != LIN_OK) break;
+        if (hipStreamSynchronize(ts) != hipSuccess) { rc = LIN_ERR_HIP; break; }
+        hipGraph_t g = nullptr;
+        hipGraphExec_t ge = nullptr;
+        if (hipStreamBeginCapture(ts, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+            rc = LIN_ERR_HIP;
+            break;
+        }
+        int lrc = LIN_OK;
+        for (int j = 0; j < n && lrc == LIN_OK; ++j) lrc = launch_variant(vi, args(j), ts);
+        const hipError_t ce = hipStreamEndCapture(ts, &g);
+        if (lrc != LIN_OK || ce != hipSuccess) rc = lrc != LIN_OK ? lrc : LIN_ERR_HIP;
+        if (rc == LIN_OK && hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess)
+            rc = LIN_ERR_HIP;
+        float ms = 0.f;
+        if (rc == LIN_OK && (hipGraphLaunch(ge, ts) != hipSuccess ||   // warm replay
+                             hipEventRecord(e0, ts) != hipSuccess))
+            rc = LIN_ERR_HIP;
+        for (int r = 0; r < reps && rc == LIN_OK; ++r)
+            if (hipGraphLaunch(ge, ts) != hipSuccess) rc = LIN_ERR_HIP;
+        if (rc == LIN_OK && (hipEventRecord(e1, ts) != hipSuccess ||
+                             hipEventSynchronize(e1) != hipSuccess ||
+                             hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            rc = LIN_ERR_HIP;
+        if (ge) (void)hipGraphExecDestroy(ge);
+        if (g) (void)hipGraphDestroy(g);
+        if (rc != LIN_OK) break;
+        const float us = ms * 1000.f / (float)(reps * n);
+        if (best < 0 || us < best_us) {
+            best = vi;
+            best_us = us;
+        }
+    }
+    (void)hipStreamSynchronize(ts);
+    if (e0) (void)hipEventDestroy(e0);
+    if (e1) (void)hipEventDestroy(e1);
+    (void)hipStreamDestroy(ts);
     if (rc != LIN_OK) return rc;
     {
         std::lock_guard<std::mutex> lk(g_mu);

@@ -41,6 +41,8 @@ hipError_t launch_flush(void* buf, size_t n16, uint32_t salt, hipStream_t stream
 // Read-only streaming pass (achievable-bandwidth ceiling).
 hipError_t launch_stream_read(const void* buf, size_t bytes, hipStream_t stream);
 
-constexpr size_t kMaxDynLds = 64 * 1024;
+// Largest dynamic LDS a workgroup may ask for (gfx950: 160 KB per compute
+// unit; a little is left for the kernels' static arrays).
+constexpr size_t kMaxDynLds = 156 * 1024;
 
 }  // namespace lin

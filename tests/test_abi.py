@@ -97,6 +97,23 @@ def test_autotune_validation():
     assert t(0, None, None, None, None, 0, 8, 8, None, ctypes.byref(cfg)) == L.LIN_OK
 
 
+def test_autotune_set_validation():
+    cfg = L.LinConfig()
+    t = L._lib.lin_autotune_set
+    two = (ctypes.c_void_p * 2)(P, P)
+    null2 = (ctypes.c_void_p * 2)(None, None)
+    assert t(7, two, None, 2, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
+    assert t(0, two, None, 0, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
+    assert t(0, None, None, 2, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_NULL
+    assert t(1, two, None, 2, P, P, 1, 8, 64, None, ctypes.byref(cfg)) == L.LIN_ERR_NULL
+    assert t(0, null2, None, 2, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_NULL
+    assert t(0, two, None, 2, P, P, 9, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_SHAPE
+    assert t(0, two, None, 2, P, P, 1, 8, 12, None, ctypes.byref(cfg)) == L.LIN_ERR_SHAPE
+    misaligned = (ctypes.c_void_p * 2)(P, P + 8)
+    assert t(0, misaligned, None, 2, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ALIGN
+    assert t(0, two, None, 2, None, None, 0, 8, 8, None, ctypes.byref(cfg)) == L.LIN_OK
+
+
 def test_candidate_enumeration():
     for kind, M, N, K in [(0, 1, 2048, 2048), (0, 8, 512, 3584), (1, 1, 2048, 2048),
                           (1, 3, 512, 18944), (2, 8, 4096, 4096), (2, 17, 1024, 4096)]:

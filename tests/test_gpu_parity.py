@@ -27,7 +27,9 @@ def _inputs(seed, M, N, K):
 
 
 # shapes: one wave-load rows, ragged K tails (K % 512 != 0), ragged N, several tiles
-BF16_SHAPES = [(1, 8), (3, 24), (7, 520), (64, 2048), (129, 1032), (257, 4104), (2048, 2048)]
+# (37, 18944): x staged in more than 64 KB of LDS
+BF16_SHAPES = [(1, 8), (3, 24), (7, 520), (64, 2048), (129, 1032), (257, 4104), (2048, 2048),
+               (37, 18944)]
 BF16_M = [1, 2, 3, 5, 8]
 
 
@@ -48,7 +50,7 @@ def test_gemv_bf16_every_candidate(M, N, K):
             assert_within_bound(y, Y, B, "bf16 %s" % cfg)
 
 
-Q4_SHAPES = [(1, 64), (5, 192), (33, 576), (64, 2048), (130, 3584), (2048, 2048)]
+Q4_SHAPES = [(1, 64), (5, 192), (33, 576), (64, 2048), (130, 3584), (2048, 2048), (37, 18944)]
 Q4_M = [1, 2, 3, 8]
 
 
@@ -272,6 +274,43 @@ def test_split_k_workspace_shared_across_shapes():
                     y = L.lin_gemm_skinny_bf16(Wd, Xd)
                     torch.cuda.synchronize()
                     assert_within_bound(y, Y, B, "split-K %dx%dx%d %s" % (M, N, K, cfg))
+
+
+@pytest.mark.parametrize("kind,M,N,K", [(0, 1, 300, 2048), (1, 1, 300, 2048), (2, 64, 300, 1024)])
+def test_autotune_set_keeps_results_exact(kind, M, N, K):
+    """Tuning over a set of same-shaped matrices picks a candidate that the
+    later calls use, and that candidate still matches the oracle."""
+    print("case autotune_set kind=%d M=%d N=%d K=%d" % (kind, M, N, K), flush=True)
+    mats = [synth.weight(9700 + i, 0, 0, N, K) for i in range(3)]
+    X = synth.activation(9700, 0, 0, M, K)
+    Xd = X.to(DEV)
+    y = torch.empty((M, N), device=DEV)
+    if kind == L.LIN_KIND_GEMV_Q4G64:
+        qs = [oracle.quantize_q4g64(u16(W)) for W in mats]
+        Wqs = [torch.from_numpy(q).to(DEV) for q, _ in qs]
+        Ss = [synth.from_bits(sc, torch.float16, DEV) for _, sc in qs]
+        cfg = L.lin_autotune_set(kind, Wqs, Xd, y, Ss=Ss)
+    else:
+        Wds = [W.to(DEV) for W in mats]
+        cfg = L.lin_autotune_set(kind, Wds, Xd, y)
+    try:
+        assert cfg["us"] > 0
+        assert L.lin_get_config(kind, M, N, K) == dict(cfg, us=0.0)
+        for i in range(3):
+            y = torch.full((M, N), float("nan"), device=DEV)
+            if kind == L.LIN_KIND_GEMV_Q4G64:
+                Y, B = oracle.gemm_q4g64(qs[i][0], qs[i][1], u16(X))
+                L.lin_gemv_q4g64(Wqs[i], Ss[i], Xd, y)
+            else:
+                Y, B = oracle.gemm_dense(u16(mats[i]), u16(X))
+                if kind == L.LIN_KIND_GEMV_BF16:
+                    L.lin_gemv_bf16(Wds[i], Xd, y)
+                else:
+                    L.lin_gemm_skinny_bf16(Wds[i], Xd, y)
+            torch.cuda.synchronize()
+            assert_within_bound(y, Y, B, "autotune_set %s" % cfg)
+    finally:
+        L.lin_set_config(kind, M, N, K, None)
 
 
 def test_stream_read_runs_on_ragged_sizes():

@@ -297,8 +297,9 @@ class SkinnyCase:
 def skinny_variant(c):
     cfg = L.lin_get_config(L.LIN_KIND_SKINNY_BF16, c.M, c.N, c.K)
     if cfg["algo"] == L.LIN_ALGO_MFMA:
-        return "mfma rows%d tm%d D%d S%d X%d" % (cfg["rows"], cfg["tile_m"], cfg["unroll"],
-                                                cfg["split"], cfg["stage_x"])
+        return "mfma rows%d tm%d D%d S%d X%d%s" % (cfg["rows"], cfg["tile_m"], cfg["unroll"],
+                                                  cfg["split"], cfg["stage_x"],
+                                                  " W%d" % cfg["waves"] if cfg.get("waves") else "")
     return "valu R%d U%d S%d X%d tm%d" % (cfg["rows"], cfg["unroll"], cfg["split"],
                                          cfg["stage_x"], cfg["tile_m"])
 

@@ -81,8 +81,10 @@ typedef enum lin_algo {
  * 64-k block of X is staged in LDS per step; `stage_x` = 3 or 4: W and X
  * blocks both stream through an LDS ring of `unroll` stages filled by direct
  * global-to-LDS loads, in the matrix-core operand order (3) or in whole
- * 128-byte lines with a swizzled layout (4).  `us` is filled by lin_autotune
- * (median microseconds per call, cold caches) and ignored on input. */
+ * 128-byte lines with a swizzled layout (4); `waves` = wavefronts per
+ * workgroup of the ring kernel (0 means the default, four; 8 puts two on each
+ * SIMD).  `us` is filled by lin_autotune (median microseconds per call, cold
+ * caches) and ignored on input. */
 typedef struct lin_config {
     int32_t algo;
     int32_t rows;
@@ -90,7 +92,8 @@ typedef struct lin_config {
     int32_t split;
     int32_t stage_x;
     int32_t tile_m;
-    int32_t reserved[2];
+    int32_t waves;
+    int32_t reserved;
     float us;
 } lin_config;
 

@@ -43,17 +43,18 @@ EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemm_skinny_bf16", "lin_autot
 class LinConfig(ctypes.Structure):
     _fields_ = [("algo", ctypes.c_int32), ("rows", ctypes.c_int32), ("unroll", ctypes.c_int32),
                 ("split", ctypes.c_int32), ("stage_x", ctypes.c_int32), ("tile_m", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2), ("us", ctypes.c_float)]
+                ("waves", ctypes.c_int32), ("reserved", ctypes.c_int32), ("us", ctypes.c_float)]
 
     def as_dict(self):
         return dict(algo=self.algo, rows=self.rows, unroll=self.unroll, split=self.split,
-                    stage_x=self.stage_x, tile_m=self.tile_m, us=self.us)
+                    stage_x=self.stage_x, tile_m=self.tile_m, waves=self.waves, us=self.us)
 
     @classmethod
     def from_dict(cls, d):
         c = cls()
         for k in ("algo", "rows", "unroll", "split", "stage_x", "tile_m"):
             setattr(c, k, int(d[k]))
+        c.waves = int(d.get("waves", 0))
         return c
 
 
@@ -288,8 +289,8 @@ TUNING_DIR = os.path.join(_HERE, "tuning")
 
 def save_tuning(path, entries):
     """Persist tuned configurations: entries = {(kind, M, N, K): cfg dict}."""
-    rows = [dict(kind=k[0], M=k[1], N=k[2], K=k[3], cfg={f: v[f] for f in
-            ("algo", "rows", "unroll", "split", "stage_x", "tile_m", "us")})
+    rows = [dict(kind=k[0], M=k[1], N=k[2], K=k[3], cfg={f: v.get(f, 0) for f in
+            ("algo", "rows", "unroll", "split", "stage_x", "tile_m", "waves", "us")})
             for k, v in sorted(entries.items())]
     with open(path, "w") as f:
         json.dump({"device": torch.cuda.get_device_name(0) if torch.cuda.is_available() else "",

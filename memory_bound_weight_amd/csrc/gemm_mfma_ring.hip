@@ -182,18 +182,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
         asm volatile("" ::: "memory");
         if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
         const int slot = i % D;
+        // All operand reads of the stage are issued up front; the scheduler
+        // is then asked to interleave the reads of the second half with the
+        // products of the first, so that their LDS latency overlaps the
+        // matrix cores instead of stalling in front of them.
+        u32x4 bw[H][NF], ax[H][MT];
 #pragma unroll
         for (int h = 0; h < H; ++h) {
-            u32x4 bw[NF], ax[MT];
 #pragma unroll
-            for (int f = 0; f < NF; ++f) bw[f] = operand(slot, 2 * (wr * NF + f), h);
+            for (int f = 0; f < NF; ++f) bw[h][f] = operand(slot, 2 * (wr * NF + f), h);
 #pragma unroll
-            for (int t = 0; t < MT; ++t) ax[t] = operand(slot, FW + 2 * (wc * MT + t), h);
+            for (int t = 0; t < MT; ++t) ax[h][t] = operand(slot, FW + 2 * (wc * MT + t), h);
+        }
+#pragma unroll
+        for (int h = 0; h < H; ++h)
 #pragma unroll
             for (int f = 0; f < NF; ++f)
 #pragma unroll
-                for (int t = 0; t < MT; ++t) acc[f][t] = mfma16(ax[t], bw[f], acc[f][t]);
+                for (int t = 0; t < MT; ++t) acc[f][t] = mfma16(ax[h][t], bw[h][f], acc[f][t]);
+        // first half's reads, then one read of the second half per product
+        __builtin_amdgcn_sched_group_barrier(0x100, NF + MT, 0);
+#pragma unroll
+        for (int q = 0; q < (H - 1) * (NF + MT); ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, H * NF * MT - (H - 1) * (NF + MT), 0);
     }
 
     // Output: lane holds W row n0 + 16 f + l16, tokens m0 + 16 t + 4 lg + r.
@@ -299,6 +313,7 @@ void add_ring1(std::vector<Variant>& out, int S) {
     // W and X blocks through an LDS ring of direct loads: 3 fragment order,
     // 4 line order
     v.cfg.stage_x = LINE ? 4 : 3;
+    v.cfg.waves = NW == 4 ? 0 : NW;
     v.cfg.tile_m = TM;
     v.mt = 0;
     v.min_m = TM <= 16 ? 1 : 16;
@@ -329,6 +344,12 @@ void register_gemm_mfma_ring(std::vector<Variant>& out) {
         add_ring<128, 64, 4>(out, S);
         add_ring<64, 256, 3>(out, S);
         add_ring<128, 128, 4>(out, S);
+        add_ring<128, 128, 2>(out, S);
+        add_ring<64, 128, 3>(out, S);
+        add_ring<128, 64, 3>(out, S);
+        add_ring1<128, 128, 4, true, 8>(out, S);
+        add_ring1<128, 128, 2, true, 8>(out, S);
+        add_ring1<64, 64, 4, true, 8>(out, S);
     }
 }
 

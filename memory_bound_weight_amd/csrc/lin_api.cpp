@@ -45,7 +45,7 @@ int pow2ceil(int64_t m) {
 
 bool same_cfg(const lin_config& a, const lin_config& b) {
     return a.algo == b.algo && a.rows == b.rows && a.unroll == b.unroll && a.split == b.split &&
-           a.stage_x == b.stage_x && a.tile_m == b.tile_m;
+           a.stage_x == b.stage_x && a.tile_m == b.tile_m && a.waves == b.waves;
 }
 
 bool applicable(const Variant& v, int kind, int64_t M, int64_t N, int64_t K) {
@@ -95,7 +95,9 @@ int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
             const int tm_pick = tm == 256 ? 128 : tm;
             for (int i : candidates(kind, M, N, K)) {
                 const Variant& v = registry()[i];
-                if (v.cfg.algo != LIN_ALGO_MFMA || v.cfg.stage_x != 3 || v.cfg.split != 1) continue;
+                if (v.cfg.algo != LIN_ALGO_MFMA || v.cfg.stage_x != 4 || v.cfg.split != 1 ||
+                    v.cfg.waves != 0)
+                    continue;
                 if (v.cfg.tile_m == tm_pick && v.cfg.rows == bn) return i;
             }
             for (int i : candidates(kind, M, N, K))

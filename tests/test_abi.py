@@ -144,4 +144,4 @@ def test_default_skinny_config_needs_no_workspace():
         for N, K in ((1024, 4096), (14336, 4096), (4096, 14336), (300, 4104)):
             c = L.lin_get_config(L.LIN_KIND_SKINNY_BF16, M, N, K)
             if c["algo"] == L.LIN_ALGO_MFMA:
-                assert c["split"] == 1 and c["stage_x"] == 3, (M, N, K, c)
+                assert c["split"] == 1 and c["stage_x"] == 4 and c["waves"] == 0, (M, N, K, c)

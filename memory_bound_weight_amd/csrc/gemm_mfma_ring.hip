@@ -23,7 +23,7 @@
 //    (two units) are still one ds_read_b128 spread over the banks.  Half as
 //    many cache lines per load instruction: X, which every workgroup re-reads
 //    from L2, streams faster (measured 40 %), at a small cost in LDS reads.
-// The four wavefronts share the loads of a stage.  Iteration i waits (vmcnt)
+// The wavefronts share the loads of a stage.  Iteration i waits (vmcnt)
 // until its own loads of stage i have landed, meets the others at one
 // s_barrier (their loads have landed too, and everyone has finished reading
 // stage i - 1), refills the slot of stage i - 1 with stage i + D - 1, then
@@ -31,7 +31,8 @@
 // re-read the last row (never stored).
 //
 // Wave tile.  The workgroup tile BN x TM is split 2 x 2 (or 1 x 4 when TM is
-// 256) among the four wavefronts; each keeps its NF x MT 16x16 fp32
+// 256) among four wavefronts, or 2 x 4 / 4 x 2 among eight (two per SIMD,
+// so one can multiply while the other waits); each keeps its NF x MT 16x16 fp32
 // accumulators in registers and writes them directly, or as a split-K partial
 // that the last workgroup of the tile adds in split order (deterministic).
 #include "registry.h"

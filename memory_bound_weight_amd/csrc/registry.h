@@ -15,7 +15,7 @@ namespace lin {
 
 struct Variant {
     int kind;          // LIN_KIND_*
-    lin_config cfg;    // public description (algo, rows, unroll, split, stage_x, tile_m)
+    lin_config cfg;    // public description (algo, rows, unroll, split, stage_x, tile_m, waves)
     int mt;            // VALU: tokens per instance (M <= mt); MFMA: 0 (any M in range)
     int min_m;         // smallest M this variant accepts
     const void* func;  // __global__ function

@@ -161,7 +161,9 @@ int lin_get_config(int kind, int64_t M, int64_t N, int64_t K, lin_config* out);
  * split-K configuration makes the library grow its per-device workspace here
  * (allocation and device synchronisation), never in the product calls; a
  * product call whose pinned configuration lacks workspace returns
- * LIN_ERR_UNSUPPORTED.  Product calls that use split-K share the device's
+ * LIN_ERR_UNSUPPORTED.  A configuration that stages x in more than 64 KB of
+ * LDS has that limit raised for its kernel here as well (otherwise on its
+ * first launch).  Product calls that use split-K share the device's
  * workspace, so such calls on one device must not run concurrently on
  * different streams. */
 int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg);

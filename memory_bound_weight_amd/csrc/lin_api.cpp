@@ -363,6 +363,13 @@ int set_config_reserving(int kind, int64_t M, int64_t N, int64_t K, const lin_co
         if (dev < 0) return LIN_ERR_HIP;
         int rc = ensure_workspace(dev, workspace_need(registry()[vi], M, N, K));
         if (rc != LIN_OK) return rc;
+        // enable the dynamic LDS the configuration needs now, not at its
+        // first launch (which may be inside a graph capture)
+        dim3 grid;
+        size_t lds = 0;
+        const Variant& v = registry()[vi];
+        if (v.geometry(v, (int)M, (int)N, (int)K, &grid, &lds) && !allow_lds(vi, lds))
+            return LIN_ERR_HIP;
     }
     return LIN_OK;
 }

@@ -313,6 +313,41 @@ def test_autotune_set_keeps_results_exact(kind, M, N, K):
         L.lin_set_config(kind, M, N, K, None)
 
 
+def test_large_lds_configuration_pinned_then_captured_in_a_graph():
+    """A staged-x configuration above 64 KB of LDS, pinned at load time, runs
+    correctly when its first launch is inside a graph capture; every replay
+    (with eager work in between) matches the oracle."""
+    N, K, M = 37, 18944, 1
+    print("case large-LDS graph N=%d K=%d" % (N, K), flush=True)
+    W, X = _inputs(9800, M, N, K)
+    Wq, S = oracle.quantize_q4g64(u16(W))
+    Y, B = oracle.gemm_q4g64(Wq, S, u16(X))
+    Wqd = torch.from_numpy(Wq).to(DEV)
+    Sd = synth.from_bits(S, torch.float16, DEV)
+    Xd = X.to(DEV)
+    staged = [c for c in L.lin_candidates(L.LIN_KIND_GEMV_Q4G64, M, N, K) if c["stage_x"] == 1]
+    assert staged
+    cfg = staged[0]
+    y = torch.full((M, N), float("nan"), device=DEV)
+    try:
+        L.lin_set_config(L.LIN_KIND_GEMV_Q4G64, M, N, K, cfg)
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                L.lin_gemv_q4g64(Wqd, Sd, Xd, y)
+        for rep in range(3):
+            y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert_within_bound(y, Y, B, "graph replay %d %s" % (rep, cfg))
+            torch.empty(1 << 20, device=DEV).normal_()   # eager work between replays
+    finally:
+        L.lin_set_config(L.LIN_KIND_GEMV_Q4G64, M, N, K, None)
+
+
 def test_stream_read_runs_on_ragged_sizes():
     """The read-only pass used as the bandwidth ceiling: any multiple of 16
     bytes, including sizes that leave a partial workgroup, completes without

@@ -23,7 +23,8 @@
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points
- * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemm_skinny_bf16, lin_quantize_q4g64)
+ * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemm_skinny_bf16, lin_gemm_skinny_q4g64,
+ * lin_quantize_q4g64, lin_q4g64_tile)
  * validate their arguments in O(1), enqueue kernels on `stream` (a hipStream_t;
  * NULL = the null stream) and return without waiting: they never allocate,
  * never synchronise and are safe inside HIP graph capture.  Results are
@@ -50,23 +51,24 @@ typedef enum lin_status {
     LIN_OK = 0,
     LIN_ERR_NULL = -1,        /* a required pointer is NULL */
     LIN_ERR_SHAPE = -2,       /* M, N or K out of range, or K not a multiple of 8 (bf16) / 64 (int4) */
-    LIN_ERR_ALIGN = -3,       /* W, Wq, x or X not 16-byte aligned; y, Y not 4-byte; S not 2-byte */
+    LIN_ERR_ALIGN = -3,       /* W, Wq, Wt, St, x or X not 16-byte aligned; y, Y not 4-byte; S not 2-byte */
     LIN_ERR_UNSUPPORTED = -4, /* the requested configuration cannot run this shape */
     LIN_ERR_HIP = -5,         /* the HIP runtime reported an error */
     LIN_ERR_ARG = -6          /* unknown kind, malformed configuration, bad index */
 } lin_status;
 
-/* The three products; `kind` selects one in the tuning calls. */
+/* The four products; `kind` selects one in the tuning calls. */
 typedef enum lin_kind {
     LIN_KIND_GEMV_BF16 = 0,   /* lin_gemv_bf16 */
     LIN_KIND_GEMV_Q4G64 = 1,  /* lin_gemv_q4g64 */
-    LIN_KIND_SKINNY_BF16 = 2  /* lin_gemm_skinny_bf16 */
+    LIN_KIND_SKINNY_BF16 = 2, /* lin_gemm_skinny_bf16 */
+    LIN_KIND_SKINNY_Q4G64 = 3 /* lin_gemm_skinny_q4g64 (tiled int4-g64 weights) */
 } lin_kind;
 
 /* Kernel families. */
 typedef enum lin_algo {
     LIN_ALGO_VALU = 1,        /* vector-ALU streaming product: each wavefront owns `rows` rows */
-    LIN_ALGO_MFMA = 2         /* matrix-core tiles (skinny bf16 product only) */
+    LIN_ALGO_MFMA = 2         /* matrix-core tiles (the two skinny products) */
 } lin_algo;
 
 /* One launch configuration.  VALU: a wavefront owns `rows` consecutive rows and
@@ -83,8 +85,11 @@ typedef enum lin_algo {
  * global-to-LDS loads, in the matrix-core operand order (3) or in whole
  * 128-byte lines with a swizzled layout (4); `waves` = wavefronts per
  * workgroup of the ring kernel (0 means the default, four; 8 puts two on each
- * SIMD).  `us` is filled by lin_autotune (median microseconds per call, cold
- * caches) and ignored on input. */
+ * SIMD).  LIN_KIND_SKINNY_Q4G64 has one family, `stage_x` = 4: codes, scales
+ * and X stream through an LDS ring of `unroll` stages of 128 k, `rows` W rows
+ * by `tile_m` tokens per workgroup, `split` as above.  `us` is filled by
+ * lin_autotune (median microseconds per call, cold caches) and ignored on
+ * input. */
 typedef struct lin_config {
     int32_t algo;
     int32_t rows;
@@ -97,7 +102,7 @@ typedef struct lin_config {
     float us;
 } lin_config;
 
-/* Largest M accepted by lin_gemv_bf16 / lin_gemv_q4g64, and by lin_gemm_skinny_bf16. */
+/* Largest M accepted by lin_gemv_bf16 / lin_gemv_q4g64, and by the skinny products. */
 #define LIN_GEMV_MAX_M 8
 #define LIN_SKINNY_MAX_M 256
 /* Largest K accepted by every product. */
@@ -119,11 +124,42 @@ int lin_gemv_q4g64(const void* Wq, const void* S, const void* x, float* y,
 int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y,
                          int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Batched-token product with int4-g64 weights, for 1 <= M <= LIN_SKINNY_MAX_M
+ * tokens: Y[m][n] = sum_k q[n][k] * S[n][k/64] * X[m][k], fp32 Y [M][N], bf16 X
+ * [M][K], K % 64 == 0, the weights in the tiled layout of lin_q4g64_tile (Wt
+ * and St 16-byte aligned).  The reordering is the one the llm-rs benchmark
+ * post (section 6) describes for 4-bit GEMMs: done once at load time, so that
+ * one 16-byte load gives each lane exactly the codes of its matrix-core
+ * operands.  Runs on the matrix cores for every M; products are exact in fp32
+ * and the scales are applied in fp32 per group (the bound above holds). */
+int lin_gemm_skinny_q4g64(const void* Wt, const void* St, const void* X, float* Y,
+                          int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Bytes of the tiled int4-g64 layout of an N x K matrix (K % 64 == 0):
+ * *wt_bytes = ceil(N/16) * ceil(K/128) * 1024, *st_bytes = ceil(N/16) *
+ * ceil(K/128) * 64. */
+int lin_q4g64_tiled_size(int64_t N, int64_t K, int64_t* wt_bytes, int64_t* st_bytes);
+
+/* Load-time weight preparation for lin_gemm_skinny_q4g64: rearrange Wq [N][K/2]
+ * and S [N][K/64] (the layouts above; Wq 16-byte, S 2-byte aligned) into
+ * caller-owned Wt and St (16-byte aligned, sizes from lin_q4g64_tiled_size).
+ * With N16 = ceil(N/16) and KB = ceil(K/128):
+ *   Wt: N16 x KB units of 1024 bytes, unit (T, j) at byte (T * KB + j) * 1024;
+ *       its byte 16 l + 4 t + b (lane l < 64, t < 4, b < 4) is byte
+ *       64 j + 16 t + 4 (l / 16) + b of Wq row 16 T + (l mod 16), i.e. the
+ *       codes of k = 128 j + 32 t + 8 (l / 16) + 2 b and + 1;
+ *   St: KB x N16 units of 64 bytes, unit (j, T) at byte (j * N16 + T) * 64;
+ *       its fp16 element 2 r + h (r < 16, h < 2) is S[16 T + r][2 j + h].
+ * Entries past row N - 1 or past k = K - 1 are zero.  Enqueued on `stream`;
+ * allocates nothing.  N == 0 or K == 0 enqueues nothing. */
+int lin_q4g64_tile(const void* Wq, const void* S, void* Wt, void* St,
+                   int64_t N, int64_t K, void* stream);
+
 /* Load-time tuning (tinyinfer post, "v0.2": time the candidates on every
  * distinct shape when the model loads, keep the fastest).  Times every
  * candidate configuration of `kind` for (M, N, K) on the caller's buffers,
- * which must be valid for that kind (S is used only by LIN_KIND_GEMV_Q4G64 and
- * may be NULL otherwise; y receives scratch results).  Each timed call starts
+ * which must be valid for that kind (S is used only by the int4 kinds and
+ * may be NULL otherwise; W and S are Wt and St for LIN_KIND_SKINNY_Q4G64; y receives scratch results).  Each timed call starts
  * from cold caches.  The fastest configuration is stored in the per-device
  * table and used by later calls with the same (kind, M, N, K); if `out` is not
  * NULL it receives it, with `us` set.  Unlike the compute calls this one
@@ -135,8 +171,8 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
 
 /* The same load-time tuning timed the way a decode step runs the layer: every
  * candidate is captured as one graph of back-to-back calls cycling over the
- * `count` >= 1 weight matrices W[0..count-1] (and S[0..count-1] for
- * LIN_KIND_GEMV_Q4G64; S may be NULL otherwise) of the same shape, e.g. the
+ * `count` >= 1 weight matrices W[0..count-1] (and S[0..count-1] for the
+ * int4 kinds; S may be NULL otherwise) of the same shape, e.g. the
  * layers of a model, and the graph is replayed; `us` is the mean time per
  * call.  W and S are host arrays of device pointers, owned by the caller and
  * only read during the call.  Stores the fastest configuration like

@@ -27,6 +27,7 @@ LIN_ERR_ARG = -6
 LIN_KIND_GEMV_BF16 = 0
 LIN_KIND_GEMV_Q4G64 = 1
 LIN_KIND_SKINNY_BF16 = 2
+LIN_KIND_SKINNY_Q4G64 = 3
 
 LIN_ALGO_VALU = 1
 LIN_ALGO_MFMA = 2
@@ -35,7 +36,8 @@ LIN_GEMV_MAX_M = 8
 LIN_SKINNY_MAX_M = 256
 
 # Every symbol include/lin.h declares.
-EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemm_skinny_bf16", "lin_autotune",
+EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemm_skinny_bf16", "lin_gemm_skinny_q4g64",
+           "lin_q4g64_tiled_size", "lin_q4g64_tile", "lin_autotune",
            "lin_autotune_set", "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
            "lin_quantize_q4g64", "lin_stream_read", "lin_status_string", "lin_version")
 
@@ -74,6 +76,9 @@ def _load():
         "lin_gemv_bf16": [P, P, P, I64, I64, I64, P],
         "lin_gemv_q4g64": [P, P, P, P, I64, I64, I64, P],
         "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
+        "lin_gemm_skinny_q4g64": [P, P, P, P, I64, I64, I64, P],
+        "lin_q4g64_tiled_size": [I64, I64, ctypes.POINTER(I64), ctypes.POINTER(I64)],
+        "lin_q4g64_tile": [P, P, P, P, I64, I64, P],
         "lin_autotune": [I, P, P, P, P, I64, I64, I64, P, ctypes.POINTER(LinConfig)],
         "lin_autotune_set": [I, ctypes.POINTER(P), ctypes.POINTER(P), I, P, P, I64, I64, I64, P,
                              ctypes.POINTER(LinConfig)],
@@ -186,6 +191,69 @@ def lin_gemm_skinny_bf16(W, X, Y=None):
     return Y
 
 
+class Q4Tiled:
+    """int4-g64 weights of an N x K matrix in the matrix-core tiled layout of
+    lin_q4g64_tile: Wt and St are flat uint8 device tensors."""
+    __slots__ = ("Wt", "St", "N", "K")
+
+    def __init__(self, Wt, St, N, K):
+        self.Wt, self.St, self.N, self.K = Wt, St, int(N), int(K)
+
+    @property
+    def shape(self):
+        return (self.N, self.K)
+
+    @property
+    def dtype(self):
+        return "q4g64_tiled"
+
+    @property
+    def device(self):
+        return self.Wt.device
+
+
+def lin_q4g64_tiled_size(N, K):
+    """(Wt bytes, St bytes) of the tiled layout of an N x K matrix."""
+    wt, st = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.lin_q4g64_tiled_size(N, K, ctypes.byref(wt), ctypes.byref(st)),
+           "lin_q4g64_tiled_size")
+    return wt.value, st.value
+
+
+def lin_q4g64_tile(Wq, S):
+    """Rearrange int4-g64 weights (Wq uint8 [N, K/2], S fp16 [N, K/64]) into the
+    tiled layout lin_gemm_skinny_q4g64 reads; returns a Q4Tiled."""
+    _need(Wq, torch.uint8, "Wq", 2)
+    _need(S, torch.float16, "S", 2)
+    N, K = Wq.shape[0], 2 * Wq.shape[1]
+    if tuple(S.shape) != (N, K // 64):
+        raise ValueError("shape mismatch: Wq [N, K/2], S [N, K/64]")
+    wb, sb = lin_q4g64_tiled_size(N, K)
+    Wt = torch.empty(max(wb, 16), dtype=torch.uint8, device=Wq.device)
+    St = torch.empty(max(sb, 16), dtype=torch.uint8, device=Wq.device)
+    _check(_lib.lin_q4g64_tile(Wq.data_ptr(), S.data_ptr(), Wt.data_ptr(), St.data_ptr(), N, K,
+                               _stream(Wq)), "lin_q4g64_tile")
+    return Q4Tiled(Wt, St, N, K)
+
+
+def lin_gemm_skinny_q4g64(W, X, Y=None):
+    """Y = X . W^T for M <= 256 tokens with int4-g64 weights W (a Q4Tiled from
+    lin_q4g64_tile), X bf16 [M, K]."""
+    X = _as2d(X)
+    if not isinstance(W, Q4Tiled):
+        raise TypeError("W must be a Q4Tiled (lin_q4g64_tile)")
+    _need(X, torch.bfloat16, "X", 2)
+    N, K = W.N, W.K
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X must have K = %d columns" % K)
+    Y = _out(Y, M, N, X.device)
+    _check(_lib.lin_gemm_skinny_q4g64(W.Wt.data_ptr(), W.St.data_ptr(), X.data_ptr(),
+                                      Y.data_ptr(), M, N, K, _stream(X)),
+           "lin_gemm_skinny_q4g64")
+    return Y
+
+
 def lin_quantize_q4g64(W, Wq=None, S=None):
     """int4-g64 weights from bf16 W [N, K]: returns (Wq uint8 [N, K/2], S fp16 [N, K/64])."""
     _need(W, torch.bfloat16, "W", 2)
@@ -212,6 +280,10 @@ def lin_stream_read(buf):
 
 def _shape_args(kind, W, S, x):
     x = _as2d(x)
+    if kind == LIN_KIND_SKINNY_Q4G64:
+        if not isinstance(W, Q4Tiled):
+            raise TypeError("LIN_KIND_SKINNY_Q4G64 takes Q4Tiled weights")
+        return x, x.shape[0], W.N, W.K
     if kind == LIN_KIND_GEMV_Q4G64:
         return x, x.shape[0], W.shape[0], 2 * W.shape[1]
     return x, x.shape[0], W.shape[0], W.shape[1]
@@ -221,6 +293,8 @@ def lin_autotune(kind, W, x, y, S=None):
     """Time every candidate for this shape on these buffers (cold caches), keep
     the fastest for later calls; returns it as a dict with 'us'."""
     x, M, N, K = _shape_args(kind, W, S, x)
+    if isinstance(W, Q4Tiled):
+        W, S = W.Wt, W.St
     cfg = LinConfig()
     _check(_lib.lin_autotune(int(kind), W.data_ptr(), S.data_ptr() if S is not None else None,
                              x.data_ptr(), y.data_ptr(), M, N, K, _stream(W), ctypes.byref(cfg)),
@@ -239,6 +313,9 @@ def lin_autotune_set(kind, Ws, x, y, Ss=None):
     for W in Ws:
         if tuple(W.shape) != tuple(Ws[0].shape) or W.dtype != Ws[0].dtype:
             raise ValueError("lin_autotune_set: every matrix must have the same shape and dtype")
+    if isinstance(Ws[0], Q4Tiled):
+        Ss = [W.St for W in Ws]
+        Ws = [W.Wt for W in Ws]
     wp = (ctypes.c_void_p * len(Ws))(*[W.data_ptr() for W in Ws])
     sp = None
     if Ss is not None:

@@ -36,100 +36,12 @@
 // 0, 1, ... (so the result does not depend on which one finishes last), writes
 // Y and resets the counter to zero for the next call.  No workgroup ever waits
 // for another.
+#include "mfma_common.h"
 #include "registry.h"
 
 namespace lin {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kBK = 64;   // k per block: two MFMA steps of 32
-
-__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-// Write a finished fp32 tile: lane holds rows 4*lg + r of each 16-token
-// sub-tile, column l16 of each W fragment.  With S > 1 the tile is a split-K
-// partial: publish it, count, and let the last arriver add the S partials in
-// split order and write Y (see the header comment).
-template <int NF, int TM>
-__device__ __forceinline__ void finish_tile(const KArgs& a, const f32x4 (&acc)[NF][TM / 16], int S,
-                                            int ks, int n_tile, int m_tile, int m_tiles,
-                                            int n_tiles, int n0, int m0) {
-    constexpr int BN = 64 * NF;
-    constexpr int MT = TM / 16;
-    const int M = a.M, N = a.N;
-    const int lane = threadIdx.x & 63;
-    const int wave = wave_id();
-    const int l16 = lane & 15, lg = lane >> 4;
-    if (S == 1) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            const int n = n0 + f * 16 + l16;
-            if (n >= N) continue;
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + t * 16 + lg * 4 + r;
-                    if (m < M) a.Y[(int64_t)m * N + n] = acc[f][t][r];
-                }
-        }
-        return;
-    }
-    const int tiles = m_tiles * n_tiles;
-    const int tile = n_tile * m_tiles + m_tile;
-    uint32_t* cnt = (uint32_t*)a.ws;
-    float* parts = (float*)((uint8_t*)a.ws + ws_counter_bytes(tiles));
-    const size_t tile_elems = (size_t)TM * BN;
-    float* mine = parts + ((size_t)ks * tiles + tile) * tile_elems;
-    // Partials are written and read with agent-scope atomic accesses, which go
-    // to the device-coherent level directly, so publishing needs no L2
-    // writeback and the reader no L2 invalidate (both are whole-cache
-    // operations on this chip and cost more than the product itself).  Order:
-    // every wave waits until its partial stores are complete, the workgroup
-    // synchronises, then one lane counts the tile; the workgroup that brings
-    // the count to S reads all S partials.
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __hip_atomic_store(&mine[(t * 16 + lg * 4 + r) * BN + wave * 16 * NF + f * 16 + l16],
-                                   acc[f][t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);   // vmcnt(0) expcnt(0) lgkmcnt(0): stores complete
-    __shared__ int last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last = (old == (uint32_t)(S - 1));
-    }
-    __syncthreads();
-    if (!last) return;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const int n = n0 + f * 16 + l16;
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ml = t * 16 + lg * 4 + r;
-                const size_t e = (size_t)ml * BN + wave * 16 * NF + f * 16 + l16;
-                float v = 0.f;
-                for (int j = 0; j < S; ++j)
-                    v += __hip_atomic_load(&parts[((size_t)j * tiles + tile) * tile_elems + e],
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const int m = m0 + ml;
-                if (m < M && n < N) a.Y[(int64_t)m * N + n] = v;
-            }
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 template <int NF, int TM, int D>
 __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
@@ -250,7 +162,7 @@ __global__ __launch_bounds__(kBlock) void gemm_mfma_kernel(KArgs a) {
         }
     }
 
-    finish_tile<NF, TM>(a, acc, S, ks, n_tile, m_tile, m_tiles, n_tiles, n0, m0);
+    store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wave * 16 * NF, 0);
 }
 
 template <int NF, int TM, int D>

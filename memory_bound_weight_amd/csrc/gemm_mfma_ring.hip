@@ -35,17 +35,11 @@
 // so one can multiply while the other waits); each keeps its NF x MT 16x16 fp32
 // accumulators in registers and writes them directly, or as a split-K partial
 // that the last workgroup of the tile adds in split order (deterministic).
+#include "mfma_common.h"
 #include "registry.h"
 
 namespace lin {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
 
 // Position of k-chunk c (8 k, 16 bytes) in row r of a ring group is
 // c ^ ring_swz(r).  The 16 rows of a group are 128 bytes apart, so unswizzled
@@ -211,71 +205,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, H * NF * MT - (H - 1) * (NF + MT), 0);
     }
 
-    // Output: lane holds W row n0 + 16 f + l16, tokens m0 + 16 t + 4 lg + r.
-    const int n0 = n_tile * BN + wr * SH::WN;
-    const int m0 = m_tile * TM + wc * SH::WM;
-    if (S == 1) {
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            const int n = n0 + f * 16 + l16;
-            if (n >= N) continue;
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m0 + t * 16 + lg * 4 + r;
-                    if (m < M) a.Y[(int64_t)m * N + n] = acc[f][t][r];
-                }
-        }
-        return;
-    }
-    // Split-K: publish the partial tile with coherent (agent-scope) stores, count
-    // the tile, and let the workgroup that completes the count add the S
-    // partials in split order.  Partial element (m, n) of a tile sits at
-    // m * BN + n (tile-local indices).
-    const int tiles = m_tiles * n_tiles;
-    const int tile = n_tile * m_tiles + m_tile;
-    uint32_t* cnt = (uint32_t*)a.ws;
-    float* parts = (float*)((uint8_t*)a.ws + ws_counter_bytes(tiles));
-    const size_t tile_elems = (size_t)TM * BN;
-    float* mine = parts + ((size_t)ks * tiles + tile) * tile_elems;
-    const int nl0 = wr * SH::WN, ml0 = wc * SH::WM;
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __hip_atomic_store(&mine[(size_t)(ml0 + t * 16 + lg * 4 + r) * BN + nl0 + f * 16 + l16],
-                                   acc[f][t][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);   // the partial stores are complete
-    __shared__ int last;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&cnt[tile], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last = (old == (uint32_t)(S - 1));
-    }
-    __syncthreads();
-    if (!last) return;
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-        const int n = n0 + f * 16 + l16;
-#pragma unroll
-        for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const size_t e = (size_t)(ml0 + t * 16 + lg * 4 + r) * BN + nl0 + f * 16 + l16;
-                float v = 0.f;
-                for (int j = 0; j < S; ++j)
-                    v += __hip_atomic_load(&parts[((size_t)j * tiles + tile) * tile_elems + e],
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const int m = m0 + t * 16 + lg * 4 + r;
-                if (m < M && n < N) a.Y[(int64_t)m * N + n] = v;
-            }
-    }
-    if (threadIdx.x == 0)
-        __hip_atomic_store(&cnt[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Output: lane holds W row n_tile BN + wr WN + 16 f + l16, tokens
+    // m_tile TM + wc WM + 16 t + 4 lg + r.
+    store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,
+                                wc * SH::WM);
 }
 
 template <int BN, int TM, int D, int NW, int KB>

@@ -1,0 +1,378 @@
+// Matrix-core product Y = X . W^T with int4-g64 weights, for batched decode
+// (M <= 256 tokens), and the load-time rearrangement of the weights it reads.
+//
+// Why this shape.  4-bit weights make the batched product four times lighter
+// on memory, so it reaches the matrix-core roof at a smaller batch; whether it
+// then stays faster than bf16 depends on how cheaply the codes become
+// matrix-core operands (llm-rs benchmark post, section 6: reordered weights at
+// load time, one 16-byte load per lane handing it exactly its fragment, and a
+// bit-trick conversion).  Here:
+//  - Tiled weights.  lin_q4g64_tile rearranges Wq once so that one 1 KB
+//    unit holds the codes of 16 rows x 128 k in operand order: lane l's 16
+//    bytes are the four 8-code k-slices it feeds to the four 16x16x32 products
+//    of that block (row l mod 16; k-step t covers 32 consecutive k inside one
+//    scale group).  Scales are rearranged so that one 64-byte unit holds the
+//    two groups of a 128-k block for 16 rows.
+//  - Unpacking.  As in the GEMV: ((w >> 4i) & 0x000F000F) ^ 0x43084308 turns a
+//    dword of codes into bf16 pairs 136 + q (exact), pairing nibble i with
+//    nibble i + 4; X is re-paired to match with four v_perm per operand.
+//  - The offset and the scales.  The products of one scale group start from
+//    C = -136 * sum(x) over the group, itself a matrix-core product of the X
+//    operands with a constant operand of -136 (exact products, fp32 sums), so
+//    D = sum(q x) for the group; then acc += s * D, one fma per output and
+//    group.  Every product is exact in fp32 and the scale is applied in fp32:
+//    nothing is rounded to bf16 on the way, unlike a dequantise-to-bf16 GEMM.
+//  - Data path.  Codes, scales and X stream through an LDS ring of direct
+//    global-to-LDS loads (gfx950 global_load_lds_dwordx4), D stages of one
+//    128-k block, like the bf16 ring kernel; the codes are a quarter of the
+//    bf16 bytes, so the ring mostly carries X.  X units are four token rows of
+//    256 bytes, whole cache lines, with the 16-byte chunks of row r stored at
+//    position c ^ r so that the operand reads of 16 rows spread over the banks.
+//  - Tiles, split-K, tile order and the output store are those of the bf16
+//    ring kernel (XCD-aware order, deterministic split-K).
+#include "mfma_common.h"
+#include "registry.h"
+
+namespace lin {
+namespace {
+
+constexpr int kQB = 128;   // k per ring stage and per tiled unit
+
+// bf16 pairs (-136, -136): the constant operand of the offset products.
+constexpr uint32_t kNeg136 = 0xC308C308u;
+
+template <int BN, int TM, int NW>
+struct Q4Shape {
+    static constexpr int WR = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4));
+    static constexpr int WC = NW / WR;
+    static constexpr int WN = BN / WR, WM = TM / WC;
+    static constexpr int NF = WN / 16, MT = WM / 16;
+    static constexpr int FW = BN / 16;       // code units (1 KB) per stage
+    static constexpr int FX = TM / 16 * 4;   // X units per stage (four token rows each)
+    static constexpr int XU = FW + 1;        // first X unit; unit FW holds the scales
+    static constexpr int F = (FW + 1 + FX + NW - 1) / NW * NW;   // units per stage, padded
+    static constexpr int L = F / NW;         // units each wavefront loads per stage
+    static_assert(NF >= 1 && MT >= 1 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
+    static_assert(FW * 64 <= 1024, "the scales of a stage fit one unit");
+};
+
+// x pairs (x_i, x_{i+4}) of one 8-k slice, in the order the unpacked codes use.
+__device__ __forceinline__ u32x4 pair_slice(const u32x4& v) {
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);   // x0, x4
+    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);   // x1, x5
+    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);   // x2, x6
+    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);   // x3, x7
+    return o;
+}
+
+template <int SH>
+__device__ __forceinline__ uint64_t shr64(uint64_t v) {
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "I"(SH), "v"(v));
+    return r;
+}
+
+// Two dwords of codes (two consecutive 8-k slices) to two B operands of bf16
+// codes 136 + q; one v_bitop3 per pair, the shifts on both dwords at once.
+__device__ __forceinline__ void unpack2(uint32_t w0, uint32_t w1, u32x4& b0, u32x4& b1) {
+    constexpr uint32_t MK = 0x000F000Fu, C = 0x43084308u;
+    const uint64_t w = (uint64_t)w0 | ((uint64_t)w1 << 32);
+    const uint64_t t1 = shr64<4>(w), t2 = shr64<8>(w), t3 = shr64<12>(w);
+    b0[0] = (w0 & MK) ^ C;
+    b0[1] = ((uint32_t)t1 & MK) ^ C;
+    b0[2] = ((uint32_t)t2 & MK) ^ C;
+    b0[3] = ((uint32_t)t3 & MK) ^ C;
+    b1[0] = (w1 & MK) ^ C;
+    b1[1] = ((uint32_t)(t1 >> 32) & MK) ^ C;
+    b1[2] = ((uint32_t)(t2 >> 32) & MK) ^ C;
+    b1[3] = ((uint32_t)(t3 >> 32) & MK) ^ C;
+}
+
+__device__ __forceinline__ float half_lo(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float half_hi(uint32_t v) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm0_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+// Wait until the loads of the stage `after` stages back have landed: L loads
+// per stage, issued in stage order, complete in order.
+template <int L, int D, int J = 0>
+__device__ __forceinline__ void wait_stages_q4(int after) {
+    if constexpr (J <= D - 2) {
+        if (after == J) {
+            wait_vm0_lgkm0<J * L>();
+            return;
+        }
+        wait_stages_q4<L, D, J + 1>(after);
+    } else {
+        wait_vm0_lgkm0<0>();
+    }
+}
+
+template <int BN, int TM, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
+    using SH = Q4Shape<BN, TM, NW>;
+    constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, FX = SH::FX, XU = SH::XU, F = SH::F,
+                  L = SH::L;
+    const int M = a.M, N = a.N, K = a.K;
+    const int S = a.splits;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int l16 = lane & 15, lg = lane >> 4;
+
+    const int m_tiles = (M + TM - 1) / TM;
+    const int n_tiles = (N + BN - 1) / BN;
+    int n_tile, m_tile, ks;
+    if (!tile_of(blockIdx.x, n_tiles, m_tiles, S, n_tile, ks, m_tile))
+        return;   // padding slot: the whole workgroup leaves together
+    const int N16 = (N + 15) >> 4;
+    const int KBn = (K + kQB - 1) / kQB;   // 128-k blocks (units per row tile)
+    const int bps = (KBn + S - 1) / S;
+    const int kb0 = ks * bps;
+    const int nkb = max(0, min(KBn, kb0 + bps) - kb0);
+
+    __shared__ u32x4 ring[D][F][64];
+
+    // Per unit this wavefront loads: the lane's source at block 0 (nullptr:
+    // the zero word), the bytes per block, and for X the k of its chunk.
+    const uint8_t* src[L];
+    int64_t step[L];
+    int kx[L];
+    const int T0 = n_tile * (BN / 16);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+        const int u = wave * L + i;
+        src[i] = nullptr;
+        step[i] = 0;
+        kx[i] = 0;
+        if (u < FW) {
+            const int T = T0 + u;
+            if (T < N16) src[i] = (const uint8_t*)a.W + ((int64_t)T * KBn) * 1024 + 16 * lane;
+            step[i] = 1024;
+        } else if (u == FW) {
+            // 16 bytes per lane: lanes 4 f .. 4 f + 3 carry the 64-byte unit of row tile f
+            const int T = T0 + (lane >> 2);
+            if (lane < 4 * FW && T < N16) src[i] = (const uint8_t*)a.S + (int64_t)T * 64 + 16 * (lane & 3);
+            step[i] = (int64_t)N16 * 64;
+        } else if (u < XU + FX) {
+            const int x = u - XU;
+            const int r = 4 * (x & 3) + (lane >> 4);   // token row within the 16-token tile
+            const int c = (lane & 15) ^ r;             // chunk stored at position lane & 15
+            int m = m_tile * TM + (x >> 2) * 16 + r;
+            m = m < M ? m : M - 1;                     // rows past M: computed, never stored
+            src[i] = (const uint8_t*)a.X + (int64_t)m * K * 2 + c * 16;
+            step[i] = kQB * 2;
+            kx[i] = 8 * c;
+        }
+    }
+    auto issue = [&](int kb, int slot) {
+#pragma unroll
+        for (int i = 0; i < L; ++i) {
+            const int u = wave * L + i;
+            const bool isx = u >= XU && u < XU + FX;
+            const void* p = &g_zero16;
+            if (src[i] && (!isx || kb * kQB + kx[i] < K)) p = src[i] + kb * step[i];
+            dma16(p, &ring[slot][u][0]);
+        }
+    };
+
+    f32x4 acc[NF][MT];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int wr = wave / SH::WC, wc = wave - (wave / SH::WC) * SH::WC;
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (d < nkb) issue(kb0 + d, d);
+
+    const u32x4 neg = {kNeg136, kNeg136, kNeg136, kNeg136};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < nkb; ++i) {
+        wait_stages_q4<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();                     // everyone's loads of stage i landed
+        asm volatile("" ::: "memory");
+        if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
+        const int slot = i % D;
+
+        u32x4 wq[NF];
+        uint32_t sc[NF];
+        const uint32_t* su = (const uint32_t*)&ring[slot][FW][0];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            wq[f] = ring[slot][wr * NF + f][lane];
+            sc[f] = su[(wr * NF + f) * 16 + l16];
+        }
+        // X operand of token tile t, k-step q: row l16, chunk 4 q + lg.
+        u32x4 ax[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const u32x4* xt = &ring[slot][XU + 4 * (wc * MT + t)][0];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ax[t][q] = pair_slice(xt[l16 * 16 + ((4 * q + lg) ^ l16)]);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {   // scale group 2 (kb0 + i) + h
+            f32x4 cor[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                cor[t] = mfma16(ax[t][2 * h], neg, zero);
+                cor[t] = mfma16(ax[t][2 * h + 1], neg, cor[t]);
+            }
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                u32x4 b0, b1;
+                unpack2(wq[f][2 * h], wq[f][2 * h + 1], b0, b1);
+                const float s = h ? half_hi(sc[f]) : half_lo(sc[f]);
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    f32x4 d = mfma16(ax[t][2 * h], b0, cor[t]);
+                    d = mfma16(ax[t][2 * h + 1], b1, d);
+                    acc[f][t] = d * s + acc[f][t];
+                }
+            }
+        }
+    }
+
+    store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,
+                                wc * SH::WM);
+}
+
+template <int BN, int TM, int D, int NW>
+bool geom_q4_ring(const Variant& v, int M, int N, int K, dim3* grid, size_t* lds) {
+    if (K < 0) return false;
+    if (TM > 16 && M <= TM / 2) return false;   // a smaller token tile fits
+    const int S = v.cfg.split;
+    const int m_tiles = (M + TM - 1) / TM;
+    const int n_tiles = (N + BN - 1) / BN;
+    const int nkb = (K + kQB - 1) / kQB;
+    if (S > 1 && nkb < 2 * S) return false;      // at least two k-blocks per split
+    if (S > 1 && m_tiles * n_tiles > kMaxTileCounters) return false;
+    *grid = dim3(tile_grid(n_tiles, m_tiles, S));
+    *lds = 0;
+    return true;
+}
+
+template <int BN, int TM, int D, int NW>
+size_t ws_q4_ring(const Variant& v, int M, int N, int K) {
+    (void)K;
+    const int S = v.cfg.split;
+    if (S <= 1) return 0;
+    const size_t tiles = (size_t)((M + TM - 1) / TM) * ((N + BN - 1) / BN);
+    return ws_counter_bytes((int)tiles) + (size_t)S * tiles * TM * BN * sizeof(float);
+}
+
+template <int BN, int TM, int D, int NW = 4>
+void add_q4(std::vector<Variant>& out, int S) {
+    static_assert(D * Q4Shape<BN, TM, NW>::F * 1024 <= 160 * 1024, "LDS ring too large");
+    Variant v{};
+    v.kind = LIN_KIND_SKINNY_Q4G64;
+    v.cfg.algo = LIN_ALGO_MFMA;
+    v.cfg.rows = BN;
+    v.cfg.unroll = D;
+    v.cfg.split = S;
+    v.cfg.stage_x = 4;   // everything through the LDS ring, X in whole lines
+    v.cfg.waves = NW == 4 ? 0 : NW;
+    v.cfg.tile_m = TM;
+    v.mt = 0;
+    v.min_m = 1;
+    v.func = (const void*)&gemm_q4_ring_kernel<BN, TM, D, NW>;
+    v.geometry = &geom_q4_ring<BN, TM, D, NW>;
+    v.workspace = &ws_q4_ring<BN, TM, D, NW>;
+    v.block = 64 * NW;
+    out.push_back(v);
+}
+
+// Tiled codes: one thread per lane of a unit (16 bytes).
+__global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t* __restrict__ Wq,
+                                                         uint8_t* __restrict__ Wt, int N, int K) {
+    const int KBn = (K + kQB - 1) / kQB;
+    const int64_t units = (int64_t)((N + 15) >> 4) * KBn;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= units * 64) return;
+    const int l = (int)(i & 63);
+    const int64_t unit = i >> 6;
+    const int64_t T = unit / KBn;
+    const int j = (int)(unit - T * KBn);
+    const int64_t n = T * 16 + (l & 15);
+    const int rowb = K / 2;   // bytes per plain row (a multiple of 32)
+    u32x4 v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int off = 64 * j + 16 * t + 4 * (l >> 4);
+        v[t] = (n < N && off < rowb) ? *(const uint32_t*)(Wq + n * rowb + off) : 0u;
+    }
+    *(u32x4*)(Wt + i * 16) = v;
+}
+
+// Tiled scales: one thread per (block, row tile, row) = one dword (two fp16).
+__global__ __launch_bounds__(256) void tile_scales_kernel(const uint16_t* __restrict__ S,
+                                                          uint32_t* __restrict__ St, int N, int K) {
+    const int KBn = (K + kQB - 1) / kQB;
+    const int N16 = (N + 15) >> 4;
+    const int G = K / 64;
+    const int64_t total = (int64_t)KBn * N16 * 16;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    const int r = (int)(i & 15);
+    const int64_t unit = i >> 4;   // j * N16 + T
+    const int j = (int)(unit / N16);
+    const int64_t T = unit - (int64_t)j * N16;
+    const int64_t n = T * 16 + r;
+    uint32_t lo = 0, hi = 0;
+    if (n < N) {
+        if (2 * j < G) lo = S[n * G + 2 * j];
+        if (2 * j + 1 < G) hi = S[n * G + 2 * j + 1];
+    }
+    St[i] = lo | (hi << 16);
+}
+
+}  // namespace
+
+void q4g64_tiled_bytes(int64_t N, int64_t K, int64_t* wt, int64_t* st) {
+    const int64_t n16 = (N + 15) / 16, kb = (K + kQB - 1) / kQB;
+    *wt = n16 * kb * 1024;
+    *st = n16 * kb * 64;
+}
+
+hipError_t launch_tile_q4g64(const void* Wq, const void* S, void* Wt, void* St, int N, int K,
+                             hipStream_t stream) {
+    const int64_t n16 = (N + 15) / 16, kb = (K + kQB - 1) / kQB;
+    const int64_t code_threads = n16 * kb * 64;
+    const int64_t scale_threads = n16 * kb * 16;
+    if (code_threads > 0) {
+        hipLaunchKernelGGL(tile_codes_kernel, dim3((unsigned)((code_threads + 255) / 256)), dim3(256),
+                           0, stream, (const uint8_t*)Wq, (uint8_t*)Wt, N, K);
+        hipLaunchKernelGGL(tile_scales_kernel, dim3((unsigned)((scale_threads + 255) / 256)),
+                           dim3(256), 0, stream, (const uint16_t*)S, (uint32_t*)St, N, K);
+    }
+    return hipGetLastError();
+}
+
+void register_gemm_q4_ring(std::vector<Variant>& out) {
+    for (int S : {1, 2, 4, 8}) {
+        add_q4<64, 16, 6>(out, S);
+        add_q4<128, 16, 6>(out, S);
+        add_q4<256, 16, 4>(out, S);
+        add_q4<64, 32, 6>(out, S);
+        add_q4<128, 32, 4>(out, S);
+        add_q4<64, 64, 4>(out, S);
+        add_q4<128, 64, 4>(out, S);
+        add_q4<128, 64, 3>(out, S);
+        add_q4<64, 128, 3>(out, S);
+        add_q4<128, 128, 3>(out, S);
+        add_q4<128, 128, 2>(out, S);
+        add_q4<64, 256, 2>(out, S);
+    }
+}
+
+}  // namespace lin

@@ -24,6 +24,7 @@ const std::vector<Variant>& registry() {
         register_gemv_q4g64(*r);
         register_gemm_mfma(*r);
         register_gemm_mfma_ring(*r);
+        register_gemm_q4_ring(*r);
         return r;
     }();
     return *reg;
@@ -53,7 +54,7 @@ bool applicable(const Variant& v, int kind, int64_t M, int64_t N, int64_t K) {
     if (v.cfg.algo == LIN_ALGO_VALU) {
         if (v.mt != pow2ceil(M)) return false;
     } else {
-        if (M < v.min_m || K == 0) return false;
+        if (M < v.min_m || (K == 0 && kind != LIN_KIND_SKINNY_Q4G64)) return false;
     }
     dim3 g;
     size_t lds;
@@ -82,6 +83,17 @@ int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
     want.algo = LIN_ALGO_VALU;
     want.tile_m = pow2ceil(M);
     const int mt = want.tile_m;
+    if (kind == LIN_KIND_SKINNY_Q4G64) {
+        // matrix cores without split-K: the token tile that covers M best
+        const int tm = mt <= 16 ? 16 : (mt <= 32 ? 32 : (mt <= 64 ? 64 : 128));
+        for (int i : candidates(kind, M, N, K)) {
+            const Variant& v = registry()[i];
+            if (v.cfg.split == 1 && v.cfg.tile_m == tm && v.cfg.rows == 128) return i;
+        }
+        for (int i : candidates(kind, M, N, K))
+            if (workspace_need(registry()[i], M, N, K) == 0) return i;
+        return -1;
+    }
     if (kind == LIN_KIND_GEMV_Q4G64) {
         want.rows = mt <= 1 ? 4 : (mt <= 4 ? 2 : 1);
         want.unroll = 1;
@@ -233,16 +245,20 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 int check(int kind, const void* W, const void* S, const void* x, const float* y, int64_t M,
           int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return LIN_ERR_SHAPE;
-    const int64_t maxm = kind == LIN_KIND_SKINNY_BF16 ? LIN_SKINNY_MAX_M : LIN_GEMV_MAX_M;
+    const bool q4 = kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64;
+    const int64_t maxm = (kind == LIN_KIND_SKINNY_BF16 || kind == LIN_KIND_SKINNY_Q4G64)
+                             ? LIN_SKINNY_MAX_M
+                             : LIN_GEMV_MAX_M;
     if (M > maxm || N > 0x7FFFFFFF || K > LIN_MAX_K) return LIN_ERR_SHAPE;
-    if (kind == LIN_KIND_GEMV_Q4G64 ? (K % 64) : (K % 8)) return LIN_ERR_SHAPE;
+    if (q4 ? (K % 64) : (K % 8)) return LIN_ERR_SHAPE;
     if (M == 0 || N == 0) return 1;
     if (!y) return LIN_ERR_NULL;
-    if (K > 0 && (!W || !x || (kind == LIN_KIND_GEMV_Q4G64 && !S))) return LIN_ERR_NULL;
+    if (K > 0 && (!W || !x || (q4 && !S))) return LIN_ERR_NULL;
     if (!aligned(y, 4)) return LIN_ERR_ALIGN;
     if (K > 0) {
         if (!aligned(W, 16) || !aligned(x, 16)) return LIN_ERR_ALIGN;
         if (kind == LIN_KIND_GEMV_Q4G64 && !aligned(S, 2)) return LIN_ERR_ALIGN;
+        if (kind == LIN_KIND_SKINNY_Q4G64 && !aligned(S, 16)) return LIN_ERR_ALIGN;
     }
     return LIN_OK;
 }
@@ -303,8 +319,31 @@ int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y, int64_t M, int6
     return run(LIN_KIND_SKINNY_BF16, W, nullptr, X, Y, M, N, K, stream);
 }
 
+int lin_gemm_skinny_q4g64(const void* Wt, const void* St, const void* X, float* Y, int64_t M,
+                          int64_t N, int64_t K, void* stream) {
+    return run(LIN_KIND_SKINNY_Q4G64, Wt, St, X, Y, M, N, K, stream);
+}
+
+int lin_q4g64_tiled_size(int64_t N, int64_t K, int64_t* wt_bytes, int64_t* st_bytes) {
+    if (N < 0 || K < 0 || N > 0x7FFFFFFF || K > LIN_MAX_K || K % 64) return LIN_ERR_SHAPE;
+    if (!wt_bytes || !st_bytes) return LIN_ERR_NULL;
+    q4g64_tiled_bytes(N, K, wt_bytes, st_bytes);
+    return LIN_OK;
+}
+
+int lin_q4g64_tile(const void* Wq, const void* S, void* Wt, void* St, int64_t N, int64_t K,
+                   void* stream) {
+    if (N < 0 || K < 0 || N > 0x7FFFFFFF || K > LIN_MAX_K || K % 64) return LIN_ERR_SHAPE;
+    if (N == 0 || K == 0) return LIN_OK;
+    if (!Wq || !S || !Wt || !St) return LIN_ERR_NULL;
+    if (!aligned(Wq, 16) || !aligned(S, 2) || !aligned(Wt, 16) || !aligned(St, 16))
+        return LIN_ERR_ALIGN;
+    hipError_t e = launch_tile_q4g64(Wq, S, Wt, St, (int)N, (int)K, (hipStream_t)stream);
+    return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
+}
+
 int lin_num_candidates(int kind, int64_t M, int64_t N, int64_t K) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_BF16) return LIN_ERR_ARG;
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_Q4G64) return LIN_ERR_ARG;
     int st = check(kind, (void*)16, (void*)16, (void*)16, (float*)16, M, N, K);
     if (st < 0) return st;
     if (st > 0) return 0;
@@ -404,7 +443,7 @@ int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, v
 
 int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y, int64_t M,
                  int64_t N, int64_t K, void* stream, lin_config* out) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_BF16) return LIN_ERR_ARG;
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_Q4G64) return LIN_ERR_ARG;
     int st = check(kind, W, S, x, y, M, N, K);
     if (st < 0) return st;
     if (st > 0) return LIN_OK;
@@ -489,9 +528,10 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
 int lin_autotune_set(int kind, const void* const* W, const void* const* S, int count,
                      const void* x, float* y, int64_t M, int64_t N, int64_t K, void* stream,
                      lin_config* out) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_BF16) return LIN_ERR_ARG;
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_Q4G64) return LIN_ERR_ARG;
     if (count < 1) return LIN_ERR_ARG;
-    if (!W || (kind == LIN_KIND_GEMV_Q4G64 && !S)) return LIN_ERR_NULL;
+    if (!W || ((kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64) && !S))
+        return LIN_ERR_NULL;
     for (int j = 0; j < count; ++j) {
         const int st = check(kind, W[j], S ? S[j] : nullptr, x, y, M, N, K);
         if (st < 0) return st;

@@ -31,9 +31,15 @@ void register_gemv_bf16(std::vector<Variant>& out);
 void register_gemv_q4g64(std::vector<Variant>& out);
 void register_gemm_mfma(std::vector<Variant>& out);
 void register_gemm_mfma_ring(std::vector<Variant>& out);
+void register_gemm_q4_ring(std::vector<Variant>& out);
 
 // Quantiser launch (int4-g64 weight preparation).
 hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream);
+
+// Matrix-core tiled int4-g64 layout: sizes and the rearrangement launch.
+void q4g64_tiled_bytes(int64_t N, int64_t K, int64_t* wt, int64_t* st);
+hipError_t launch_tile_q4g64(const void* Wq, const void* S, void* Wt, void* St, int N, int K,
+                             hipStream_t stream);
 
 // Cache sweep used while tuning: reads n 16-byte words.
 hipError_t launch_flush(void* buf, size_t n16, uint32_t salt, hipStream_t stream);

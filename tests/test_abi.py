@@ -47,23 +47,29 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_bf16", (P, P, P, 1, 8, (1 << 22) + 8, None), L.LIN_ERR_SHAPE),
     ("lin_gemv_q4g64", (P, P, P, P, 1, 8, 96, None), L.LIN_ERR_SHAPE),
     ("lin_gemm_skinny_bf16", (P, P, P, 257, 8, 8, None), L.LIN_ERR_SHAPE),
+    ("lin_gemm_skinny_q4g64", (P, P, P, P, 257, 8, 64, None), L.LIN_ERR_SHAPE),
+    ("lin_gemm_skinny_q4g64", (P, P, P, P, 4, 8, 96, None), L.LIN_ERR_SHAPE),
     # empty calls succeed without pointers
     ("lin_gemv_bf16", (None, None, None, 0, 8, 8, None), L.LIN_OK),
     ("lin_gemv_bf16", (None, None, None, 1, 0, 8, None), L.LIN_OK),
     ("lin_gemv_q4g64", (None, None, None, None, 0, 0, 64, None), L.LIN_OK),
     ("lin_gemm_skinny_bf16", (None, None, None, 0, 0, 0, None), L.LIN_OK),
+    ("lin_gemm_skinny_q4g64", (None, None, None, None, 0, 8, 64, None), L.LIN_OK),
     # null pointers
     ("lin_gemv_bf16", (P, P, None, 1, 8, 8, None), L.LIN_ERR_NULL),
     ("lin_gemv_bf16", (None, P, P, 1, 8, 8, None), L.LIN_ERR_NULL),
     ("lin_gemv_bf16", (P, None, P, 1, 8, 8, None), L.LIN_ERR_NULL),
     ("lin_gemv_q4g64", (P, None, P, P, 1, 8, 64, None), L.LIN_ERR_NULL),
     ("lin_gemm_skinny_bf16", (P, P, None, 4, 8, 8, None), L.LIN_ERR_NULL),
+    ("lin_gemm_skinny_q4g64", (P, None, P, P, 4, 8, 64, None), L.LIN_ERR_NULL),
     # alignment
     ("lin_gemv_bf16", (P + 8, P, P, 1, 8, 8, None), L.LIN_ERR_ALIGN),
     ("lin_gemv_bf16", (P, P + 2, P, 1, 8, 8, None), L.LIN_ERR_ALIGN),
     ("lin_gemv_bf16", (P, P, P + 2, 1, 8, 8, None), L.LIN_ERR_ALIGN),
     ("lin_gemv_q4g64", (P, P + 1, P, P, 1, 8, 64, None), L.LIN_ERR_ALIGN),
     ("lin_gemm_skinny_bf16", (P + 4, P, P, 4, 8, 8, None), L.LIN_ERR_ALIGN),
+    ("lin_gemm_skinny_q4g64", (P, P + 2, P, P, 4, 8, 64, None), L.LIN_ERR_ALIGN),
+    ("lin_gemm_skinny_q4g64", (P + 8, P, P, P, 4, 8, 64, None), L.LIN_ERR_ALIGN),
 ])
 def test_argument_validation(fn, args, expect):
     assert getattr(L._lib, fn)(*args) == expect
@@ -77,6 +83,25 @@ def test_quantizer_validation():
     assert q(None, P, P, 4, 64, None) == L.LIN_ERR_NULL
     assert q(P + 8, P, P, 4, 64, None) == L.LIN_ERR_ALIGN
     assert q(P, P, P + 1, 4, 64, None) == L.LIN_ERR_ALIGN
+
+
+def test_tile_validation_and_sizes():
+    t = L._lib.lin_q4g64_tile
+    assert t(P, P, P, P, 4, 96, None) == L.LIN_ERR_SHAPE
+    assert t(P, P, P, P, -1, 64, None) == L.LIN_ERR_SHAPE
+    assert t(None, None, None, None, 0, 64, None) == L.LIN_OK
+    assert t(None, None, None, None, 4, 0, None) == L.LIN_OK
+    assert t(P, P, None, P, 4, 64, None) == L.LIN_ERR_NULL
+    assert t(P, P, P, P + 8, 4, 64, None) == L.LIN_ERR_ALIGN
+    assert t(P, P + 1, P, P, 4, 64, None) == L.LIN_ERR_ALIGN
+    # ceil(N/16) * ceil(K/128) units of 1024 and 64 bytes
+    assert L.lin_q4g64_tiled_size(1, 64) == (1024, 64)
+    assert L.lin_q4g64_tiled_size(16, 128) == (1024, 64)
+    assert L.lin_q4g64_tiled_size(17, 192) == (4 * 1024, 4 * 64)
+    assert L.lin_q4g64_tiled_size(14336, 4096) == (896 * 32 * 1024, 896 * 32 * 64)
+    assert L.lin_q4g64_tiled_size(0, 0) == (0, 0)
+    with pytest.raises(L.LinError):
+        L.lin_q4g64_tiled_size(8, 100)
 
 
 def test_stream_read_validation():
@@ -116,7 +141,8 @@ def test_autotune_set_validation():
 
 def test_candidate_enumeration():
     for kind, M, N, K in [(0, 1, 2048, 2048), (0, 8, 512, 3584), (1, 1, 2048, 2048),
-                          (1, 3, 512, 18944), (2, 8, 4096, 4096), (2, 17, 1024, 4096)]:
+                          (1, 3, 512, 18944), (2, 8, 4096, 4096), (2, 17, 1024, 4096),
+                          (3, 1, 4096, 4096), (3, 64, 14336, 4096), (3, 256, 300, 4160)]:
         n = L.lin_num_candidates(kind, M, N, K)
         assert n > 0
         cands = L.lin_candidates(kind, M, N, K)
@@ -145,3 +171,11 @@ def test_default_skinny_config_needs_no_workspace():
             c = L.lin_get_config(L.LIN_KIND_SKINNY_BF16, M, N, K)
             if c["algo"] == L.LIN_ALGO_MFMA:
                 assert c["split"] == 1 and c["stage_x"] == 4 and c["waves"] == 0, (M, N, K, c)
+
+
+def test_default_q4_skinny_config_needs_no_workspace():
+    for M in (1, 8, 16, 17, 32, 33, 64, 100, 128, 200, 256):
+        for N, K in ((1024, 4096), (14336, 4096), (4096, 14336), (300, 4160)):
+            c = L.lin_get_config(L.LIN_KIND_SKINNY_Q4G64, M, N, K)
+            assert c["algo"] == L.LIN_ALGO_MFMA and c["split"] == 1, (M, N, K, c)
+            assert c["tile_m"] >= min(M, 128) or c["tile_m"] == 16, (M, N, K, c)

@@ -281,13 +281,15 @@ MFMA_PEAK_TFS = 2500.0   # MI355X dense bf16 matrix-core peak
 
 
 class SkinnyCase:
-    """One batched-token product Y = X . W^T of a Mistral-7B-shaped matrix."""
+    """One batched-token product Y = X . W^T of a Mistral-7B-shaped matrix, bf16
+    weights or int4-g64 weights in the tiled layout."""
 
-    def __init__(self, M, N, K):
-        self.M, self.N, self.K = M, N, K
-        self.bytes = bytes_bf16(N, K, M)
+    def __init__(self, M, N, K, fmt="bf16"):
+        self.M, self.N, self.K, self.fmt = M, N, K, fmt
+        self.bytes = bytes_bf16(N, K, M) if fmt == "bf16" else bytes_q4(N, K, M)
         self.flop = 2 * M * N * K
-        self.key = (L.LIN_KIND_SKINNY_BF16, M, N, K)
+        self.kind = L.LIN_KIND_SKINNY_BF16 if fmt == "bf16" else L.LIN_KIND_SKINNY_Q4G64
+        self.key = (self.kind, M, N, K)
 
     @property
     def name(self):
@@ -295,7 +297,7 @@ class SkinnyCase:
 
 
 def skinny_variant(c):
-    cfg = L.lin_get_config(L.LIN_KIND_SKINNY_BF16, c.M, c.N, c.K)
+    cfg = L.lin_get_config(*c.key)
     if cfg["algo"] == L.LIN_ALGO_MFMA:
         return "mfma rows%d tm%d D%d S%d X%d%s" % (cfg["rows"], cfg["tile_m"], cfg["unroll"],
                                                   cfg["split"], cfg["stage_x"],
@@ -304,19 +306,36 @@ def skinny_variant(c):
                                          cfg["stage_x"], cfg["tile_m"])
 
 
-def run_skinny(args, dev):
+def skinny_weights(N, K, fmt, copies, dev):
+    """Distinct seeded weight copies of one shape: bf16 tensors, or int4-g64
+    (quantised on the GPU) rearranged into the tiled layout at load."""
+    out = []
+    for i in range(copies):
+        W = synth.weight(synth.MISTRAL_SEED, 0, N + i, N, K, device=dev)
+        if fmt == "bf16":
+            out.append(W)
+        else:
+            Wq, S = L.lin_quantize_q4g64(W)
+            out.append(L.lin_q4g64_tile(Wq, S))
+            del Wq, S, W
+    torch.cuda.synchronize()
+    return out
+
+
+def run_skinny(args, dev, fmt):
     """Every (shape, M) product of the batched-decode workload: per case, a graph
     of back-to-back launches cycling over enough distinct weight copies to
     exceed the 256 MB last-level cache (so each launch streams W from HBM);
     the step is one launch of every case."""
-    cases = [SkinnyCase(M, N, K) for M in synth.MISTRAL_M for N, K in synth.MISTRAL_SHAPES]
-    tfile = args.tuning or os.path.join(L.TUNING_DIR, "mistral-7b-skinny.json")
+    cases = [SkinnyCase(M, N, K, fmt) for M in synth.MISTRAL_M for N, K in synth.MISTRAL_SHAPES]
+    tname = "mistral-7b-skinny.json" if fmt == "bf16" else "mistral-7b-skinny-q4.json"
+    tfile = args.tuning or os.path.join(L.TUNING_DIR, tname)
     ok, stale = L.load_tuning(tfile) if (os.path.exists(tfile) and not args.tune) else ([], [])
     weights = {}
     for N, K in synth.MISTRAL_SHAPES:
-        copies = max(2, -(-(600 << 20) // (2 * N * K)))
-        weights[(N, K)] = [synth.weight(synth.MISTRAL_SEED, 0, N + i, N, K, device=dev)
-                           for i in range(copies)]
+        wbytes = 2 * N * K if fmt == "bf16" else bytes_q4(N, K, 0)
+        copies = max(2, -(-(600 << 20) // wbytes))
+        weights[(N, K)] = skinny_weights(N, K, fmt, copies, dev)
     X = {(M, K): synth.activation(synth.MISTRAL_SEED, 0, 0, M, K, device=dev)
          for M in synth.MISTRAL_M for K in {k for _, k in synth.MISTRAL_SHAPES}}
     Y = {c.key: torch.empty((c.M, c.N), dtype=torch.float32, device=dev) for c in cases}
@@ -324,8 +343,7 @@ def run_skinny(args, dev):
     for c in cases:
         if c.key in ok:
             continue
-        cfg = L.lin_autotune_set(L.LIN_KIND_SKINNY_BF16, weights[(c.N, c.K)], X[(c.M, c.K)],
-                                 Y[c.key])
+        cfg = L.lin_autotune_set(c.kind, weights[(c.N, c.K)], X[(c.M, c.K)], Y[c.key])
         tuned[c.key] = cfg
         log("tuned skinny %-16s -> %s" % (c.name, cfg))
     if tuned:
@@ -350,7 +368,8 @@ def run_skinny(args, dev):
 
     def call(c, i):
         Wc = weights[(c.N, c.K)]
-        return lambda: L.lin_gemm_skinny_bf16(Wc[i % len(Wc)], X[(c.M, c.K)], Y[c.key])
+        fn = L.lin_gemm_skinny_bf16 if fmt == "bf16" else L.lin_gemm_skinny_q4g64
+        return lambda: fn(Wc[i % len(Wc)], X[(c.M, c.K)], Y[c.key])
 
     reps = max(5, args.steps // 2)
     per_case = {}
@@ -387,16 +406,20 @@ def run_skinny(args, dev):
     out = {"metric": METRIC, "value": round(step_bytes / wall / 1e9, 1), "unit": "GB/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16 weights and tokens, fp32 accumulate",
+           "vs_baseline": None,
+           "dtype": ("bf16 weights and tokens, fp32 accumulate" if fmt == "bf16" else
+                     "int4-g64 weights (tiled at load), bf16 tokens, bf16 matrix-core products, "
+                     "fp32 accumulate and scales"),
            "data": "synthetic",
-           "config": {"workload": "mistral-7b-shaped batched-decode products, M in %s tokens x %d "
-                      "shapes, one launch each per step" % (list(synth.MISTRAL_M),
+           "config": {"workload": "mistral-7b-shaped batched-decode products%s, M in %s tokens x %d "
+                      "shapes, one launch each per step" % ("" if fmt == "bf16" else ", int4-g64",
+                                                          list(synth.MISTRAL_M),
                                                           len(synth.MISTRAL_SHAPES)),
                       "bytes_per_step": step_bytes, "tuning": tuning},
            "pct_of_hbm_peak": round(100.0 * step_bytes / wall / 1e9 / HBM_PEAK_GBS, 2),
            "gpu_ms_per_step": round(gpu * 1e3, 4), "cases": per_case, "roofline": roofline}
     if not args.skip_cpu:
-        out["cpu_baseline"] = cpu_baseline_skinny(min(16, os.cpu_count() or 1))
+        out["cpu_baseline"] = cpu_baseline_skinny(min(16, os.cpu_count() or 1), fmt)
     print(json.dumps(out), flush=True)
 
 
@@ -440,7 +463,7 @@ def cpu_baseline(model, layers, threads):
                       % (model["name"], layers - 1, len(work) // 2, total_bytes / 1e6, dt)}
 
 
-def cpu_baseline_skinny(threads, rows=96):
+def cpu_baseline_skinny(threads, fmt="bf16", rows=96):
     """The oracle on a bounded sample of the batched workload: the first `rows`
     rows of every shape against all M tokens, for every M."""
     import oracle
@@ -449,12 +472,17 @@ def cpu_baseline_skinny(threads, rows=96):
         for N, K in synth.MISTRAL_SHAPES:
             W = synth.bits(synth.weight(synth.MISTRAL_SEED, 0, N, N, K)[:rows])
             Xb = synth.bits(synth.activation(synth.MISTRAL_SEED, 0, 0, M, K))
-            work.append((W, Xb, bytes_bf16(rows, K, M)))
+            if fmt == "bf16":
+                work.append(((W,), Xb, bytes_bf16(rows, K, M)))
+            else:
+                work.append((oracle.quantize_q4g64(W), Xb, bytes_q4(rows, K, M)))
     total = sum(w[2] for w in work)
-    jobs = [(W[lo:lo + 8], Xb) for W, Xb, _ in work for lo in range(0, W.shape[0], 8)]
+    jobs = [(tuple(a[lo:lo + 8] for a in Ws), Xb) for Ws, Xb, _ in work
+            for lo in range(0, rows, 8)]
+    fn = oracle.gemm_dense if fmt == "bf16" else oracle.gemm_q4g64
     t0 = time.perf_counter()
     with concurrent.futures.ThreadPoolExecutor(threads) as ex:
-        list(ex.map(lambda j: oracle.gemm_dense(*j), jobs))
+        list(ex.map(lambda j: fn(*j[0], j[1]), jobs))
     dt = time.perf_counter() - t0
     return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
@@ -469,7 +497,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="tinyllama", choices=["tinyllama", "qwen7b", "mistral-skinny"])
+    ap.add_argument("--workload", default="tinyllama",
+                    choices=["tinyllama", "qwen7b", "mistral-skinny", "mistral-skinny-q4"])
     ap.add_argument("--tune", action="store_true",
                     help="re-run lin_autotune for every shape and rewrite the tuning table")
     ap.add_argument("--tuning", default=None, help="tuning table path")
@@ -497,8 +526,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "copies": 3}), flush=True)
         return
-    if args.workload == "mistral-skinny":
-        run_skinny(args, dev)
+    if args.workload in ("mistral-skinny", "mistral-skinny-q4"):
+        run_skinny(args, dev, "bf16" if args.workload == "mistral-skinny" else "q4")
         return
     model = synth.TINYLLAMA if args.workload == "tinyllama" else synth.QWEN7B
     log("building %s weight sets on %s" % (model["name"], torch.cuda.get_device_name(dev)))

@@ -145,9 +145,11 @@ int lin_q4g64_tiled_size(int64_t N, int64_t K, int64_t* wt_bytes, int64_t* st_by
  * caller-owned Wt and St (16-byte aligned, sizes from lin_q4g64_tiled_size).
  * With N16 = ceil(N/16) and KB = ceil(K/128):
  *   Wt: N16 x KB units of 1024 bytes, unit (T, j) at byte (T * KB + j) * 1024;
- *       its byte 16 l + 4 t + b (lane l < 64, t < 4, b < 4) is byte
- *       64 j + 16 t + 4 (l / 16) + b of Wq row 16 T + (l mod 16), i.e. the
- *       codes of k = 128 j + 32 t + 8 (l / 16) + 2 b and + 1;
+ *       its dword 4 l + t (lane l < 64, t < 4) holds the 8 codes of Wq row
+ *       16 T + (l mod 16) at k = k0 + e, e < 8, k0 = 128 j + 32 t + 8 (l / 16)
+ *       (Wq bytes 64 j + 16 t + 4 (l / 16) .. + 3), reordered: the code of
+ *       k0 + 2 i in bits 4 i .. 4 i + 3 and that of k0 + 2 i + 1 in bits
+ *       16 + 4 i .. 19 + 4 i (i < 4);
  *   St: KB x N16 units of 64 bytes, unit (j, T) at byte (j * N16 + T) * 64;
  *       its fp16 element 2 r + h (r < 16, h < 2) is S[16 T + r][2 j + h].
  * Entries past row N - 1 or past k = K - 1 are zero.  Enqueued on `stream`;

@@ -11,11 +11,12 @@
 //    unit holds the codes of 16 rows x 128 k in operand order: lane l's 16
 //    bytes are the four 8-code k-slices it feeds to the four 16x16x32 products
 //    of that block (row l mod 16; k-step t covers 32 consecutive k inside one
-//    scale group).  Scales are rearranged so that one 64-byte unit holds the
-//    two groups of a 128-k block for 16 rows.
+//    scale group).  Inside a dword the codes of k0 + 2i and k0 + 2i + 1 sit at
+//    bits 4i and 16 + 4i.  Scales are rearranged so that one 64-byte unit
+//    holds the two groups of a 128-k block for 16 rows.
 //  - Unpacking.  As in the GEMV: ((w >> 4i) & 0x000F000F) ^ 0x43084308 turns a
-//    dword of codes into bf16 pairs 136 + q (exact), pairing nibble i with
-//    nibble i + 4; X is re-paired to match with four v_perm per operand.
+//    dword of codes into bf16 pairs 136 + q (exact); with the nibble order of
+//    the tiles the pairs come out in natural k order, so X is used as loaded.
 //  - The offset and the scales.  The products of one scale group start from
 //    C = -136 * sum(x) over the group, itself a matrix-core product of the X
 //    operands with a constant operand of -136 (exact products, fp32 sums), so
@@ -41,6 +42,7 @@ constexpr int kQB = 128;   // k per ring stage and per tiled unit
 // bf16 pairs (-136, -136): the constant operand of the offset products.
 constexpr uint32_t kNeg136 = 0xC308C308u;
 
+// Wave tile of a workgroup tile: NW wavefronts as WR x WC (as the bf16 ring).
 template <int BN, int TM, int NW>
 struct Q4Shape {
     static constexpr int WR = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4));
@@ -55,16 +57,6 @@ struct Q4Shape {
     static_assert(NF >= 1 && MT >= 1 && WN % 16 == 0 && WM % 16 == 0, "tile shape");
     static_assert(FW * 64 <= 1024, "the scales of a stage fit one unit");
 };
-
-// x pairs (x_i, x_{i+4}) of one 8-k slice, in the order the unpacked codes use.
-__device__ __forceinline__ u32x4 pair_slice(const u32x4& v) {
-    u32x4 o;
-    o[0] = __builtin_amdgcn_perm(v[2], v[0], 0x05040100u);   // x0, x4
-    o[1] = __builtin_amdgcn_perm(v[2], v[0], 0x07060302u);   // x1, x5
-    o[2] = __builtin_amdgcn_perm(v[3], v[1], 0x05040100u);   // x2, x6
-    o[3] = __builtin_amdgcn_perm(v[3], v[1], 0x07060302u);   // x3, x7
-    return o;
-}
 
 template <int SH>
 __device__ __forceinline__ uint64_t shr64(uint64_t v) {
@@ -218,7 +210,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
         for (int t = 0; t < MT; ++t) {
             const u32x4* xt = &ring[slot][XU + 4 * (wc * MT + t)][0];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) ax[t][q] = pair_slice(xt[l16 * 16 + ((4 * q + lg) ^ l16)]);
+            for (int q = 0; q < 4; ++q) ax[t][q] = xt[l16 * 16 + ((4 * q + lg) ^ l16)];
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {   // scale group 2 (kb0 + i) + h
@@ -309,7 +301,12 @@ __global__ __launch_bounds__(256) void tile_codes_kernel(const uint8_t* __restri
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int off = 64 * j + 16 * t + 4 * (l >> 4);
-        v[t] = (n < N && off < rowb) ? *(const uint32_t*)(Wq + n * rowb + off) : 0u;
+        const uint32_t w = (n < N && off < rowb) ? *(const uint32_t*)(Wq + n * rowb + off) : 0u;
+        // plain nibble e (k0 + e) at bits 4e -> even k at 4 (e / 2), odd at 16 + 4 (e / 2)
+        uint32_t o = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o |= ((w >> (4 * e)) & 0xFu) << ((e & 1) * 16 + 4 * (e >> 1));
+        v[t] = o;
     }
     *(u32x4*)(Wt + i * 16) = v;
 }
@@ -372,6 +369,14 @@ void register_gemm_q4_ring(std::vector<Variant>& out) {
         add_q4<128, 128, 3>(out, S);
         add_q4<128, 128, 2>(out, S);
         add_q4<64, 256, 2>(out, S);
+        // eight wavefronts, two per SIMD: one multiplies while the other unpacks
+        add_q4<128, 16, 6, 8>(out, S);
+        add_q4<128, 64, 4, 8>(out, S);
+        add_q4<256, 64, 3, 8>(out, S);
+        add_q4<128, 128, 3, 8>(out, S);
+        add_q4<128, 128, 2, 8>(out, S);
+        add_q4<256, 128, 2, 8>(out, S);
+        add_q4<64, 256, 2, 8>(out, S);
     }
 }
 

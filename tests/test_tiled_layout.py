@@ -1,38 +1,42 @@
 """The numpy statement of the tiled int4-g64 layout (tests/tiled_layout.py)
-checked on the CPU against properties its definition fixes: every plain byte
-appears exactly once, padding is zero, and each 8-code slice a lane feeds one
-matrix-core step lies inside one 64-k scale group."""
+checked on the CPU against properties its definition fixes: every code lands
+in one slot and reads back, padding is zero, the nibble order unpacks into
+natural k pairs, and each 8-code slice a lane feeds one matrix-core step lies
+inside one 64-k scale group."""
 import numpy as np
 
-from tiled_layout import tile_codes, tile_scales, tiled_sizes
+from tiled_layout import codes_of, tile_codes, tile_scales, tiled_sizes, untile_codes
 
 
-def _unique_plain(N, K, seed):
-    # bytes that identify their own position: a permutation check by value
-    rng = np.random.default_rng(seed)
-    idx = rng.permutation(N * (K // 2)).reshape(N, K // 2)
-    return idx
-
-
-def test_codes_are_a_permutation_with_zero_padding():
+def test_codes_round_trip_with_zero_padding():
+    """Every code of Wq lands in exactly one slot and reads back unchanged;
+    every slot past row N - 1 or k = K - 1 holds zero bits."""
+    rng = np.random.default_rng(3)
     for N, K in [(1, 64), (16, 128), (17, 192), (33, 640), (40, 256)]:
-        ids = _unique_plain(N, K, N + K)
-        # move positions instead of bytes: tile three byte-planes of the index
-        planes = [((ids >> (8 * p)) & 0xFF).astype(np.uint8) for p in range(3)]
-        tiled = [tile_codes(pl, N, K).astype(np.int64) for pl in planes]
-        pos = tiled[0] | (tiled[1] << 8) | (tiled[2] << 16)
-        wt, _ = tiled_sizes(N, K)
-        assert pos.size == wt
-        # every valid byte appears once; padding bytes (position 0 aside) read 0
-        valid = np.zeros(wt, dtype=bool)
-        n16, kb = -(-N // 16), -(-K // 128)
-        T, j, l, t, b = np.unravel_index(np.arange(wt), (n16, kb, 64, 4, 4))
-        row = 16 * T + l % 16
-        col = 64 * j + 16 * t + 4 * (l // 16) + b
-        valid = (row < N) & (col < K // 2)
-        assert np.array_equal(np.sort(pos[valid]), np.arange(N * (K // 2)))
-        assert np.all(pos[~valid] == 0)
-        assert np.array_equal(pos[valid], ids[row[valid], col[valid]])
+        Wq = rng.integers(0, 256, (N, K // 2)).astype(np.uint8)
+        Wt = tile_codes(Wq, N, K)
+        assert Wt.size == tiled_sizes(N, K)[0]
+        back, w, pad_dword, pad_bit = untile_codes(Wt, N, K)
+        assert np.array_equal(back, codes_of(Wq))
+        assert np.all(((w[pad_dword] >> pad_bit.astype(np.uint32)) & 0xF) == 0)
+
+
+def test_nibble_order_gives_natural_pairs():
+    """((w >> 4 i) & 0x000F000F) of a tiled dword holds the codes of k0 + 2 i
+    (low half) and k0 + 2 i + 1 (high half)."""
+    N, K = 16, 128
+    Wq = np.zeros((N, K // 2), dtype=np.uint8)
+    codes = (np.arange(K) % 16).astype(np.uint8)   # code of k is k mod 16 in row 0
+    Wq[0] = codes[0::2] | (codes[1::2] << 4)
+    w = tile_codes(Wq, N, K).view(np.uint32)
+    for lane in (0, 16, 32, 48):
+        for t in range(4):
+            k0 = 32 * t + 8 * (lane // 16)
+            d = int(w[lane * 4 + t])
+            for i in range(4):
+                v = (d >> (4 * i)) & 0x000F000F
+                assert v & 0xF == (k0 + 2 * i) % 16
+                assert v >> 16 == (k0 + 2 * i + 1) % 16
 
 
 def test_each_matrix_core_step_stays_in_one_group():

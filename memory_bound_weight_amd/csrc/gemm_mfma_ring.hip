@@ -28,7 +28,9 @@
 // s_barrier (their loads have landed too, and everyone has finished reading
 // stage i - 1), refills the slot of stage i - 1 with stage i + D - 1, then
 // multiplies stage i.  k past K reads from a zero word, rows past N or M
-// re-read the last row (never stored).
+// re-read the last row (never stored); the loads take a wavefront-uniform
+// base in SGPRs and a per-lane offset, so moving to the next stage is a
+// scalar add.
 //
 // Wave tile.  The workgroup tile BN x TM is split 2 x 2 (or 1 x 4 when TM is
 // 256) among four wavefronts, or 2 x 4 / 4 x 2 among eight (two per SIMD,
@@ -120,32 +122,52 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
     // k 32 (u % 2) + 8 (l / 16).  Line order: unit u is rows 8 (u % 2) .. + 7
     // of group u / 2, lane l takes row 8 (u % 2) + l / 8 and stores, at
     // position l % 8 of that row, k-chunk (l % 8) ^ swz(row).
-    const uint8_t* src[L];
+    // Per unit: a wavefront-uniform base (the first row of its 16-row group,
+    // clamped), the lane's byte offset from it, and the lane's k within a
+    // block.  Steady-state loads use the scalar-base form with no per-lane
+    // address arithmetic; only the last block of a K that is not a multiple of
+    // KB checks each chunk against K (k >= K loads the zero word).  Padding
+    // units read bytes nobody uses.
+    const uint8_t* base[L];
+    uint32_t voff[L];
     int koff[L];
+    int step[L];
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int u = wave * L + i;
         const int r = LINE ? (u & 1) * 8 + (lane >> 3) : l16;   // row within the group
         koff[i] = LINE ? ((lane & 7) ^ ring_swz(r)) * 8 : (u & 1) * 32 + lg * 8;
-        if (u >= FW + SH::FX) {
-            src[i] = nullptr;   // padding unit: loads the zero word
-        } else if (u < FW) {
-            int n = n_tile * BN + (u >> 1) * 16 + r;
-            n = n < N ? n : N - 1;
-            src[i] = (const uint8_t*)a.W + (int64_t)n * K * 2;
-        } else {
-            int m = m_tile * TM + ((u - FW) >> 1) * 16 + r;
-            m = m < M ? m : M - 1;
-            src[i] = (const uint8_t*)a.X + (int64_t)m * K * 2;
+        base[i] = (const uint8_t*)&g_zero16;
+        voff[i] = 0;
+        step[i] = 0;
+        if (u < FW + SH::FX) {
+            const bool isw = u < FW;
+            const int lim = isw ? N : M;
+            const int g0 = isw ? n_tile * BN + (u >> 1) * 16 : m_tile * TM + ((u - FW) >> 1) * 16;
+            const int r0 = min(g0, lim - 1);
+            const int row = min(g0 + r, lim - 1);   // rows past the end: computed, never stored
+            base[i] = (const uint8_t*)(isw ? a.W : a.X) + (int64_t)r0 * K * 2;
+            voff[i] = (uint32_t)(row - r0) * (uint32_t)K * 2u + 2u * koff[i];
+            step[i] = KB * 2;
         }
+        base[i] = uniform_ptr(base[i]);
     }
+    const bool ktail = (K % KB) != 0;
     auto issue = [&](int kb, int slot) {
+        if (ktail && kb == nkb_all - 1) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const int u = wave * L + i;
+                const uint8_t* p = base[i] + (int64_t)kb * step[i] + voff[i];
+                if (kb * KB + koff[i] >= K) p = (const uint8_t*)&g_zero16;   // K % 8 == 0
+                dma16(p, &ring[slot][u][0]);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int u = wave * L + i;
-            const int k = kb * KB + koff[i];   // K % 8 == 0: a chunk is wholly in or out
-            const void* p = (src[i] && k < K) ? (const void*)(src[i] + (size_t)k * 2) : (const void*)&g_zero16;
-            dma16(p, &ring[slot][u][0]);
+            dma16s(base[i] + (int64_t)kb * step[i], voff[i], &ring[slot][u][0]);
         }
     };
 

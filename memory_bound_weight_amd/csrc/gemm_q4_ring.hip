@@ -132,46 +132,66 @@ __global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
 
     __shared__ u32x4 ring[D][F][64];
 
-    // Per unit this wavefront loads: the lane's source at block 0 (nullptr:
-    // the zero word), the bytes per block, and for X the k of its chunk.
-    const uint8_t* src[L];
+    // Per unit this wavefront loads: a wavefront-uniform base at block 0, the
+    // bytes per block and the lane's byte offset from the base.  Row tiles past
+    // the last one re-read the last (their outputs are never stored); lanes of
+    // the scale unit past the workgroup's row tiles, and padding units, read
+    // bytes nobody uses.  Only X chunks past K must be zero: the last block of
+    // a K that is not a multiple of 128 takes the per-lane path with the zero
+    // word.
+    const uint8_t* base[L];
     int64_t step[L];
-    int kx[L];
+    uint32_t voff[L];
+    int kx[L];   // X units: k of the lane's chunk within a block
     const int T0 = n_tile * (BN / 16);
 #pragma unroll
     for (int i = 0; i < L; ++i) {
         const int u = wave * L + i;
-        src[i] = nullptr;
+        base[i] = (const uint8_t*)&g_zero16;
         step[i] = 0;
+        voff[i] = 0;
         kx[i] = 0;
         if (u < FW) {
-            const int T = T0 + u;
-            if (T < N16) src[i] = (const uint8_t*)a.W + ((int64_t)T * KBn) * 1024 + 16 * lane;
+            const int T = min(T0 + u, N16 - 1);
+            base[i] = (const uint8_t*)a.W + (int64_t)T * KBn * 1024;
             step[i] = 1024;
+            voff[i] = 16 * lane;
         } else if (u == FW) {
-            // 16 bytes per lane: lanes 4 f .. 4 f + 3 carry the 64-byte unit of row tile f
-            const int T = T0 + (lane >> 2);
-            if (lane < 4 * FW && T < N16) src[i] = (const uint8_t*)a.S + (int64_t)T * 64 + 16 * (lane & 3);
+            // lanes 4 f .. 4 f + 3 carry the 64-byte unit of row tile f
+            base[i] = (const uint8_t*)a.S + (int64_t)T0 * 64;
             step[i] = (int64_t)N16 * 64;
+            const int f = min(lane >> 2, FW - 1);
+            voff[i] = 64 * (min(T0 + f, N16 - 1) - T0) + 16 * (lane & 3);
         } else if (u < XU + FX) {
             const int x = u - XU;
             const int r = 4 * (x & 3) + (lane >> 4);   // token row within the 16-token tile
             const int c = (lane & 15) ^ r;             // chunk stored at position lane & 15
             int m = m_tile * TM + (x >> 2) * 16 + r;
             m = m < M ? m : M - 1;                     // rows past M: computed, never stored
-            src[i] = (const uint8_t*)a.X + (int64_t)m * K * 2 + c * 16;
+            base[i] = (const uint8_t*)a.X;
             step[i] = kQB * 2;
+            voff[i] = (uint32_t)m * (uint32_t)K * 2u + 16u * c;
             kx[i] = 8 * c;
         }
+        base[i] = uniform_ptr(base[i]);
     }
+    const bool ktail = (K % kQB) != 0;
     auto issue = [&](int kb, int slot) {
+        if (ktail && kb == KBn - 1) {
+#pragma unroll
+            for (int i = 0; i < L; ++i) {
+                const int u = wave * L + i;
+                const bool isx = u >= XU && u < XU + FX;
+                const uint8_t* p = base[i] + kb * step[i] + voff[i];
+                if (isx && kb * kQB + kx[i] >= K) p = (const uint8_t*)&g_zero16;
+                dma16(p, &ring[slot][u][0]);
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int u = wave * L + i;
-            const bool isx = u >= XU && u < XU + FX;
-            const void* p = &g_zero16;
-            if (src[i] && (!isx || kb * kQB + kx[i] < K)) p = src[i] + kb * step[i];
-            dma16(p, &ring[slot][u][0]);
+            dma16s(base[i] + kb * step[i], voff[i], &ring[slot][u][0]);
         }
     };
 

@@ -310,6 +310,8 @@ void register_gemm_mfma_ring(std::vector<Variant>& out) {
         add_ring1<128, 64, 3, true, 8>(out, S);
         add_ring1<256, 64, 3, true, 8>(out, S);
         add_ring1<128, 128, 3, true, 8>(out, S);
+        add_ring1<256, 128, 3, true, 8>(out, S);
+        add_ring1<256, 128, 3, true, 4>(out, S);
     }
 }
 

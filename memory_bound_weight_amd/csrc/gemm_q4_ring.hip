@@ -389,6 +389,9 @@ void register_gemm_q4_ring(std::vector<Variant>& out) {
         add_q4<128, 128, 3>(out, S);
         add_q4<128, 128, 2>(out, S);
         add_q4<64, 256, 2>(out, S);
+        add_q4<256, 128, 3>(out, S);
+        add_q4<256, 128, 2>(out, S);
+        add_q4<256, 64, 4>(out, S);
         // eight wavefronts, two per SIMD: one multiplies while the other unpacks
         add_q4<128, 16, 6, 8>(out, S);
         add_q4<128, 64, 4, 8>(out, S);

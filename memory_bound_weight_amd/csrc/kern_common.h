@@ -75,24 +75,7 @@ __device__ __forceinline__ void dma16(const void* g, const void* lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l)
                  : "memory", "m0");
 }
-// The same load with a wavefront-uniform 64-bit base in SGPRs and a 32-bit
-// per-lane byte offset (the saddr form): moving to the next block is a scalar
-// add, with no per-lane address arithmetic.
-__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, const void* lds) {
-    const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS const void*)lds;
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(l)
-                 : "memory", "m0");
-}
 #pragma clang diagnostic pop
-
-// A pointer every lane of the wavefront holds the same value of, as such.
-template <typename T>
-__device__ __forceinline__ const T* uniform_ptr(const T* p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
 
 namespace {
 // Lanes with nothing to load read these zeros (a valid address).

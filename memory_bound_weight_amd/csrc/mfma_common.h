@@ -1,11 +1,33 @@
-// Pieces shared by the matrix-core kernels: the 16x16x32 bf16 product and the
-// store of a wavefront's output tiles (direct, or split-K through the
-// workspace with a deterministic reduction).
+// Pieces shared by the matrix-core ring kernels: the scalar-base form of the
+// direct-to-LDS load, the 16x16x32 bf16 product and the store of a
+// wavefront's output tiles (direct, or split-K through the workspace with a
+// deterministic reduction).
 #pragma once
 
 #include "kern_common.h"
 
 namespace lin {
+
+// dma16 with a wavefront-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the saddr form of global_load_lds_dwordx4): moving to the next
+// block is a scalar add, with no per-lane address arithmetic.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved: set here, used by nothing else
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, const void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)(LDS_AS const void*)lds;
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(l)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// A pointer every lane of the wavefront holds the same value of, as such.
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -396,13 +396,17 @@ def run_skinny(args, dev, fmt):
     dom = max(cases, key=lambda c: per_case[c.name]["us"])
     d = per_case[dom.name]
     ceil = read_ceiling(dom.bytes, dev, reps)
-    roofline = {"bound": "hbm", "achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": d["hbm_frac"], "traffic": None,
-                "read_ceiling_GB_s": round(ceil, 1), "frac_of_read_ceiling": round(d["GB_s"] / ceil, 4),
-                "kernel": d["variant"], "case": dom.name,
-                "avg_launch_us": d["us"], "bytes_per_launch": dom.bytes,
-                "mfma": {"achieved": d["TFLOP_s"], "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": d["mfma_frac"]}}
+    # the roof that bounds the dominant case at peak specs: HBM bytes or MFMA FLOPs
+    mfma_bound = dom.flop / (MFMA_PEAK_TFS * 1e6) > dom.bytes / (HBM_PEAK_GBS * 1e3)
+    hbm = {"achieved": d["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["hbm_frac"],
+           "read_ceiling_GB_s": round(ceil, 1), "frac_of_read_ceiling": round(d["GB_s"] / ceil, 4)}
+    mfma = {"achieved": d["TFLOP_s"], "peak": MFMA_PEAK_TFS, "unit": "TFLOP/s", "frac": d["mfma_frac"],
+            "flop_per_launch": dom.flop}
+    roofline = {"bound": "mfma" if mfma_bound else "hbm"}
+    roofline.update(mfma if mfma_bound else hbm)
+    roofline.update({"traffic": None, "kernel": d["variant"], "case": dom.name,
+                     "avg_launch_us": d["us"], "bytes_per_launch": dom.bytes})
+    roofline["hbm" if mfma_bound else "mfma"] = hbm if mfma_bound else mfma
     out = {"metric": METRIC, "value": round(step_bytes / wall / 1e9, 1), "unit": "GB/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(wall * 1e3, 4), "higher_is_better": True, "scaling": "weak",

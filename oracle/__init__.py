@@ -11,14 +11,17 @@ from .oracle import (  # noqa: F401
     LIB_PATH,
     bf16_value,
     build,
+    dequant_i8,
     dequant_q4g64,
     f16_from_f64,
     f16_value,
     gemm_dense,
     gemm_f64w,
+    gemm_i8,
     gemm_q4g64,
     load,
     open_lib,
+    quantize_i8,
     quantize_q4g64,
     use,
 )

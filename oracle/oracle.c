@@ -20,6 +20,11 @@
  *    two codes per byte along k.
  *  - "llm-rs" (roofline essay), section 5 "Batching moves decode from memory toward
  *    math": a batch of M tokens multiplies the same weights, i.e. Y = X . W^T.
+ *  - TileInfer.jl post, "Pushing further with cheating: INT8 quantization":
+ *    symmetric INT8 in -127..127 with one Float32 scale per output channel,
+ *    scale = max|w| / 127, every weight rounded to the nearest multiple of the
+ *    scale; the product multiplies the INT8 values in and applies the channel's
+ *    scale once at the end.
  *
  * Readings where the definition leaves a step open (each is also pinned by a test):
  *  - bf16 and fp16 are decoded from their bit definitions (IEEE-754 binary16;
@@ -30,6 +35,9 @@
  *  - The scale used to quantize is the stored fp16 value.  A group whose absmax
  *    is 0 gets s = 0 and q = 0.  A scale beyond the fp16 range saturates to the
  *    largest finite fp16 (65504); weights are assumed finite.
+ *  - INT8: the stored scale is the fp32 nearest to max|w| / 127 (formed as an
+ *    fp64 quotient rounded to fp32); q = round_half_even(w / s) with w / s in
+ *    fp64, clamped to [-127, 127]; a row whose absmax is 0 gets s = 0, q = 0.
  *
  * Parity status: every function below is pinned by tests/test_oracle.py against
  * brute force, closed forms, library conversions or figures printed on the pages.
@@ -211,6 +219,59 @@ void orc_quantize_q4g64(const uint16_t* W, int64_t N, int64_t K, uint8_t* Wq,
                 }
                 Wq[n * (K / 2) + k / 2] = (uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4));
             }
+        }
+    }
+}
+
+/* ---- int8, one fp32 scale per output channel ---------------------------- */
+
+/* Quantise bf16 weights W[N][K] to int8 with one fp32 scale per row n:
+ *   a = max_k |w|;  s = fp32 nearest to a/127;
+ *   q = s > 0 ? clamp(round_half_even(w/s), -127, 127) : 0.
+ * Wq: int8 [N][K], S: fp32 [N]. */
+void orc_quantize_i8(const uint16_t* W, int64_t N, int64_t K, int8_t* Wq, float* S) {
+    for (int64_t n = 0; n < N; ++n) {
+        double a = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double w = fabs(orc_bf16_value(W[n * K + k]));
+            if (w > a) a = w;
+        }
+        float s = (float)(a / 127.0);
+        S[n] = s;
+        for (int64_t k = 0; k < K; ++k) {
+            double r = 0.0;
+            if (s > 0.0f) {
+                double v = orc_bf16_value(W[n * K + k]) / (double)s;
+                r = (v < 0.0) ? -round_half_even(-v) : round_half_even(v);
+                if (r < -127.0) r = -127.0;
+                if (r > 127.0) r = 127.0;
+            }
+            Wq[n * K + k] = (int8_t)r;
+        }
+    }
+}
+
+/* w[n][k] = q[n][k] * s[n], exact in fp64.  Wd: [N][K]. */
+void orc_dequant_i8(const int8_t* Wq, const float* S, int64_t N, int64_t K, double* Wd) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) Wd[n * K + k] = (double)Wq[n * K + k] * (double)S[n];
+}
+
+/* Y[m][n] = s[n] * sum_k q[n][k] * X[m][k]: the integer weights multiply in
+ * (fp64, k ascending) and the channel scale is applied once at the end.
+ * B[m][n] = sum_k |q[n][k] * s[n] * X[m][k]|.  B may be NULL. */
+void orc_gemm_i8(const int8_t* Wq, const float* S, const uint16_t* X, int64_t M, int64_t N,
+                 int64_t K, double* Y, double* B) {
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double p = (double)Wq[n * K + k] * orc_bf16_value(X[m * K + k]);
+                acc += p;
+                mag += fabs(p);
+            }
+            Y[m * N + n] = (double)S[n] * acc;
+            if (B) B[m * N + n] = fabs((double)S[n]) * mag;
         }
     }
 }

@@ -1,7 +1,8 @@
 """ctypes marshalling for oracle.c (test infrastructure only; no arithmetic here).
 
 Arrays cross the boundary as raw bit patterns: bf16 and fp16 values travel as
-uint16 arrays, packed int4 weights as uint8 arrays, results come back as fp64.
+uint16 arrays, packed int4 weights as uint8 arrays, int8 weights as int8 and
+their fp32 scales as float32 arrays; results come back as fp64.
 """
 import ctypes
 import os
@@ -68,6 +69,12 @@ def open_lib(path):
     lib.orc_gemm_q4g64.restype = None
     lib.orc_quantize_q4g64.argtypes = [P, I64, I64, P, P]
     lib.orc_quantize_q4g64.restype = None
+    lib.orc_quantize_i8.argtypes = [P, I64, I64, P, P]
+    lib.orc_quantize_i8.restype = None
+    lib.orc_dequant_i8.argtypes = [P, P, I64, I64, P]
+    lib.orc_dequant_i8.restype = None
+    lib.orc_gemm_i8.argtypes = [P, P, P, I64, I64, I64, P, P]
+    lib.orc_gemm_i8.restype = None
     return lib
 
 
@@ -175,3 +182,44 @@ def quantize_q4g64(W):
     S = np.empty((N, K // 64), dtype=np.uint16)
     lib.orc_quantize_q4g64(_ptr(W), N, K, _ptr(Wq), _ptr(S))
     return Wq, S
+
+
+def quantize_i8(W):
+    """W: uint16 [N, K] bf16 bits.  Returns (Wq int8 [N, K], S float32 [N])."""
+    lib = load()
+    W = _c(W, np.uint16)
+    N, K = W.shape
+    Wq = np.empty((N, K), dtype=np.int8)
+    S = np.empty((N,), dtype=np.float32)
+    lib.orc_quantize_i8(_ptr(W), N, K, _ptr(Wq), _ptr(S))
+    return Wq, S
+
+
+def dequant_i8(Wq, S):
+    """Wq int8 [N, K], S float32 [N].  Returns fp64 [N, K] = q * s."""
+    lib = load()
+    Wq = _c(Wq, np.int8)
+    S = _c(S, np.float32)
+    N, K = Wq.shape
+    if S.shape != (N,):
+        raise ValueError("scale shape mismatch")
+    Wd = np.empty((N, K), dtype=np.float64)
+    lib.orc_dequant_i8(_ptr(Wq), _ptr(S), N, K, _ptr(Wd))
+    return Wd
+
+
+def gemm_i8(Wq, S, X):
+    """INT8 product: Wq int8 [N, K], S float32 [N], X uint16 [M, K] bf16 bits.
+    Returns (Y, B), fp64 [M, N]."""
+    lib = load()
+    Wq = _c(Wq, np.int8)
+    S = _c(S, np.float32)
+    X = _c(X, np.uint16)
+    N, K = Wq.shape
+    M = X.shape[0]
+    if X.shape[1] != K or S.shape != (N,):
+        raise ValueError("shape mismatch")
+    Y = np.empty((M, N), dtype=np.float64)
+    B = np.empty((M, N), dtype=np.float64)
+    lib.orc_gemm_i8(_ptr(Wq), _ptr(S), _ptr(X), M, N, K, _ptr(Y), _ptr(B))
+    return Y, B

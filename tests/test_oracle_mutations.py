@@ -1,6 +1,7 @@
 """The oracle's pins must catch plausible mistakes.  Each case below compiles a
 copy of oracle.c with one planted mistake (on the CPU, in a temporary
-directory) and checks that at least one pin in test_oracle.py fails on it."""
+directory) and checks that at least one pin in test_oracle.py or
+test_oracle_i8.py fails on it."""
 import os
 import subprocess
 import tempfile
@@ -9,6 +10,7 @@ import pytest
 
 import oracle
 import test_oracle as pins
+import test_oracle_i8 as pins_i8
 
 SRC = oracle.oracle.SRC_PATH
 
@@ -38,15 +40,27 @@ MUTATIONS = [
     ("quant-scale-divisor", "orc_f16_from_f64(a / 7.0)", "orc_f16_from_f64(a / 8.0)"),
     ("quant-clamp-low", "if (r < -8.0) r = -8.0;", "if (r < -7.0) r = -7.0;"),
     ("quant-no-saturation", "if ((sbits & 0x7FFF) == 0x7C00) sbits = 0x7BFF;", ""),
-    ("quant-truncating-round", "r = (v < 0.0) ? -round_half_even(-v) : round_half_even(v);",
-     "r = trunc(v);"),
+    ("quant-truncating-round", "r = (v < 0.0) ? -round_half_even(-v) : round_half_even(v);\n                        if (r < -8.0)",
+     "r = trunc(v);\n                        if (r < -8.0)"),
     ("quant-pack-order", "(uint8_t)((q[0] & 0xF) | ((q[1] & 0xF) << 4))",
      "(uint8_t)((q[1] & 0xF) | ((q[0] & 0xF) << 4))"),
-    ("quant-absmax-signed", "double w = fabs(orc_bf16_value(W[n * K + k]));",
-     "double w = orc_bf16_value(W[n * K + k]);"),
+    ("quant-absmax-signed", "double w = fabs(orc_bf16_value(W[n * K + k]));\n                if (w > a) a = w;\n            }\n            uint16_t",
+     "double w = orc_bf16_value(W[n * K + k]);\n                if (w > a) a = w;\n            }\n            uint16_t"),
+    ("i8-scale-divisor", "(float)(a / 127.0)", "(float)(a / 128.0)"),
+    ("i8-truncating-round", "r = (v < 0.0) ? -round_half_even(-v) : round_half_even(v);\n                if (r < -127.0)",
+     "r = trunc(v);\n                if (r < -127.0)"),
+    ("i8-round-half-up", "r = (v < 0.0) ? -round_half_even(-v) : round_half_even(v);\n                if (r < -127.0)",
+     "r = floor(v + 0.5);\n                if (r < -127.0)"),
+    ("i8-absmax-signed", "double w = fabs(orc_bf16_value(W[n * K + k]));\n            if (w > a) a = w;\n        }\n        float s",
+     "double w = orc_bf16_value(W[n * K + k]);\n            if (w > a) a = w;\n        }\n        float s"),
+    ("i8-scale-not-applied", "Y[m * N + n] = (double)S[n] * acc;", "Y[m * N + n] = acc;"),
+    ("i8-unsigned-codes", "double p = (double)Wq[n * K + k] * orc_bf16_value",
+     "double p = (double)(uint8_t)Wq[n * K + k] * orc_bf16_value"),
+    ("i8-dequant-scale-index", "Wd[n * K + k] = (double)Wq[n * K + k] * (double)S[n];",
+     "Wd[n * K + k] = (double)Wq[n * K + k] * (double)S[k % N];"),
 ]
 
-PIN_FUNCS = [getattr(pins, n) for n in dir(pins) if n.startswith("test_")]
+PIN_FUNCS = [getattr(m, n) for m in (pins, pins_i8) for n in dir(m) if n.startswith("test_")]
 
 
 def _run_pins():

@@ -16,6 +16,8 @@
  *                          k = 2j in bits 0..3 and k = 2j+1 in bits 4..7; each
  *                          code is 4-bit two's complement q in [-8, 7]
  *   S   fp16    [N][K/64]  scale of each group of 64 consecutive k; w = q * s
+ *   Wi  int8    [N][K]     INT8 weights q in [-127, 127] (lin_gemv_i8)
+ *   Si  fp32    [N]        one scale per output channel (row); w = q * s
  *   x/X bf16    [M][K]     activations, one row per token
  *   y/Y fp32    [M][N]     outputs, overwritten (no accumulation into y)
  * Accumulation is fp32.  The result of every configuration is within
@@ -23,8 +25,8 @@
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points
- * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemm_skinny_bf16, lin_gemm_skinny_q4g64,
- * lin_quantize_q4g64, lin_q4g64_tile)
+ * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemv_i8, lin_gemm_skinny_bf16,
+ * lin_gemm_skinny_q4g64, lin_quantize_q4g64, lin_quantize_i8, lin_q4g64_tile)
  * validate their arguments in O(1), enqueue kernels on `stream` (a hipStream_t;
  * NULL = the null stream) and return without waiting: they never allocate,
  * never synchronise and are safe inside HIP graph capture.  Results are
@@ -50,19 +52,20 @@ extern "C" {
 typedef enum lin_status {
     LIN_OK = 0,
     LIN_ERR_NULL = -1,        /* a required pointer is NULL */
-    LIN_ERR_SHAPE = -2,       /* M, N or K out of range, or K not a multiple of 8 (bf16) / 64 (int4) */
-    LIN_ERR_ALIGN = -3,       /* W, Wq, Wt, St, x or X not 16-byte aligned; y, Y not 4-byte; S not 2-byte */
+    LIN_ERR_SHAPE = -2,       /* M, N or K out of range, or K not a multiple of 8 (bf16) / 64 (int4) / 16 (int8) */
+    LIN_ERR_ALIGN = -3,       /* W, Wq, Wi, Wt, St, x or X not 16-byte aligned; y, Y, Si not 4-byte; S not 2-byte */
     LIN_ERR_UNSUPPORTED = -4, /* the requested configuration cannot run this shape */
     LIN_ERR_HIP = -5,         /* the HIP runtime reported an error */
     LIN_ERR_ARG = -6          /* unknown kind, malformed configuration, bad index */
 } lin_status;
 
-/* The four products; `kind` selects one in the tuning calls. */
+/* The five products; `kind` selects one in the tuning calls. */
 typedef enum lin_kind {
     LIN_KIND_GEMV_BF16 = 0,   /* lin_gemv_bf16 */
     LIN_KIND_GEMV_Q4G64 = 1,  /* lin_gemv_q4g64 */
     LIN_KIND_SKINNY_BF16 = 2, /* lin_gemm_skinny_bf16 */
-    LIN_KIND_SKINNY_Q4G64 = 3 /* lin_gemm_skinny_q4g64 (tiled int4-g64 weights) */
+    LIN_KIND_SKINNY_Q4G64 = 3, /* lin_gemm_skinny_q4g64 (tiled int4-g64 weights) */
+    LIN_KIND_GEMV_I8 = 4       /* lin_gemv_i8 */
 } lin_kind;
 
 /* Kernel families. */
@@ -102,7 +105,7 @@ typedef struct lin_config {
     float us;
 } lin_config;
 
-/* Largest M accepted by lin_gemv_bf16 / lin_gemv_q4g64, and by the skinny products. */
+/* Largest M accepted by lin_gemv_bf16 / lin_gemv_q4g64 / lin_gemv_i8, and by the skinny products. */
 #define LIN_GEMV_MAX_M 8
 #define LIN_SKINNY_MAX_M 256
 /* Largest K accepted by every product. */
@@ -117,6 +120,14 @@ int lin_gemv_bf16(const void* W, const void* x, float* y,
  * K % 64 == 0, 1 <= M <= LIN_GEMV_MAX_M. */
 int lin_gemv_q4g64(const void* Wq, const void* S, const void* x, float* y,
                    int64_t M, int64_t N, int64_t K, void* stream);
+
+/* The same product with INT8 weights and one fp32 scale per output channel
+ * (TileInfer.jl post, "Pushing further with cheating: INT8 quantization": the
+ * INT8 values are multiplied in and the channel's scale applied once at the
+ * end): y[m][n] = Si[n] * sum_k Wi[n][k] * x[m][k].  K % 16 == 0,
+ * 1 <= M <= LIN_GEMV_MAX_M; Wi 16-byte and Si 4-byte aligned. */
+int lin_gemv_i8(const void* Wi, const void* Si, const void* x, float* y,
+                int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Batched-token product Y = X . W^T for 1 <= M <= LIN_SKINNY_MAX_M tokens,
  * K % 8 == 0.  Small M streams W once through the vector ALUs; larger M runs on
@@ -160,8 +171,9 @@ int lin_q4g64_tile(const void* Wq, const void* S, void* Wt, void* St,
 /* Load-time tuning (tinyinfer post, "v0.2": time the candidates on every
  * distinct shape when the model loads, keep the fastest).  Times every
  * candidate configuration of `kind` for (M, N, K) on the caller's buffers,
- * which must be valid for that kind (S is used only by the int4 kinds and
- * may be NULL otherwise; W and S are Wt and St for LIN_KIND_SKINNY_Q4G64; y receives scratch results).  Each timed call starts
+ * which must be valid for that kind (S is used only by the int4 and INT8 kinds
+ * and may be NULL otherwise; W and S are Wt and St for LIN_KIND_SKINNY_Q4G64, Wi
+ * and Si for LIN_KIND_GEMV_I8; y receives scratch results).  Each timed call starts
  * from cold caches.  The fastest configuration is stored in the per-device
  * table and used by later calls with the same (kind, M, N, K); if `out` is not
  * NULL it receives it, with `us` set.  Unlike the compute calls this one
@@ -174,7 +186,7 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
 /* The same load-time tuning timed the way a decode step runs the layer: every
  * candidate is captured as one graph of back-to-back calls cycling over the
  * `count` >= 1 weight matrices W[0..count-1] (and S[0..count-1] for the
- * int4 kinds; S may be NULL otherwise) of the same shape, e.g. the
+ * int4 and INT8 kinds; S may be NULL otherwise) of the same shape, e.g. the
  * layers of a model, and the graph is replayed; `us` is the mean time per
  * call.  W and S are host arrays of device pointers, owned by the caller and
  * only read during the call.  Stores the fastest configuration like
@@ -212,6 +224,15 @@ int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* 
  * q = s > 0 ? clamp(round_half_even(w / s), -8, 7) : 0, with w/s in fp64.
  * Writes Wq [N][K/2] and S [N][K/64].  W must hold finite values. */
 int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, void* stream);
+
+/* Load-time weight preparation for lin_gemv_i8: quantise bf16 W [N][K]
+ * (K % 16 == 0) to INT8 with one fp32 scale per row (TileInfer.jl post, INT8
+ * section: scale = max |w| / 127, each weight rounded to the nearest multiple of
+ * the scale).  Per row: a = max_k |w|; s = fp32 nearest to a/127 (the quotient
+ * formed in fp64, rounded once); q = s > 0 ? clamp(round_half_even(w / s),
+ * -127, 127) : 0 with w / s in fp64.  Writes Wi [N][K] and Si [N].  W must hold
+ * finite values. */
+int lin_quantize_i8(const void* W, void* Wi, void* Si, int64_t N, int64_t K, void* stream);
 
 /* Measurement: read every byte of `buf` (device, 16-byte aligned, `bytes` a
  * multiple of 16) once and discard it.  This is the ceiling a product is

@@ -28,6 +28,7 @@ LIN_KIND_GEMV_BF16 = 0
 LIN_KIND_GEMV_Q4G64 = 1
 LIN_KIND_SKINNY_BF16 = 2
 LIN_KIND_SKINNY_Q4G64 = 3
+LIN_KIND_GEMV_I8 = 4
 
 LIN_ALGO_VALU = 1
 LIN_ALGO_MFMA = 2
@@ -36,7 +37,8 @@ LIN_GEMV_MAX_M = 8
 LIN_SKINNY_MAX_M = 256
 
 # Every symbol include/lin.h declares.
-EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemm_skinny_bf16", "lin_gemm_skinny_q4g64",
+EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemv_i8", "lin_gemm_skinny_bf16",
+           "lin_gemm_skinny_q4g64", "lin_quantize_i8",
            "lin_q4g64_tiled_size", "lin_q4g64_tile", "lin_autotune",
            "lin_autotune_set", "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
            "lin_quantize_q4g64", "lin_stream_read", "lin_status_string", "lin_version")
@@ -75,6 +77,8 @@ def _load():
     sig = {
         "lin_gemv_bf16": [P, P, P, I64, I64, I64, P],
         "lin_gemv_q4g64": [P, P, P, P, I64, I64, I64, P],
+        "lin_gemv_i8": [P, P, P, P, I64, I64, I64, P],
+        "lin_quantize_i8": [P, P, P, I64, I64, P],
         "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
         "lin_gemm_skinny_q4g64": [P, P, P, P, I64, I64, I64, P],
         "lin_q4g64_tiled_size": [I64, I64, ctypes.POINTER(I64), ctypes.POINTER(I64)],
@@ -174,6 +178,37 @@ def lin_gemv_q4g64(Wq, S, x, y=None):
     _check(_lib.lin_gemv_q4g64(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(),
                                M, N, K, _stream(Wq)), "lin_gemv_q4g64")
     return y
+
+
+def lin_gemv_i8(Wq, S, x, y=None):
+    """Same product with INT8 weights Wq int8 [N, K] and one fp32 scale per row S [N]."""
+    x = _as2d(x)
+    _need(Wq, torch.int8, "Wq", 2)
+    _need(S, torch.float32, "S", 1)
+    _need(x, torch.bfloat16, "x", 2)
+    N, K = Wq.shape
+    M = x.shape[0]
+    if x.shape[1] != K or tuple(S.shape) != (N,):
+        raise ValueError("shape mismatch: Wq [N, K], S [N], x [M, K]")
+    y = _out(y, M, N, Wq.device)
+    _check(_lib.lin_gemv_i8(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K,
+                            _stream(Wq)), "lin_gemv_i8")
+    return y
+
+
+def lin_quantize_i8(W, Wq=None, S=None):
+    """INT8 weights from bf16 W [N, K]: returns (Wq int8 [N, K], S fp32 [N])."""
+    _need(W, torch.bfloat16, "W", 2)
+    N, K = W.shape
+    if Wq is None:
+        Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    if S is None:
+        S = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _need(Wq, torch.int8, "Wq", 2)
+    _need(S, torch.float32, "S", 1)
+    _check(_lib.lin_quantize_i8(W.data_ptr(), Wq.data_ptr(), S.data_ptr(), N, K, _stream(W)),
+           "lin_quantize_i8")
+    return Wq, S
 
 
 def lin_gemm_skinny_bf16(W, X, Y=None):

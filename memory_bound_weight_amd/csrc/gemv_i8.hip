@@ -1,0 +1,70 @@
+// Standalone kernels, launch geometry and the candidate list of the INT8
+// product in gemv_i8_impl.h.
+#include "gemv_i8_impl.h"
+#include "registry.h"
+
+namespace lin {
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+__global__ __launch_bounds__(kBlock) void gemv_i8_valu(KArgs a) {
+    gemv_i8_valu_block<MT, R, U, SPLIT, STAGE>(a, blockIdx.x);
+}
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static bool geom_i8(const Variant&, int M, int N, int K, dim3* grid, size_t* lds) {
+    constexpr int rows_per_block = R * (4 / SPLIT);
+    size_t bytes = STAGE ? 16 * stage_x_units(MT, K) : 0;
+    if (bytes > kMaxDynLds) return false;
+    (void)M;
+    *grid = dim3((unsigned)((N + rows_per_block - 1) / rows_per_block));
+    *lds = bytes;
+    return true;
+}
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static void add(std::vector<Variant>& out) {
+    Variant v{};
+    v.kind = LIN_KIND_GEMV_I8;
+    v.cfg.algo = LIN_ALGO_VALU;
+    v.cfg.rows = R;
+    v.cfg.unroll = U;
+    v.cfg.split = SPLIT;
+    v.cfg.stage_x = STAGE ? 1 : 0;
+    v.cfg.tile_m = MT;
+    v.mt = MT;
+    v.min_m = MT / 2 + 1;
+    v.func = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE>;
+    v.geometry = &geom_i8<MT, R, U, SPLIT, STAGE>;
+    out.push_back(v);
+}
+
+template <int MT, int R, int U>
+static void add_splits(std::vector<Variant>& out) {
+    add<MT, R, U, 1, false>(out);
+    add<MT, R, U, 2, false>(out);
+    add<MT, R, U, 4, false>(out);
+    add<MT, R, U, 1, true>(out);
+    add<MT, R, U, 2, true>(out);
+    add<MT, R, U, 4, true>(out);
+}
+
+void register_gemv_i8(std::vector<Variant>& out) {
+    add_splits<1, 1, 2>(out);
+    add_splits<1, 1, 4>(out);
+    add_splits<1, 2, 1>(out);
+    add_splits<1, 2, 2>(out);
+    add_splits<1, 4, 1>(out);
+    add_splits<1, 4, 2>(out);
+    add_splits<1, 8, 1>(out);
+
+    add_splits<2, 1, 2>(out);
+    add_splits<2, 2, 1>(out);
+    add_splits<2, 4, 1>(out);
+
+    add_splits<4, 1, 2>(out);
+    add_splits<4, 2, 1>(out);
+
+    add_splits<8, 1, 1>(out);
+}
+
+}  // namespace lin

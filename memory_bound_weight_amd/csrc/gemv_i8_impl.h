@@ -1,0 +1,195 @@
+// INT8 streaming product on the vector ALUs, one fp32 scale per output
+// channel: y[m][n] = s[n] * sum_k q[n][k] x[m][k] for M <= 8 tokens (TileInfer.jl
+// post, "Pushing further with cheating: INT8 quantization": the INT8 values
+// are multiplied in and the channel's scale is applied once at the end).  One
+// byte per weight halves the bf16 stream.
+//
+// Mapping.  As the bf16 kernel: four wavefronts per workgroup, a wavefront
+// owns R rows, each lane reads consecutive 16-byte chunks (16 weights) of a
+// row with a two-stage register pipeline, SPLIT wavefronts may share rows
+// along K, x comes through the caches or is staged in LDS once per workgroup.
+//
+// Conversion.  q + 128 is an unsigned byte (one XOR with 0x80 per byte, four
+// bytes per instruction), and v_cvt_f32_ubyte0..3 turn each byte into an fp32
+// directly, so a weight costs one conversion and one fp32 fma with x, whose
+// bf16 values become fp32 by a shift (shared by the R rows).  The products of
+// (q + 128) with x are exact in fp32; the offset is removed once per lane and
+// row at the end: acc - 128 * sum(x), with sum(x) over the lane's chunks shared
+// by all rows.  The wavefront then reduces as usual and one lane per output
+// multiplies by the row's scale.
+#pragma once
+
+#include <type_traits>
+
+#include "kern_common.h"
+
+namespace lin {
+
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+__device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block) {
+    constexpr int GROUPS = 4 / SPLIT;
+    constexpr int V = R * MT;
+    constexpr int STEP = kWave * U;   // chunks per pipeline step
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+    const int grp = wave / SPLIT;
+    const int part = wave - grp * SPLIT;
+    const int M = a.M, N = a.N, K = a.K;
+    const int nch = K >> 4;   // 16-byte chunks (16 weights) per row
+    const int xun = K >> 3;   // 16-byte units of x per token row
+    const int8_t* __restrict__ W = (const int8_t*)a.W;
+    const float* __restrict__ S = (const float*)a.S;
+    const uint16_t* __restrict__ X = (const uint16_t*)a.X;
+
+    extern __shared__ u32x4 xs[];   // STAGE: [MT][K/8] units of x
+    if constexpr (STAGE) stage_x_dma(X, M, MT, K, xs);
+
+    const int64_t row0 = (block * GROUPS + grp) * R;
+    const uint8_t* wb[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int64_t row = row0 + r;
+        row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
+        wb[r] = (const uint8_t*)(W + row * (int64_t)K);
+    }
+    const uint8_t* xb[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xb[m] = (const uint8_t*)(X + (size_t)(m < M ? m : 0) * K);
+
+    const int per = (nch + SPLIT - 1) / SPLIT;
+    const int cbeg = part * per;
+    const int cend = min(nch, cbeg + per);
+
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.f;
+    float xsum[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xsum[m] = 0.f;
+
+    struct Stage {
+        u32x4 w[U][R];
+        u32x4 x[U][MT][STAGE ? 1 : 2];   // the chunk's 16 x values (unstaged x only)
+    };
+    // As in the bf16 kernel, a partial last step re-loads chunk cend - 1 in
+    // the lanes past cend and drops its products and its x sum.
+    auto load = [&](Stage& s, int cb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = min(cb + kWave * u + lane, cend - 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r) s.w[u][r] = load_w16(wb[r], (uint32_t)c * 16u);
+            if constexpr (!STAGE) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m) {
+                    s.x[u][m][0] = load_x16(xb[m], (uint32_t)c * 32u);
+                    s.x[u][m][1] = load_x16(xb[m], (uint32_t)c * 32u + 16u);
+                }
+            }
+        }
+    };
+    auto compute = [&](const Stage& s, int cb, auto masked) {
+        constexpr bool MASK = decltype(masked)::value;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int c = cb + kWave * u + lane;
+            const int cc = min(c, cend - 1);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                u32x4 x0, x1;
+                if constexpr (STAGE) {
+                    x0 = xs[m * xun + 2 * cc];
+                    x1 = xs[m * xun + 2 * cc + 1];
+                } else {
+                    x0 = s.x[u][m][0];
+                    x1 = s.x[u][m][1];
+                }
+                float xf[16];
+                float t = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t d = i < 4 ? x0[i] : x1[i - 4];
+                    t = dot2(d, 0x3F803F80u, t);   // bf16 (1, 1): sum of the pair
+                    xf[2 * i] = bitsf(d << 16);
+                    xf[2 * i + 1] = bitsf(d & 0xFFFF0000u);
+                }
+                xsum[m] += (MASK && c >= cend) ? 0.f : t;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    float p = MASK ? 0.f : acc[r * MT + m];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t wu = s.w[u][r][j] ^ 0x80808080u;   // q + 128 per byte
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            p = fmaf((float)((wu >> (8 * e)) & 0xFFu), xf[4 * j + e], p);
+                    }
+                    if constexpr (MASK)
+                        acc[r * MT + m] += c < cend ? p : 0.f;
+                    else
+                        acc[r * MT + m] = p;
+                }
+            }
+        }
+    };
+    auto step = [&](const Stage& s, int cb) {
+        if (cb + STEP > cend)
+            compute(s, cb, std::true_type{});
+        else
+            compute(s, cb, std::false_type{});
+    };
+
+    const int nsteps = cend > cbeg ? (cend - cbeg + STEP - 1) / STEP : 0;
+    int cb = cbeg;
+    Stage s0, s1;
+    if (nsteps > 0) load(s0, cb);
+    if constexpr (STAGE) {
+        // x copies were issued before the U R loads of stage 0 (see the bf16 kernel)
+        if (nsteps > 0)
+            wait_cnt<U * R, 15>();
+        else
+            wait_cnt<0, 15>();
+        barrier_only();
+    }
+    if (nsteps > 0) {
+        for (int it = 0;;) {
+            if (it + 1 < nsteps) load(s1, cb + STEP);
+            step(s0, cb);
+            cb += STEP;
+            if (++it >= nsteps) break;
+            if (it + 1 < nsteps) load(s0, cb + STEP);
+            step(s1, cb);
+            cb += STEP;
+            if (++it >= nsteps) break;
+        }
+    }
+    // remove the +128 offset: sum_k (q + 128) x - 128 sum_k x
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r * MT + m] = fmaf(-128.f, xsum[m], acc[r * MT + m]);
+
+    wave_reduce<V>(acc);
+    if constexpr (SPLIT == 1) {
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) {
+            const int r = idx / MT, m = idx - (idx / MT) * MT;
+            if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = K > 0 ? S[row0 + r] * val : 0.f;
+        });
+    } else {
+        __shared__ float red[4][V];
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) { red[wave][idx] = val; });
+        __syncthreads();
+        if (part == 0) {
+            for_each_reduced<V>(acc, lane, [&](int idx, float) {
+                const int r = idx / MT, m = idx - (idx / MT) * MT;
+                float t = red[wave][idx];
+#pragma unroll
+                for (int p = 1; p < SPLIT; ++p) t += red[wave + p][idx];
+                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = K > 0 ? S[row0 + r] * t : 0.f;
+            });
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace lin

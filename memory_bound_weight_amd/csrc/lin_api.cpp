@@ -25,6 +25,7 @@ const std::vector<Variant>& registry() {
         register_gemm_mfma(*r);
         register_gemm_mfma_ring(*r);
         register_gemm_q4_ring(*r);
+        register_gemv_i8(*r);
         return r;
     }();
     return *reg;
@@ -94,7 +95,11 @@ int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
             if (workspace_need(registry()[i], M, N, K) == 0) return i;
         return -1;
     }
-    if (kind == LIN_KIND_GEMV_Q4G64) {
+    if (kind == LIN_KIND_GEMV_I8) {
+        want.rows = 2;
+        want.unroll = mt <= 1 ? 2 : 1;
+        want.split = N >= 4096 ? 1 : (N >= 1024 ? 2 : 4);
+    } else if (kind == LIN_KIND_GEMV_Q4G64) {
         want.rows = mt <= 1 ? 4 : (mt <= 4 ? 2 : 1);
         want.unroll = 1;
         want.split = N >= 4096 ? 1 : (N >= 1024 ? 2 : 4);
@@ -246,19 +251,21 @@ int check(int kind, const void* W, const void* S, const void* x, const float* y,
           int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return LIN_ERR_SHAPE;
     const bool q4 = kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64;
+    const bool i8 = kind == LIN_KIND_GEMV_I8;
     const int64_t maxm = (kind == LIN_KIND_SKINNY_BF16 || kind == LIN_KIND_SKINNY_Q4G64)
                              ? LIN_SKINNY_MAX_M
                              : LIN_GEMV_MAX_M;
     if (M > maxm || N > 0x7FFFFFFF || K > LIN_MAX_K) return LIN_ERR_SHAPE;
-    if (q4 ? (K % 64) : (K % 8)) return LIN_ERR_SHAPE;
+    if (q4 ? (K % 64) : (i8 ? (K % 16) : (K % 8))) return LIN_ERR_SHAPE;
     if (M == 0 || N == 0) return 1;
     if (!y) return LIN_ERR_NULL;
-    if (K > 0 && (!W || !x || (q4 && !S))) return LIN_ERR_NULL;
+    if (K > 0 && (!W || !x || ((q4 || i8) && !S))) return LIN_ERR_NULL;
     if (!aligned(y, 4)) return LIN_ERR_ALIGN;
     if (K > 0) {
         if (!aligned(W, 16) || !aligned(x, 16)) return LIN_ERR_ALIGN;
         if (kind == LIN_KIND_GEMV_Q4G64 && !aligned(S, 2)) return LIN_ERR_ALIGN;
         if (kind == LIN_KIND_SKINNY_Q4G64 && !aligned(S, 16)) return LIN_ERR_ALIGN;
+        if (i8 && !aligned(S, 4)) return LIN_ERR_ALIGN;
     }
     return LIN_OK;
 }
@@ -319,6 +326,11 @@ int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y, int64_t M, int6
     return run(LIN_KIND_SKINNY_BF16, W, nullptr, X, Y, M, N, K, stream);
 }
 
+int lin_gemv_i8(const void* Wq, const void* S, const void* x, float* y, int64_t M, int64_t N,
+                int64_t K, void* stream) {
+    return run(LIN_KIND_GEMV_I8, Wq, S, x, y, M, N, K, stream);
+}
+
 int lin_gemm_skinny_q4g64(const void* Wt, const void* St, const void* X, float* Y, int64_t M,
                           int64_t N, int64_t K, void* stream) {
     return run(LIN_KIND_SKINNY_Q4G64, Wt, St, X, Y, M, N, K, stream);
@@ -343,7 +355,7 @@ int lin_q4g64_tile(const void* Wq, const void* S, void* Wt, void* St, int64_t N,
 }
 
 int lin_num_candidates(int kind, int64_t M, int64_t N, int64_t K) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_Q4G64) return LIN_ERR_ARG;
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_GEMV_I8) return LIN_ERR_ARG;
     int st = check(kind, (void*)16, (void*)16, (void*)16, (float*)16, M, N, K);
     if (st < 0) return st;
     if (st > 0) return 0;
@@ -441,9 +453,18 @@ int lin_quantize_q4g64(const void* W, void* Wq, void* S, int64_t N, int64_t K, v
     return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
 }
 
+int lin_quantize_i8(const void* W, void* Wq, void* S, int64_t N, int64_t K, void* stream) {
+    if (N < 0 || K < 0 || N > 0x7FFFFFFF || K > LIN_MAX_K || K % 16) return LIN_ERR_SHAPE;
+    if (N == 0 || K == 0) return LIN_OK;
+    if (!W || !Wq || !S) return LIN_ERR_NULL;
+    if (!aligned(W, 16) || !aligned(Wq, 16) || !aligned(S, 4)) return LIN_ERR_ALIGN;
+    hipError_t e = launch_quantize_i8(W, Wq, S, (int)N, (int)K, (hipStream_t)stream);
+    return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
+}
+
 int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y, int64_t M,
                  int64_t N, int64_t K, void* stream, lin_config* out) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_Q4G64) return LIN_ERR_ARG;
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_GEMV_I8) return LIN_ERR_ARG;
     int st = check(kind, W, S, x, y, M, N, K);
     if (st < 0) return st;
     if (st > 0) return LIN_OK;
@@ -528,9 +549,10 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
 int lin_autotune_set(int kind, const void* const* W, const void* const* S, int count,
                      const void* x, float* y, int64_t M, int64_t N, int64_t K, void* stream,
                      lin_config* out) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_SKINNY_Q4G64) return LIN_ERR_ARG;
+    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_GEMV_I8) return LIN_ERR_ARG;
     if (count < 1) return LIN_ERR_ARG;
-    if (!W || ((kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64) && !S))
+    if (!W || ((kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64 ||
+                kind == LIN_KIND_GEMV_I8) && !S))
         return LIN_ERR_NULL;
     for (int j = 0; j < count; ++j) {
         const int st = check(kind, W[j], S ? S[j] : nullptr, x, y, M, N, K);

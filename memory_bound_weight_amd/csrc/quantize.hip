@@ -1,6 +1,7 @@
 // Load-time weight preparation for the int4-g64 format (tinyinfer post, TL;DR:
-// 4-bit weights plus one fp16 scale per 64), and the cache-flush kernel used
-// while tuning (a read sweep over a buffer larger than the caches).
+// 4-bit weights plus one fp16 scale per 64) and for INT8 with one fp32 scale
+// per output channel (TileInfer.jl post, INT8 section), and the cache-flush
+// kernel used while tuning (a read sweep over a buffer larger than the caches).
 //
 // One thread per (row, group of 64): a = max |w|; s = fp16 nearest to a/7
 // (ties to even, saturated at 65504); q = s > 0 ? clamp(rint(w/s), -8, 7) : 0
@@ -110,6 +111,63 @@ hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K,
     void* args[] = {(void*)&w, (void*)&wq, (void*)&s, (void*)&N, (void*)&K};
     return hipLaunchKernel((const void*)&quantize_q4g64_kernel, grid, dim3(256), args, 0, stream);
 }
+
+// INT8 with one fp32 scale per output channel, one workgroup per row:
+// a = max |w| over the row; s = fp32 nearest to a / 127 (the quotient formed in
+// fp64, then rounded once to fp32); q = s > 0 ? clamp(rint(w / s), -127, 127) : 0
+// with w / s in fp64 (TileInfer.jl post, INT8 section: scale = max|x| / 127,
+// every entry rounded to the nearest multiple of the scale).
+
+__global__ __launch_bounds__(256) void quantize_i8_kernel(const uint16_t* __restrict__ W,
+                                                          int8_t* __restrict__ Wq,
+                                                          float* __restrict__ S, int K) {
+    const int64_t n = blockIdx.x;
+    const uint16_t* row = W + n * (int64_t)K;
+    const int nun = K >> 3;   // 16-byte units of 8 weights
+    uint32_t amax = 0;        // |w| as bf16 bits: magnitude order = integer order
+    for (int i = threadIdx.x; i < nun; i += 256) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)row + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) amax = max(amax, max(v[j] & 0x7FFFu, (v[j] >> 16) & 0x7FFFu));
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = amax;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    const float s = (float)(bf16_to_f64(red[0]) / 127.0);
+    if (threadIdx.x == 0) S[n] = s;
+    const double sd = (double)s;
+    for (int i = threadIdx.x; i < nun; i += 256) {
+        const u32x4 v = __builtin_nontemporal_load((const u32x4*)row + i);
+        uint32_t out[2] = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                int q = 0;
+                if (s > 0.f) {
+                    double r = __builtin_rint(bf16_to_f64(h ? (v[j] >> 16) : (v[j] & 0xFFFFu)) / sd);
+                    r = r < -127.0 ? -127.0 : (r > 127.0 ? 127.0 : r);
+                    q = (int)r;
+                }
+                out[j >> 1] |= (uint32_t)(q & 0xFF) << (8 * (2 * (j & 1) + h));
+            }
+        *(uint2*)(Wq + n * (int64_t)K + 8 * i) = make_uint2(out[0], out[1]);
+    }
+}
+
+hipError_t launch_quantize_i8(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream) {
+    if (N == 0 || K == 0) return hipSuccess;
+    const uint16_t* w = (const uint16_t*)W;
+    int8_t* wq = (int8_t*)Wq;
+    float* s = (float*)S;
+    void* args[] = {(void*)&w, (void*)&wq, (void*)&s, (void*)&K};
+    return hipLaunchKernel((const void*)&quantize_i8_kernel, dim3((unsigned)N), dim3(256), args, 0, stream);
+}
+
 
 // Reads (does not write) the buffer: the caches end up full of clean lines, as
 // after other kernels' reads, with no dirty data whose write-back would slow

@@ -32,9 +32,11 @@ void register_gemv_q4g64(std::vector<Variant>& out);
 void register_gemm_mfma(std::vector<Variant>& out);
 void register_gemm_mfma_ring(std::vector<Variant>& out);
 void register_gemm_q4_ring(std::vector<Variant>& out);
+void register_gemv_i8(std::vector<Variant>& out);
 
-// Quantiser launch (int4-g64 weight preparation).
+// Quantiser launches (int4-g64 and INT8 weight preparation).
 hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream);
+hipError_t launch_quantize_i8(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream);
 
 // Matrix-core tiled int4-g64 layout: sizes and the rearrangement launch.
 void q4g64_tiled_bytes(int64_t N, int64_t K, int64_t* wt, int64_t* st);

@@ -46,6 +46,8 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_bf16", (P, P, P, 1, 1 << 31, 8, None), L.LIN_ERR_SHAPE),
     ("lin_gemv_bf16", (P, P, P, 1, 8, (1 << 22) + 8, None), L.LIN_ERR_SHAPE),
     ("lin_gemv_q4g64", (P, P, P, P, 1, 8, 96, None), L.LIN_ERR_SHAPE),
+    ("lin_gemv_i8", (P, P, P, P, 1, 8, 24, None), L.LIN_ERR_SHAPE),
+    ("lin_gemv_i8", (P, P, P, P, 9, 8, 32, None), L.LIN_ERR_SHAPE),
     ("lin_gemm_skinny_bf16", (P, P, P, 257, 8, 8, None), L.LIN_ERR_SHAPE),
     ("lin_gemm_skinny_q4g64", (P, P, P, P, 257, 8, 64, None), L.LIN_ERR_SHAPE),
     ("lin_gemm_skinny_q4g64", (P, P, P, P, 4, 8, 96, None), L.LIN_ERR_SHAPE),
@@ -53,6 +55,7 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_bf16", (None, None, None, 0, 8, 8, None), L.LIN_OK),
     ("lin_gemv_bf16", (None, None, None, 1, 0, 8, None), L.LIN_OK),
     ("lin_gemv_q4g64", (None, None, None, None, 0, 0, 64, None), L.LIN_OK),
+    ("lin_gemv_i8", (None, None, None, None, 0, 8, 32, None), L.LIN_OK),
     ("lin_gemm_skinny_bf16", (None, None, None, 0, 0, 0, None), L.LIN_OK),
     ("lin_gemm_skinny_q4g64", (None, None, None, None, 0, 8, 64, None), L.LIN_OK),
     # null pointers
@@ -60,6 +63,7 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_bf16", (None, P, P, 1, 8, 8, None), L.LIN_ERR_NULL),
     ("lin_gemv_bf16", (P, None, P, 1, 8, 8, None), L.LIN_ERR_NULL),
     ("lin_gemv_q4g64", (P, None, P, P, 1, 8, 64, None), L.LIN_ERR_NULL),
+    ("lin_gemv_i8", (P, None, P, P, 1, 8, 32, None), L.LIN_ERR_NULL),
     ("lin_gemm_skinny_bf16", (P, P, None, 4, 8, 8, None), L.LIN_ERR_NULL),
     ("lin_gemm_skinny_q4g64", (P, None, P, P, 4, 8, 64, None), L.LIN_ERR_NULL),
     # alignment
@@ -67,6 +71,8 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_bf16", (P, P + 2, P, 1, 8, 8, None), L.LIN_ERR_ALIGN),
     ("lin_gemv_bf16", (P, P, P + 2, 1, 8, 8, None), L.LIN_ERR_ALIGN),
     ("lin_gemv_q4g64", (P, P + 1, P, P, 1, 8, 64, None), L.LIN_ERR_ALIGN),
+    ("lin_gemv_i8", (P, P + 2, P, P, 1, 8, 32, None), L.LIN_ERR_ALIGN),
+    ("lin_gemv_i8", (P + 8, P, P, P, 1, 8, 32, None), L.LIN_ERR_ALIGN),
     ("lin_gemm_skinny_bf16", (P + 4, P, P, 4, 8, 8, None), L.LIN_ERR_ALIGN),
     ("lin_gemm_skinny_q4g64", (P, P + 2, P, P, 4, 8, 64, None), L.LIN_ERR_ALIGN),
     ("lin_gemm_skinny_q4g64", (P + 8, P, P, P, 4, 8, 64, None), L.LIN_ERR_ALIGN),
@@ -102,6 +108,17 @@ def test_tile_validation_and_sizes():
     assert L.lin_q4g64_tiled_size(0, 0) == (0, 0)
     with pytest.raises(L.LinError):
         L.lin_q4g64_tiled_size(8, 100)
+
+
+def test_quantize_i8_validation():
+    q = L._lib.lin_quantize_i8
+    assert q(P, P, P, 4, 24, None) == L.LIN_ERR_SHAPE
+    assert q(P, P, P, -1, 16, None) == L.LIN_ERR_SHAPE
+    assert q(None, None, None, 0, 16, None) == L.LIN_OK
+    assert q(None, P, P, 4, 16, None) == L.LIN_ERR_NULL
+    assert q(P + 8, P, P, 4, 16, None) == L.LIN_ERR_ALIGN
+    assert q(P, P + 8, P, 4, 16, None) == L.LIN_ERR_ALIGN
+    assert q(P, P, P + 2, 4, 16, None) == L.LIN_ERR_ALIGN
 
 
 def test_stream_read_validation():
@@ -142,7 +159,8 @@ def test_autotune_set_validation():
 def test_candidate_enumeration():
     for kind, M, N, K in [(0, 1, 2048, 2048), (0, 8, 512, 3584), (1, 1, 2048, 2048),
                           (1, 3, 512, 18944), (2, 8, 4096, 4096), (2, 17, 1024, 4096),
-                          (3, 1, 4096, 4096), (3, 64, 14336, 4096), (3, 256, 300, 4160)]:
+                          (3, 1, 4096, 4096), (3, 64, 14336, 4096), (3, 256, 300, 4160),
+                          (4, 1, 2048, 2048), (4, 8, 300, 4112)]:
         n = L.lin_num_candidates(kind, M, N, K)
         assert n > 0
         cands = L.lin_candidates(kind, M, N, K)

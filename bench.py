@@ -47,6 +47,11 @@ def bytes_q4(N, K, M=1):
     return N * K // 2 + N * K // 32 + 2 * M * K + 4 * M * N
 
 
+def bytes_i8(N, K, M=1):
+    """INT8: N*K code bytes + 4*N scale bytes (one fp32 per row), plus x and y."""
+    return N * K + 4 * N + 2 * M * K + 4 * M * N
+
+
 # ---------------------------------------------------------------- weight sets
 
 class Mat:
@@ -74,10 +79,14 @@ def build_set(model, fmt, dev, fused=True):
         if fmt == "bf16":
             m.W = W
             m.bytes = bytes_bf16(N, K)
-        else:
+        elif fmt == "q4":
             m.Wq, m.S = L.lin_quantize_q4g64(W)
             del W
             m.bytes = bytes_q4(N, K)
+        else:
+            m.Wq, m.S = L.lin_quantize_i8(W)
+            del W
+            m.bytes = bytes_i8(N, K)
         m.fmt = fmt
         mats.append(m)
     torch.cuda.synchronize()
@@ -87,12 +96,19 @@ def build_set(model, fmt, dev, fused=True):
 def launch(m):
     if m.fmt == "bf16":
         L.lin_gemv_bf16(m.W, m.x, m.y)
-    else:
+    elif m.fmt == "q4":
         L.lin_gemv_q4g64(m.Wq, m.S, m.x, m.y)
+    else:
+        L.lin_gemv_i8(m.Wq, m.S, m.x, m.y)
+
+
+KINDS = {"bf16": L.LIN_KIND_GEMV_BF16, "q4": L.LIN_KIND_GEMV_Q4G64, "i8": L.LIN_KIND_GEMV_I8}
+KERNEL_NAMES = {"bf16": "gemv_bf16", "q4": "gemv_q4g64", "i8": "gemv_i8"}
+FORMAT_NAMES = {"bf16": "bf16", "q4": "int4-g64", "i8": "INT8 (fp32 scale per row)"}
 
 
 def kind_of(m):
-    return L.LIN_KIND_GEMV_BF16 if m.fmt == "bf16" else L.LIN_KIND_GEMV_Q4G64
+    return KINDS[m.fmt]
 
 
 def tune_key(m):
@@ -114,7 +130,7 @@ def autotune(mats, only=None):
         if m.fmt == "bf16":
             cfg = L.lin_autotune_set(L.LIN_KIND_GEMV_BF16, [g.W for g in ms], m.x, m.y)
         else:
-            cfg = L.lin_autotune_set(L.LIN_KIND_GEMV_Q4G64, [g.Wq for g in ms], m.x, m.y,
+            cfg = L.lin_autotune_set(kind_of(m), [g.Wq for g in ms], m.x, m.y,
                                      Ss=[g.S for g in ms])
         seen[key] = cfg
         log("tuned %-5s %6d x %-6d over %d matrices -> %s" % (m.fmt, m.N, m.K, len(ms), cfg))
@@ -190,8 +206,8 @@ def time_graph(g, steps, warmup):
 
 def variant_key(m):
     c = L.lin_get_config(kind_of(m), 1, m.N, m.K)
-    return "%s R%d U%d S%d X%d" % ("gemv_bf16" if m.fmt == "bf16" else "gemv_q4g64",
-                                   c["rows"], c["unroll"], c["split"], c["stage_x"])
+    return "%s R%d U%d S%d X%d" % (KERNEL_NAMES[m.fmt], c["rows"], c["unroll"], c["split"],
+                                   c["stage_x"])
 
 
 def kernel_times(mats, reps):
@@ -429,9 +445,9 @@ def run_skinny(args, dev, fmt):
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(model, layers, threads):
+def cpu_baseline(model, layers, threads, fmts=("bf16", "q4")):
     """The oracle, as it stands, on the host cores: a bounded sample (the first
-    `layers` layers, bf16 and int4-g64), rows split over `threads` threads."""
+    `layers` layers, in the same formats), rows split over `threads` threads."""
     import oracle
     work = []
     for layer, idx, name, N, K in synth.decode_matrices(model):
@@ -439,17 +455,24 @@ def cpu_baseline(model, layers, threads):
             continue
         W = synth.bits(synth.weight(model["seed"], layer, idx, N, K))
         x = synth.bits(synth.activation(model["seed"], layer, idx, 1, K))
-        Wq, S = oracle.quantize_q4g64(W)
-        work.append(("bf16", W, None, x, bytes_bf16(N, K)))
-        work.append(("q4", Wq, S, x, bytes_q4(N, K)))
+        if "bf16" in fmts:
+            work.append(("bf16", W, None, x, bytes_bf16(N, K)))
+        if "q4" in fmts:
+            Wq, S = oracle.quantize_q4g64(W)
+            work.append(("q4", Wq, S, x, bytes_q4(N, K)))
+        if "i8" in fmts:
+            Wq, S = oracle.quantize_i8(W)
+            work.append(("i8", Wq, S, x, bytes_i8(N, K)))
     total_bytes = sum(w[4] for w in work)
 
     def run_rows(item, lo, hi):
         fmt, A, S, x, _ = item
         if fmt == "bf16":
             oracle.gemm_dense(A[lo:hi], x)
-        else:
+        elif fmt == "q4":
             oracle.gemm_q4g64(A[lo:hi], S[lo:hi], x)
+        else:
+            oracle.gemm_i8(A[lo:hi], S[lo:hi], x)
 
     jobs = []
     for item in work:
@@ -462,9 +485,10 @@ def cpu_baseline(model, layers, threads):
     dt = time.perf_counter() - t0
     return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "%s layers 0-%d (%d matrices), bf16 and int4-g64, %.1f MB of weights, "
+            "sample": "%s layers 0-%d (%d matrices), %s, %.1f MB of weights, "
                       "batch 1, fp64 sequential sums, %.2f s wall"
-                      % (model["name"], layers - 1, len(work) // 2, total_bytes / 1e6, dt)}
+                      % (model["name"], layers - 1, len(work) // len(fmts),
+                         " and ".join(FORMAT_NAMES[f] for f in fmts), total_bytes / 1e6, dt)}
 
 
 def cpu_baseline_skinny(threads, fmt="bf16", rows=96):
@@ -506,6 +530,9 @@ def main():
     ap.add_argument("--tune", action="store_true",
                     help="re-run lin_autotune for every shape and rewrite the tuning table")
     ap.add_argument("--tuning", default=None, help="tuning table path")
+    ap.add_argument("--formats", default="bf16,q4",
+                    help="weight formats of the decode-step workloads, in step order: any of "
+                         "bf16, q4 (int4-g64), i8 (INT8, fp32 scale per row)")
     ap.add_argument("--no-fuse", action="store_true",
                     help="one launch per matrix instead of q|k|v and gate|up concatenated")
     ap.add_argument("--cpu-layers", type=int, default=16)
@@ -536,9 +563,15 @@ def main():
     model = synth.TINYLLAMA if args.workload == "tinyllama" else synth.QWEN7B
     log("building %s weight sets on %s" % (model["name"], torch.cuda.get_device_name(dev)))
     fused = not args.no_fuse
-    sets = {f: build_set(model, f, dev, fused) for f in ("bf16", "q4")}
-    allm = sets["bf16"] + sets["q4"]
-    tfile = args.tuning or os.path.join(L.TUNING_DIR, "%s.json" % model["name"])
+    fmts = [f.strip() for f in args.formats.split(",") if f.strip()]
+    if not fmts or any(f not in KINDS for f in fmts) or len(set(fmts)) != len(fmts):
+        print("--formats takes distinct entries of bf16, q4, i8", file=sys.stderr)
+        sys.exit(2)
+    sets = {f: build_set(model, f, dev, fused) for f in fmts}
+    allm = [m for f in fmts for m in sets[f]]
+    default_fmts = fmts == ["bf16", "q4"]
+    tname = model["name"] + ("" if default_fmts else "-" + "-".join(fmts))
+    tfile = args.tuning or os.path.join(L.TUNING_DIR, "%s.json" % tname)
     tuning = apply_tuning(allm, tfile, args.tune)
     log("tuning: " + tuning)
 
@@ -548,15 +581,15 @@ def main():
     # one kernel per (fused) matrix, each format's step captured as one graph
     graphs = {f: capture(sets[f]) for f in sets}
     per_fmt = {}
-    for f in ("bf16", "q4"):
+    for f in fmts:
         _, gpu_f = time_graph(graphs[f], max(5, args.steps // 2), args.warmup)
         per_fmt[f] = {"ms_per_token": round(gpu_f * 1e3, 4), "equiv_tok_s": round(1.0 / gpu_f, 1),
                       "GB_s": round(fmt_bytes[f] / gpu_f / 1e9, 1), "bytes": fmt_bytes[f]}
         log("%s step: %.1f us, %.1f GB/s, %.0f tok/s" % (f, gpu_f * 1e6, fmt_bytes[f] / gpu_f / 1e9,
                                                         1 / gpu_f))
-    # the timed region: K steps of the whole path (bf16 step, then int4 step)
+    # the timed region: K steps of the whole path (one decode pass per format, in order)
     torch.cuda.synchronize()
-    wall, gpu = time_runs([graphs["bf16"].replay, graphs["q4"].replay], args.steps, args.warmup)
+    wall, gpu = time_runs([graphs[f].replay for f in fmts], args.steps, args.warmup)
     gbs = step_bytes / wall / 1e9
 
     kt = kernel_times(allm, reps=max(5, args.steps // 2))
@@ -582,9 +615,11 @@ def main():
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall * 1e3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16 and int4-g64 weights, bf16 x, fp32 accumulate", "data": "synthetic",
-           "config": {"workload": "%s decode weight set, batch 1, bf16 + int4-g64 (%d matrices "
-                      "each%s)" % (model["name"], len(synth.decode_groups(model, False)),
+           "dtype": "%s weights, bf16 x, fp32 accumulate" % " and ".join(FORMAT_NAMES[f] for f in fmts),
+           "data": "synthetic",
+           "config": {"workload": "%s decode weight set, batch 1, %s (%d matrices "
+                      "each%s)" % (model["name"], " + ".join(FORMAT_NAMES[f] for f in fmts),
+                                   len(synth.decode_groups(model, False)),
                                    ", q|k|v and gate|up concatenated at load" if fused else ""),
                       "batch": 1, "launches_per_step": len(allm), "bytes_per_step": step_bytes,
                       "fused_projections": fused, "tuning": tuning},
@@ -592,7 +627,7 @@ def main():
            "gpu_ms_per_step": round(gpu * 1e3, 4),
            "per_format": per_fmt, "kernels": kernels, "roofline": roofline}
     if not args.skip_cpu:
-        out["cpu_baseline"] = cpu_baseline(model, args.cpu_layers, min(16, os.cpu_count() or 1))
+        out["cpu_baseline"] = cpu_baseline(model, args.cpu_layers, min(16, os.cpu_count() or 1), fmts)
     print(json.dumps(out), flush=True)
 
 

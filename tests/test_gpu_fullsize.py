@@ -80,8 +80,50 @@ def test_single_gemv_full_oracle():
     assert_within_bound(y, Y, B, "single 2048x2048")
 
 
+@pytest.mark.parametrize("model", [synth.TINYLLAMA, synth.QWEN7B], ids=lambda m: m["name"])
+def test_decode_shapes_int8_sampled(model):
+    _tuned(model["name"] + "-i8")
+    for N, K in _shapes(model):
+        print("case fullsize i8 %s %dx%d" % (model["name"], N, K), flush=True)
+        W = synth.weight(model["seed"], 0, 98, N, K, device=DEV)
+        x = synth.activation(model["seed"], 0, 98, 1, K, device=DEV)
+        rows = _sample_rows(N)
+        idx = torch.from_numpy(rows).to(DEV)
+        Wr = u16(W[idx])
+        Wq, S = L.lin_quantize_i8(W)
+        y = L.lin_gemv_i8(Wq, S, x)
+        torch.cuda.synchronize()
+        Wq_o, S_o = oracle.quantize_i8(Wr)
+        assert np.array_equal(Wq[idx].cpu().numpy(), Wq_o)
+        assert np.array_equal(S[idx].cpu().numpy().view(np.uint32), S_o.view(np.uint32))
+        Y, B = oracle.gemm_i8(Wq_o, S_o, u16(x))
+        assert_within_bound(y[:, idx], Y, B, "i8 %dx%d" % (N, K))
+        del W, Wq, S
+
+
+@pytest.mark.parametrize("M", list(synth.MISTRAL_M))
+def test_mistral_skinny_q4_sampled(M):
+    _tuned("mistral-7b-skinny-q4")
+    for N, K in synth.MISTRAL_SHAPES:
+        print("case skinny q4 full M=%d %dx%d" % (M, N, K), flush=True)
+        W = synth.weight(synth.MISTRAL_SEED, 0, N, N, K, device=DEV)
+        X = synth.activation(synth.MISTRAL_SEED, 0, N, M, K, device=DEV)
+        Wq, S = L.lin_quantize_q4g64(W)
+        T = L.lin_q4g64_tile(Wq, S)
+        Y = L.lin_gemm_skinny_q4g64(T, X)
+        torch.cuda.synchronize()
+        rows = _sample_rows(N, k=12 if M == 256 else 24)
+        idx = torch.from_numpy(rows).to(DEV)
+        Wq_o, S_o = oracle.quantize_q4g64(u16(W[idx]))
+        assert np.array_equal(Wq[idx].cpu().numpy(), Wq_o)
+        Yo, Bo = oracle.gemm_q4g64(Wq_o, S_o, u16(X))
+        assert_within_bound(Y[:, idx], Yo, Bo, "skinny q4 M=%d %dx%d" % (M, N, K))
+        del W, Wq, S, T
+
+
 @pytest.mark.parametrize("M", list(synth.MISTRAL_M))
 def test_mistral_skinny_sampled(M):
+    _tuned("mistral-7b-skinny")
     for N, K in synth.MISTRAL_SHAPES:
         print("case skinny full M=%d %dx%d" % (M, N, K), flush=True)
         W = synth.weight(synth.MISTRAL_SEED, 0, N, N, K, device=DEV)
@@ -108,3 +150,13 @@ def test_maximum_k():
         Wq_o, S_o = oracle.quantize_q4g64(u16(W))
         Y4, B4 = oracle.gemm_q4g64(Wq_o, S_o, u16(x))
         assert_within_bound(y4, Y4, B4, "int4 K=2^22")
+        # INT8 and the tiled int4 batched product at the same K
+        Wi, Si = L.lin_quantize_i8(W)
+        yi = L.lin_gemv_i8(Wi, Si, x)
+        T = L.lin_q4g64_tile(Wq, S)
+        yt = L.lin_gemm_skinny_q4g64(T, x)
+        torch.cuda.synchronize()
+        Wi_o, Si_o = oracle.quantize_i8(u16(W))
+        Yi, Bi = oracle.gemm_i8(Wi_o, Si_o, u16(x))
+        assert_within_bound(yi, Yi, Bi, "i8 K=2^22")
+        assert_within_bound(yt, Y4, B4, "skinny q4 K=2^22")

@@ -23,5 +23,7 @@ from .oracle import (  # noqa: F401
     open_lib,
     quantize_i8,
     quantize_q4g64,
+    residual_add,
+    swiglu,
     use,
 )

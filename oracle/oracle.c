@@ -20,6 +20,10 @@
  *    two codes per byte along k.
  *  - "llm-rs" (roofline essay), section 5 "Batching moves decode from memory toward
  *    math": a batch of M tokens multiplies the same weights, i.e. Y = X . W^T.
+ *  - yalm post, GPU matmul section (fusing): the product with the residual add
+ *    accumulated into its destination, and Mistral's gated product
+ *    silu(w1(x)) * w3(x) computed by the kernel that forms both products; silu
+ *    is the sigmoid-weighted linear unit, silu(g) = g / (1 + exp(-g)).
  *  - TileInfer.jl post, "Pushing further with cheating: INT8 quantization":
  *    symmetric INT8 in -127..127 with one Float32 scale per output channel,
  *    scale = max|w| / 127, every weight rounded to the nearest multiple of the
@@ -274,4 +278,16 @@ void orc_gemm_i8(const int8_t* Wq, const float* S, const uint16_t* X, int64_t M,
             if (B) B[m * N + n] = fabs((double)S[n]) * mag;
         }
     }
+}
+
+/* ---- fused epilogues ------------------------------------------------------ */
+
+/* H[i] = silu(G[i]) * U[i] with silu(g) = g / (1 + exp(-g)), in fp64. */
+void orc_swiglu(const double* G, const double* U, int64_t n, double* H) {
+    for (int64_t i = 0; i < n; ++i) H[i] = G[i] / (1.0 + exp(-G[i])) * U[i];
+}
+
+/* Y[i] = P[i] + R[i]: a product plus the residual it is accumulated into. */
+void orc_residual_add(const double* P, const float* R, int64_t n, double* Y) {
+    for (int64_t i = 0; i < n; ++i) Y[i] = P[i] + (double)R[i];
 }

@@ -75,6 +75,10 @@ def open_lib(path):
     lib.orc_dequant_i8.restype = None
     lib.orc_gemm_i8.argtypes = [P, P, P, I64, I64, I64, P, P]
     lib.orc_gemm_i8.restype = None
+    lib.orc_swiglu.argtypes = [P, P, I64, P]
+    lib.orc_swiglu.restype = None
+    lib.orc_residual_add.argtypes = [P, P, I64, P]
+    lib.orc_residual_add.restype = None
     return lib
 
 
@@ -223,3 +227,27 @@ def gemm_i8(Wq, S, X):
     B = np.empty((M, N), dtype=np.float64)
     lib.orc_gemm_i8(_ptr(Wq), _ptr(S), _ptr(X), M, N, K, _ptr(Y), _ptr(B))
     return Y, B
+
+
+def swiglu(G, U):
+    """silu(G) * U elementwise in fp64 (any shape, same shapes)."""
+    lib = load()
+    G = _c(np.asarray(G, dtype=np.float64), np.float64)
+    U = _c(np.asarray(U, dtype=np.float64), np.float64)
+    if G.shape != U.shape:
+        raise ValueError("shape mismatch")
+    H = np.empty(G.shape, dtype=np.float64)
+    lib.orc_swiglu(_ptr(G), _ptr(U), G.size, _ptr(H))
+    return H
+
+
+def residual_add(P, R):
+    """P (fp64) + R (fp32 residual), elementwise, same shapes."""
+    lib = load()
+    P = _c(np.asarray(P, dtype=np.float64), np.float64)
+    R = _c(R, np.float32)
+    if P.shape != R.shape:
+        raise ValueError("shape mismatch")
+    Y = np.empty(P.shape, dtype=np.float64)
+    lib.orc_residual_add(_ptr(P), _ptr(R), P.size, _ptr(Y))
+    return Y

@@ -128,3 +128,4 @@ def test_product_equals_dense_product_on_dequantised_weights():
     Yd, Bd = oracle.gemm_f64w(oracle.dequant_i8(Wq, S), X)
     assert np.allclose(Y8, Yd, rtol=0, atol=1e-12 * Bd.max())
     assert np.allclose(B8, Bd, rtol=1e-14)
+

@@ -1,7 +1,7 @@
 """The oracle's pins must catch plausible mistakes.  Each case below compiles a
 copy of oracle.c with one planted mistake (on the CPU, in a temporary
-directory) and checks that at least one pin in test_oracle.py or
-test_oracle_i8.py fails on it."""
+directory) and checks that at least one pin in test_oracle.py,
+test_oracle_i8.py or test_oracle_epilogue.py fails on it."""
 import os
 import subprocess
 import tempfile
@@ -10,6 +10,7 @@ import pytest
 
 import oracle
 import test_oracle as pins
+import test_oracle_epilogue as pins_ep
 import test_oracle_i8 as pins_i8
 
 SRC = oracle.oracle.SRC_PATH
@@ -56,11 +57,14 @@ MUTATIONS = [
     ("i8-scale-not-applied", "Y[m * N + n] = (double)S[n] * acc;", "Y[m * N + n] = acc;"),
     ("i8-unsigned-codes", "double p = (double)Wq[n * K + k] * orc_bf16_value",
      "double p = (double)(uint8_t)Wq[n * K + k] * orc_bf16_value"),
+    ("silu-sign", "H[i] = G[i] / (1.0 + exp(-G[i])) * U[i];", "H[i] = G[i] / (1.0 + exp(G[i])) * U[i];"),
+    ("silu-missing-gate", "H[i] = G[i] / (1.0 + exp(-G[i])) * U[i];", "H[i] = 1.0 / (1.0 + exp(-G[i])) * U[i];"),
+    ("residual-dropped", "Y[i] = P[i] + (double)R[i];", "Y[i] = P[i];"),
     ("i8-dequant-scale-index", "Wd[n * K + k] = (double)Wq[n * K + k] * (double)S[n];",
      "Wd[n * K + k] = (double)Wq[n * K + k] * (double)S[k % N];"),
 ]
 
-PIN_FUNCS = [getattr(m, n) for m in (pins, pins_i8) for n in dir(m) if n.startswith("test_")]
+PIN_FUNCS = [getattr(m, n) for m in (pins, pins_i8, pins_ep) for n in dir(m) if n.startswith("test_")]
 
 
 def _run_pins():

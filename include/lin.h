@@ -25,7 +25,8 @@
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points
- * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemv_i8, lin_gemm_skinny_bf16,
+ * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemv_bf16_ep, lin_gemv_q4g64_ep, lin_gemv_i8,
+ * lin_gemm_skinny_bf16,
  * lin_gemm_skinny_q4g64, lin_quantize_q4g64, lin_quantize_i8, lin_q4g64_tile)
  * validate their arguments in O(1), enqueue kernels on `stream` (a hipStream_t;
  * NULL = the null stream) and return without waiting: they never allocate,
@@ -120,6 +121,30 @@ int lin_gemv_bf16(const void* W, const void* x, float* y,
  * K % 64 == 0, 1 <= M <= LIN_GEMV_MAX_M. */
 int lin_gemv_q4g64(const void* Wq, const void* S, const void* x, float* y,
                    int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Epilogues fused into the batch-1 products (yalm post, GPU matmul section:
+ * the residual add accumulated into the product's destination, and the gated
+ * product silu(w1 x) * w3 x formed by the kernel that computes both products). */
+typedef enum lin_epilogue {
+    LIN_EPI_NONE = 0,    /* y = W x */
+    LIN_EPI_ADD = 1,     /* y = W x + r; r fp32 [1][N], may be y itself (accumulate in place) */
+    LIN_EPI_SWIGLU = 2   /* W has 2N rows, gate rows 0..N-1 then up rows N..2N-1 (as
+                            concatenated at load); y[n] = silu(g_n) * u_n with g = W[0:N] x,
+                            u = W[N:2N] x and silu(g) = g / (1 + exp(-g)); r unused */
+} lin_epilogue;
+
+/* lin_gemv_bf16 / lin_gemv_q4g64 for M == 1 with a fused epilogue.  N counts
+ * the outputs (the weight matrix has 2N rows for LIN_EPI_SWIGLU).  The
+ * configuration is the one tuned or pinned for the plain product of the same
+ * weight matrix, i.e. (kind, 1, 2N or N, K).  Error bound per output: for ADD,
+ * 1e-3 * (sum_k |W x| + |r|); for SWIGLU, the GEMV bound propagated through
+ * silu(g) u (1e-3 * (1.1 |u| sum_k |W_g x| + |silu(g)| sum_k |W_u x|)) plus a few
+ * fp32 rounding steps of |y|.  M != 1 returns LIN_ERR_SHAPE; ADD with a NULL r
+ * LIN_ERR_NULL; an unknown epilogue LIN_ERR_ARG. */
+int lin_gemv_bf16_ep(const void* W, const void* x, float* y,
+                     int64_t M, int64_t N, int64_t K, int epilogue, const float* r, void* stream);
+int lin_gemv_q4g64_ep(const void* Wq, const void* S, const void* x, float* y,
+                      int64_t M, int64_t N, int64_t K, int epilogue, const float* r, void* stream);
 
 /* The same product with INT8 weights and one fp32 scale per output channel
  * (TileInfer.jl post, "Pushing further with cheating: INT8 quantization": the

@@ -30,6 +30,10 @@ LIN_KIND_SKINNY_BF16 = 2
 LIN_KIND_SKINNY_Q4G64 = 3
 LIN_KIND_GEMV_I8 = 4
 
+LIN_EPI_NONE = 0
+LIN_EPI_ADD = 1
+LIN_EPI_SWIGLU = 2
+
 LIN_ALGO_VALU = 1
 LIN_ALGO_MFMA = 2
 
@@ -37,7 +41,8 @@ LIN_GEMV_MAX_M = 8
 LIN_SKINNY_MAX_M = 256
 
 # Every symbol include/lin.h declares.
-EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemv_i8", "lin_gemm_skinny_bf16",
+EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemv_bf16_ep", "lin_gemv_q4g64_ep",
+           "lin_gemv_i8", "lin_gemm_skinny_bf16",
            "lin_gemm_skinny_q4g64", "lin_quantize_i8",
            "lin_q4g64_tiled_size", "lin_q4g64_tile", "lin_autotune",
            "lin_autotune_set", "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
@@ -78,6 +83,8 @@ def _load():
         "lin_gemv_bf16": [P, P, P, I64, I64, I64, P],
         "lin_gemv_q4g64": [P, P, P, P, I64, I64, I64, P],
         "lin_gemv_i8": [P, P, P, P, I64, I64, I64, P],
+        "lin_gemv_bf16_ep": [P, P, P, I64, I64, I64, I, P, P],
+        "lin_gemv_q4g64_ep": [P, P, P, P, I64, I64, I64, I, P, P],
         "lin_quantize_i8": [P, P, P, I64, I64, P],
         "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
         "lin_gemm_skinny_q4g64": [P, P, P, P, I64, I64, I64, P],
@@ -177,6 +184,52 @@ def lin_gemv_q4g64(Wq, S, x, y=None):
     y = _out(y, M, N, Wq.device)
     _check(_lib.lin_gemv_q4g64(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(),
                                M, N, K, _stream(Wq)), "lin_gemv_q4g64")
+    return y
+
+
+def _epi_out(epilogue, NW, r, y, dev):
+    if epilogue not in (LIN_EPI_NONE, LIN_EPI_ADD, LIN_EPI_SWIGLU):
+        raise ValueError("unknown epilogue %r" % (epilogue,))
+    N = NW // 2 if epilogue == LIN_EPI_SWIGLU else NW
+    if epilogue == LIN_EPI_SWIGLU and NW % 2:
+        raise ValueError("the gated product needs an even number of weight rows")
+    if epilogue == LIN_EPI_ADD:
+        _need(r, torch.float32, "r", 2)
+        if tuple(r.shape) != (1, N):
+            raise ValueError("r must have shape (1, %d)" % N)
+    return N, _out(y, 1, N, dev)
+
+
+def lin_gemv_bf16_ep(W, x, epilogue, r=None, y=None):
+    """Batch-1 bf16 product with a fused epilogue: LIN_EPI_ADD (y = W x + r, r may
+    be y) or LIN_EPI_SWIGLU (W has 2N rows: y = silu(W[:N] x) * W[N:] x)."""
+    x = _as2d(x)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    NW, K = W.shape
+    if x.shape != (1, K):
+        raise ValueError("x must be one token of K = %d" % K)
+    N, y = _epi_out(epilogue, NW, r, y, W.device)
+    _check(_lib.lin_gemv_bf16_ep(W.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, K, int(epilogue),
+                                 r.data_ptr() if r is not None else None, _stream(W)),
+           "lin_gemv_bf16_ep")
+    return y
+
+
+def lin_gemv_q4g64_ep(Wq, S, x, epilogue, r=None, y=None):
+    """Batch-1 int4-g64 product with a fused epilogue (see lin_gemv_bf16_ep)."""
+    x = _as2d(x)
+    _need(Wq, torch.uint8, "Wq", 2)
+    _need(S, torch.float16, "S", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    NW, K2 = Wq.shape
+    K = 2 * K2
+    if x.shape != (1, K) or tuple(S.shape) != (NW, K // 64):
+        raise ValueError("shape mismatch: Wq [N, K/2], S [N, K/64], x [1, K]")
+    N, y = _epi_out(epilogue, NW, r, y, Wq.device)
+    _check(_lib.lin_gemv_q4g64_ep(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, K,
+                                  int(epilogue), r.data_ptr() if r is not None else None,
+                                  _stream(Wq)), "lin_gemv_q4g64_ep")
     return y
 
 

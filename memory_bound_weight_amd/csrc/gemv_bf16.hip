@@ -5,9 +5,9 @@
 
 namespace lin {
 
-template <int MT, int R, int U, int SPLIT, bool STAGE>
+template <int MT, int R, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
 __global__ __launch_bounds__(kBlock) void gemv_bf16_valu(KArgs a) {
-    gemv_bf16_valu_block<MT, R, U, SPLIT, STAGE>(a, blockIdx.x);
+    gemv_bf16_valu_block<MT, R, U, SPLIT, STAGE, EPI>(a, blockIdx.x);
 }
 
 template <int MT, int R, int U, int SPLIT, bool STAGE>
@@ -36,7 +36,12 @@ static void add(std::vector<Variant>& out) {
     v.geometry = &geom_bf16<MT, R, U, SPLIT, STAGE>;
     if (MT <= LIN_GEMV_MAX_M) {
         v.kind = LIN_KIND_GEMV_BF16;
+        if constexpr (MT == 1) {
+            v.epi[kEpiAdd] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
+            v.epi[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu>;
+        }
         out.push_back(v);
+        v.epi[kEpiAdd] = v.epi[kEpiSwiglu] = nullptr;
     }
     v.kind = LIN_KIND_SKINNY_BF16;
     out.push_back(v);

@@ -17,6 +17,13 @@
 // of the first weight stage).
 // Products use v_dot2_f32_bf16 (two exact bf16 products per instruction, fp32
 // sums); each lane sums K/512 chunks, then a permlane/DPP tree sums the lanes.
+//
+// Epilogues (EPI, yalm post, GPU matmul section: fold the next elementwise
+// step into the product that feeds it): kEpiAdd writes y = W x + r (the
+// residual add, r may be y itself); kEpiSwiglu reads a weight matrix of 2N
+// rows (gate rows, then up rows, as concatenated at load), gives each
+// wavefront the R gate rows and the R matching up rows, and writes
+// y[n] = silu(g_n) u_n, so the gated activation never makes a round trip.
 #pragma once
 
 #include <type_traits>
@@ -26,9 +33,10 @@
 namespace lin {
 
 // One row block (R x 4/SPLIT rows) of the product, one per workgroup.
-template <int MT, int R, int U, int SPLIT, bool STAGE>
+template <int MT, int R0, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
 __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t block) {
     constexpr int GROUPS = 4 / SPLIT;
+    constexpr int R = EPI == kEpiSwiglu ? 2 * R0 : R0;   // weight rows per wavefront
     constexpr int V = R * MT;
     constexpr int STEP = kWave * U;   // chunks per pipeline step
     const int lane = threadIdx.x & 63;
@@ -43,12 +51,13 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
     extern __shared__ u32x4 xs[];   // STAGE: [MT][nch] chunks of x
     if constexpr (STAGE) stage_x_dma(X, M, MT, K, xs);
 
-    const int64_t row0 = (block * GROUPS + grp) * R;
+    const int64_t row0 = (block * GROUPS + grp) * R0;   // first output row
     const uint8_t* wb[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        int64_t row = row0 + r;
+        int64_t row = row0 + r % R0;
         row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
+        if (r >= R0) row += N;         // the up row of a gated product
         wb[r] = (const uint8_t*)(W + row * (int64_t)K);
     }
     const uint8_t* xb[MT];
@@ -145,10 +154,29 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
     }
 
     wave_reduce<V>(acc);
-    if constexpr (SPLIT == 1) {
+    if constexpr (EPI == kEpiSwiglu) {
+        // gate and up totals land in different lanes: meet in LDS
+        __shared__ float red[4][V];
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) { red[wave][idx] = val; });
+        __syncthreads();
+        if (part == 0) {
+            for (int j = lane; j < R0 * MT; j += kWave) {
+                const int r = j / MT, m = j - (j / MT) * MT;
+                float g = red[wave][j], u = red[wave][R0 * MT + j];
+#pragma unroll
+                for (int p = 1; p < SPLIT; ++p) {
+                    g += red[wave + p][j];
+                    u += red[wave + p][R0 * MT + j];
+                }
+                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = silu_mul(g, u);
+            }
+        }
+        __syncthreads();
+    } else if constexpr (SPLIT == 1) {
         for_each_reduced<V>(acc, lane, [&](int idx, float val) {
             const int r = idx / MT, m = idx - (idx / MT) * MT;
-            if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = val;
+            const int64_t o = (int64_t)m * N + row0 + r;
+            if (m < M && row0 + r < N) a.Y[o] = EPI == kEpiAdd ? val + a.R[o] : val;
         });
     } else {
         __shared__ float red[4][V];
@@ -160,7 +188,8 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
                 float s = red[wave][idx];
 #pragma unroll
                 for (int p = 1; p < SPLIT; ++p) s += red[wave + p][idx];
-                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = s;
+                const int64_t o = (int64_t)m * N + row0 + r;
+                if (m < M && row0 + r < N) a.Y[o] = EPI == kEpiAdd ? s + a.R[o] : s;
             });
         }
         __syncthreads();

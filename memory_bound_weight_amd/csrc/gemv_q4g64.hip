@@ -5,9 +5,9 @@
 
 namespace lin {
 
-template <int MT, int R, int U, int SPLIT, bool STAGE>
+template <int MT, int R, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
 __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
-    gemv_q4_valu_block<MT, R, U, SPLIT, STAGE>(a, blockIdx.x);
+    gemv_q4_valu_block<MT, R, U, SPLIT, STAGE, EPI>(a, blockIdx.x);
 }
 
 template <int MT, int R, int U, int SPLIT, bool STAGE>
@@ -35,6 +35,10 @@ static void add(std::vector<Variant>& out) {
     v.min_m = MT / 2 + 1;
     v.func = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE>;
     v.geometry = &geom_q4<MT, R, U, SPLIT, STAGE>;
+    if constexpr (MT == 1) {
+        v.epi[kEpiAdd] = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
+        v.epi[kEpiSwiglu] = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu>;
+    }
     out.push_back(v);
 }
 

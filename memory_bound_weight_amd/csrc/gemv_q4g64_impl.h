@@ -29,6 +29,9 @@
 // into [MT][4][chunks] 16-byte words (bank-conflict-free reads) plus the
 // chunk sums, and then reads x from LDS; all of this overlaps the latency of
 // the first weight stage.
+//
+// Epilogues (EPI) as in the bf16 kernel: the residual add, or the gated
+// product silu(g) u over a matrix of 2N rows (gate rows, then up rows).
 #pragma once
 
 #include <type_traits>
@@ -110,9 +113,10 @@ __host__ __device__ inline size_t q4_stage_bytes(int MT, int K) {
 }
 
 // One row block (R x 4/SPLIT rows) of the product, one per workgroup.
-template <int MT, int R, int U, int SPLIT, bool STAGE>
+template <int MT, int R0, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
 __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block) {
     constexpr int GROUPS = 4 / SPLIT;
+    constexpr int R = EPI == kEpiSwiglu ? 2 * R0 : R0;   // weight rows per wavefront
     constexpr int V = R * MT;
     constexpr int STEP = kWave * U;   // chunks per pipeline step
     const int lane = threadIdx.x & 63;
@@ -133,13 +137,14 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
     u32x4* xraw = xs + q4_stage_raw_offset(MT, K);
     if constexpr (STAGE) stage_x_dma(X, M, MT, K, xraw);
 
-    const int64_t row0 = (block * GROUPS + grp) * R;
+    const int64_t row0 = (block * GROUPS + grp) * R0;   // first output row
     const uint8_t* wb[R];
     const uint8_t* sb[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        int64_t row = row0 + r;
+        int64_t row = row0 + r % R0;
         row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
+        if (r >= R0) row += N;         // the up row of a gated product
         wb[r] = Wq + row * (int64_t)(K / 2);
         sb[r] = (const uint8_t*)(S + row * (int64_t)G);
     }
@@ -261,10 +266,28 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
     }
 
     wave_reduce<V>(acc);
-    if constexpr (SPLIT == 1) {
+    if constexpr (EPI == kEpiSwiglu) {
+        // gate and up totals land in different lanes: meet in LDS
+        __shared__ float red[4][V];
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) { red[wave][idx] = val; });
+        __syncthreads();
+        if (part == 0) {
+            for (int j = lane; j < R0 * MT; j += kWave) {
+                const int r = j / MT, m = j - (j / MT) * MT;
+                float g = red[wave][j], u = red[wave][R0 * MT + j];
+#pragma unroll
+                for (int p = 1; p < SPLIT; ++p) {
+                    g += red[wave + p][j];
+                    u += red[wave + p][R0 * MT + j];
+                }
+                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = silu_mul(g, u);
+            }
+        }
+    } else if constexpr (SPLIT == 1) {
         for_each_reduced<V>(acc, lane, [&](int idx, float val) {
             const int r = idx / MT, m = idx - (idx / MT) * MT;
-            if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = val;
+            const int64_t o = (int64_t)m * N + row0 + r;
+            if (m < M && row0 + r < N) a.Y[o] = EPI == kEpiAdd ? val + a.R[o] : val;
         });
     } else {
         __shared__ float red[4][V];
@@ -276,7 +299,8 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
                 float s = red[wave][idx];
 #pragma unroll
                 for (int p = 1; p < SPLIT; ++p) s += red[wave + p][idx];
-                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = s;
+                const int64_t o = (int64_t)m * N + row0 + r;
+                if (m < M && row0 + r < N) a.Y[o] = EPI == kEpiAdd ? s + a.R[o] : s;
             });
         }
     }

@@ -18,7 +18,14 @@ struct KArgs {
     int M, N, K;
     int splits;      // split-K factor (matrix-core path), 1 otherwise
     void* ws;        // split-K workspace: tile counters, then partial tiles
+    const float* R;  // residual fp32 [M][N] of the add epilogue (may equal Y)
 };
+
+// Epilogues of the batch-1 products (the values of lin_epilogue).
+constexpr int kEpiNone = 0, kEpiAdd = 1, kEpiSwiglu = 2;
+
+// silu(g) * u, silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.f + expf(-g)) * u; }
 
 constexpr int kWave = 64;
 constexpr int kBlock = 256;   // four wavefronts per workgroup

@@ -201,26 +201,29 @@ int ensure_workspace(int dev, size_t bytes) {
 
 // Dynamic LDS above the default 64 KB per workgroup must be allowed per
 // kernel first; the largest size allowed so far is kept per variant.
-bool allow_lds(int vi, size_t lds) {
+bool allow_lds(int vi, size_t lds, const void* func = nullptr) {
     if (lds <= 64 * 1024) return true;
-    static auto* allowed = new std::vector<size_t>(registry().size(), 64 * 1024);
+    const Variant& v = registry()[vi];
+    if (!func) func = v.func;
+    const int e = func == v.epi[kEpiAdd] ? kEpiAdd : (func == v.epi[kEpiSwiglu] ? kEpiSwiglu : 0);
+    static auto* allowed = new std::vector<size_t>(registry().size() * 3, 64 * 1024);
     std::lock_guard<std::mutex> lk(g_mu);
-    size_t& cur = (*allowed)[vi];
+    size_t& cur = (*allowed)[(size_t)vi * 3 + e];
     if (lds <= cur) return true;
-    if (hipFuncSetAttribute(registry()[vi].func, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds) != hipSuccess)
+    if (hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return false;
     cur = lds;
     return true;
 }
 
 int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
-                   hipEvent_t ev1 = nullptr) {
+                   hipEvent_t ev1 = nullptr, const void* func = nullptr) {
     const Variant& v = registry()[vi];
+    if (!func) func = v.func;
     dim3 grid;
     size_t lds = 0;
     if (!v.geometry(v, a.M, a.N, a.K, &grid, &lds)) return LIN_ERR_UNSUPPORTED;
-    if (!allow_lds(vi, lds)) return LIN_ERR_HIP;
+    if (!allow_lds(vi, lds, func)) return LIN_ERR_HIP;
     KArgs args = a;
     args.splits = v.cfg.algo == LIN_ALGO_MFMA ? v.cfg.split : 1;
     args.ws = nullptr;
@@ -237,9 +240,9 @@ int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = 
     const dim3 block(v.block ? v.block : kBlock);
     hipError_t e;
     if (ev0 || ev1)
-        e = hipExtLaunchKernel(v.func, grid, block, params, lds, stream, ev0, ev1, 0);
+        e = hipExtLaunchKernel(func, grid, block, params, lds, stream, ev0, ev1, 0);
     else
-        e = hipLaunchKernel(v.func, grid, block, params, lds, stream);
+        e = hipLaunchKernel(func, grid, block, params, lds, stream);
     return e == hipSuccess ? LIN_OK : LIN_ERR_HIP;
 }
 
@@ -324,6 +327,40 @@ int lin_gemv_q4g64(const void* Wq, const void* S, const void* x, float* y, int64
 int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y, int64_t M, int64_t N, int64_t K,
                          void* stream) {
     return run(LIN_KIND_SKINNY_BF16, W, nullptr, X, Y, M, N, K, stream);
+}
+
+// Batch-1 product with a fused epilogue, in the configuration tuned or pinned
+// for the plain product of the same weight matrix (2N rows for the gated one).
+static int run_epilogue(int kind, const void* W, const void* S, const void* x, float* y,
+                        int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
+                        void* stream) {
+    if (epilogue < LIN_EPI_NONE || epilogue > LIN_EPI_SWIGLU) return LIN_ERR_ARG;
+    if (N < 0 || N > 0x3FFFFFFF) return LIN_ERR_SHAPE;
+    const int64_t NW = epilogue == LIN_EPI_SWIGLU ? 2 * N : N;   // weight rows
+    int st = check(kind, W, S, x, y, M, NW, K);
+    if (st != LIN_OK) return st > 0 ? LIN_OK : st;
+    if (M != 1) return LIN_ERR_SHAPE;
+    if (epilogue == LIN_EPI_ADD) {
+        if (!r) return LIN_ERR_NULL;
+        if (!aligned(r, 4)) return LIN_ERR_ALIGN;
+    }
+    const int vi = lookup(kind, M, NW, K);
+    if (vi < 0) return LIN_ERR_UNSUPPORTED;
+    const Variant& v = registry()[vi];
+    const void* f = epilogue == LIN_EPI_NONE ? v.func : v.epi[epilogue];
+    if (!f) return LIN_ERR_UNSUPPORTED;
+    KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr, r};
+    return launch_variant(vi, a, (hipStream_t)stream, nullptr, nullptr, f);
+}
+
+int lin_gemv_bf16_ep(const void* W, const void* x, float* y, int64_t M, int64_t N, int64_t K,
+                     int epilogue, const float* r, void* stream) {
+    return run_epilogue(LIN_KIND_GEMV_BF16, W, nullptr, x, y, M, N, K, epilogue, r, stream);
+}
+
+int lin_gemv_q4g64_ep(const void* Wq, const void* S, const void* x, float* y, int64_t M,
+                      int64_t N, int64_t K, int epilogue, const float* r, void* stream) {
+    return run_epilogue(LIN_KIND_GEMV_Q4G64, Wq, S, x, y, M, N, K, epilogue, r, stream);
 }
 
 int lin_gemv_i8(const void* Wq, const void* S, const void* x, float* y, int64_t M, int64_t N,

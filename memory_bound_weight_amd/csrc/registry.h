@@ -25,6 +25,9 @@ struct Variant {
     // Split-K workspace bytes this variant needs for a shape (0: none).
     size_t (*workspace)(const Variant&, int M, int N, int K);
     int block = 0;     // threads per workgroup (0: kBlock)
+    // The same configuration with a fused epilogue (index kEpiAdd, kEpiSwiglu;
+    // batch-1 GEMV variants only), or nullptr.
+    const void* epi[3] = {nullptr, nullptr, nullptr};
 };
 
 void register_gemv_bf16(std::vector<Variant>& out);

@@ -121,6 +121,16 @@ def test_quantize_i8_validation():
     assert q(P, P, P + 2, 4, 16, None) == L.LIN_ERR_ALIGN
 
 
+def test_epilogue_validation():
+    for f, extra in ((L._lib.lin_gemv_bf16_ep, ()), (L._lib.lin_gemv_q4g64_ep, (P,))):
+        assert f(P, *extra, P, P, 1, 8, 64, 3, None, None) == L.LIN_ERR_ARG
+        assert f(P, *extra, P, P, 1, 8, 64, L.LIN_EPI_ADD, None, None) == L.LIN_ERR_NULL
+        assert f(P, *extra, P, P, 2, 8, 64, L.LIN_EPI_NONE, None, None) == L.LIN_ERR_SHAPE
+        assert f(P, *extra, P, P, 1, 1 << 30, 64, L.LIN_EPI_SWIGLU, None, None) == L.LIN_ERR_SHAPE
+        assert f(P, *extra, P, P, 1, 8, 64, L.LIN_EPI_ADD, P + 2, None) == L.LIN_ERR_ALIGN
+        assert f(None, *((None,) if extra else ()), None, None, 0, 8, 64, L.LIN_EPI_SWIGLU, None, None) == L.LIN_OK
+
+
 def test_stream_read_validation():
     r = L._lib.lin_stream_read
     assert r(None, 0, None) == L.LIN_OK

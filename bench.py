@@ -443,6 +443,80 @@ def run_skinny(args, dev, fmt):
     print(json.dumps(out), flush=True)
 
 
+# ---------------------------------------------------------------- fused epilogues
+
+EPI_OF = {"o": L.LIN_EPI_ADD, "down": L.LIN_EPI_ADD, "gate|up": L.LIN_EPI_SWIGLU}
+
+
+def epilogue_step(mats, fused):
+    """Launch list of one decode pass with the elementwise steps that follow
+    the projections: the residual add after o and down, silu(gate) * up after
+    gate|up.  fused: folded into the products (lin_gemv_*_ep); otherwise the
+    plain product followed by one elementwise kernel (torch) per step."""
+    fns = []
+    for m in mats:
+        e = EPI_OF.get(m.name, L.LIN_EPI_NONE)
+        if e == L.LIN_EPI_NONE:
+            fns.append(lambda m=m: launch(m))
+            continue
+        if not hasattr(m, "res"):
+            n_out = m.N // 2 if e == L.LIN_EPI_SWIGLU else m.N
+            m.res = torch.zeros((1, n_out), dtype=torch.float32, device=m.y.device)
+            m.h = torch.empty((1, n_out), dtype=torch.float32, device=m.y.device)
+        if fused:
+            if m.fmt == "bf16":
+                f = lambda m=m, e=e: L.lin_gemv_bf16_ep(m.W, m.x, e, r=m.res if e == L.LIN_EPI_ADD else None, y=m.h)
+            else:
+                f = lambda m=m, e=e: L.lin_gemv_q4g64_ep(m.Wq, m.S, m.x, e, r=m.res if e == L.LIN_EPI_ADD else None, y=m.h)
+            fns.append(f)
+        else:
+            fns.append(lambda m=m: launch(m))
+            if e == L.LIN_EPI_ADD:
+                fns.append(lambda m=m: torch.add(m.y, m.res, out=m.h))
+            else:
+                half = m.N // 2
+                fns.append(lambda m=m, half=half: torch.mul(torch.nn.functional.silu(m.y[:, :half]),
+                                                            m.y[:, half:], out=m.h))
+    return fns
+
+
+def capture_fns(fns):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def run_epilogues(sets, fmts, args):
+    """Fused against unfused decode passes; returns per-format figures."""
+    out = {}
+    for f in fmts:
+        if f not in ("bf16", "q4"):
+            continue
+        res = {}
+        for fused in (False, True):
+            fns = epilogue_step(sets[f], fused)
+            g = capture_fns(fns)
+            _, gpu = time_graph(g, max(5, args.steps // 2), args.warmup)
+            res["fused" if fused else "unfused"] = {"launches": len(fns), "us_per_token": round(gpu * 1e6, 2)}
+            del g
+        res["speedup"] = round(res["unfused"]["us_per_token"] / res["fused"]["us_per_token"], 4)
+        out[f] = res
+        log("epilogues %s: unfused %.1f us (%d launches), fused %.1f us (%d launches)"
+            % (f, res["unfused"]["us_per_token"], res["unfused"]["launches"],
+               res["fused"]["us_per_token"], res["fused"]["launches"]))
+    return out
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(model, layers, threads, fmts=("bf16", "q4")):
@@ -533,6 +607,9 @@ def main():
     ap.add_argument("--formats", default="bf16,q4",
                     help="weight formats of the decode-step workloads, in step order: any of "
                          "bf16, q4 (int4-g64), i8 (INT8, fp32 scale per row)")
+    ap.add_argument("--epilogues", action="store_true",
+                    help="also time decode passes with the residual adds and the gated silu "
+                         "product, fused into the products against separate elementwise kernels")
     ap.add_argument("--no-fuse", action="store_true",
                     help="one launch per matrix instead of q|k|v and gate|up concatenated")
     ap.add_argument("--cpu-layers", type=int, default=16)
@@ -626,6 +703,11 @@ def main():
            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
            "gpu_ms_per_step": round(gpu * 1e3, 4),
            "per_format": per_fmt, "kernels": kernels, "roofline": roofline}
+    if args.epilogues:
+        if not fused:
+            print("--epilogues needs the concatenated gate|up projections (no --no-fuse)", file=sys.stderr)
+            sys.exit(2)
+        out["epilogues"] = run_epilogues(sets, fmts, args)
     if not args.skip_cpu:
         out["cpu_baseline"] = cpu_baseline(model, args.cpu_layers, min(16, os.cpu_count() or 1), fmts)
     print(json.dumps(out), flush=True)

@@ -26,6 +26,7 @@ const std::vector<Variant>& registry() {
         register_gemm_mfma_ring(*r);
         register_gemm_q4_ring(*r);
         register_gemv_i8(*r);
+        register_gemv_q4t(*r);
         return r;
     }();
     return *reg;

@@ -9,6 +9,7 @@ builds it with gcc, loads it with ctypes and marshals numpy arrays.
 """
 from .oracle import (  # noqa: F401
     LIB_PATH,
+    bf16_from_f64,
     bf16_value,
     build,
     dequant_i8,
@@ -24,6 +25,7 @@ from .oracle import (  # noqa: F401
     quantize_i8,
     quantize_q4g64,
     residual_add,
+    rmsnorm,
     swiglu,
     use,
 )

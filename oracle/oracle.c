@@ -24,6 +24,11 @@
  *    accumulated into its destination, and Mistral's gated product
  *    silu(w1(x)) * w3(x) computed by the kernel that forms both products; silu
  *    is the sigmoid-weighted linear unit, silu(g) = g / (1 + exp(-g)).
+ *  - "How I Built an LLM Inference Engine From Scratch in CUDA" (tinyinfer),
+ *    decode section (norms folded into the projections) and the TileInfer.jl
+ *    post, "Incremental acceleration" (norms fused): RMSNorm, the input of a
+ *    projection divided by the root mean square of its entries and multiplied
+ *    by a per-channel gain, computed by the projection kernel itself.
  *  - TileInfer.jl post, "Pushing further with cheating: INT8 quantization":
  *    symmetric INT8 in -127..127 with one Float32 scale per output channel,
  *    scale = max|w| / 127, every weight rounded to the nearest multiple of the
@@ -42,6 +47,9 @@
  *  - INT8: the stored scale is the fp32 nearest to max|w| / 127 (formed as an
  *    fp64 quotient rounded to fp32); q = round_half_even(w / s) with w / s in
  *    fp64, clamped to [-127, 127]; a row whose absmax is 0 gets s = 0, q = 0.
+ *  - RMSNorm: h[k] = x[k] g[k] / sqrt(mean_k x[k]^2 + eps), evaluated in fp64
+ *    and rounded once to the nearest bfloat16 (ties to even): the bf16
+ *    activation that a separate normalisation would hand to the projection.
  *
  * Parity status: every function below is pinned by tests/test_oracle.py against
  * brute force, closed forms, library conversions or figures printed on the pages.
@@ -111,6 +119,25 @@ uint16_t orc_f16_from_f64(double v) {
     if (sig == 2048.0) { sig = 1024.0; E += 1; }
     if (E + 15 >= 31) return sign | 0x7C00;
     return sign | (uint16_t)(((E + 15) << 10) | ((int)sig - 1024));
+}
+
+/* Nearest bfloat16 to v, ties to even; overflow gives infinity. */
+uint16_t orc_bf16_from_f64(double v) {
+    if (isnan(v)) return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    /* the largest finite bf16 is (2 - 2^-7) 2^127; from halfway to 2^128 up: inf */
+    if (a >= ldexp(2.0 - ldexp(1.0, -8), 127)) return sign | 0x7F80;
+    if (a < ldexp(1.0, -126)) {                    /* subnormal range, step 2^-133 */
+        double q = round_half_even(ldexp(a, 133)); /* 0..128; 128 = min normal */
+        return sign | (uint16_t)q;
+    }
+    int ex;
+    frexp(a, &ex);                                 /* a = m * 2^ex, m in [0.5, 1) */
+    int E = ex - 1;                                /* a in [2^E, 2^(E+1)) */
+    double sig = round_half_even(ldexp(a, 7 - E)); /* in [128, 256] */
+    if (sig == 256.0) { sig = 128.0; E += 1; }
+    return sign | (uint16_t)(((E + 127) << 7) | ((int)sig - 128));
 }
 
 /* ---- dense product ------------------------------------------------------ */
@@ -290,4 +317,24 @@ void orc_swiglu(const double* G, const double* U, int64_t n, double* H) {
 /* Y[i] = P[i] + R[i]: a product plus the residual it is accumulated into. */
 void orc_residual_add(const double* P, const float* R, int64_t n, double* Y) {
     for (int64_t i = 0; i < n; ++i) Y[i] = P[i] + (double)R[i];
+}
+
+/* ---- RMSNorm prologue ----------------------------------------------------- */
+
+/* H[m][k] = bf16(X[m][k] * G[k] / sqrt(sum_k X[m][k]^2 / K + eps)) for each
+ * token row m: the sum of squares in fp64, k ascending, one rounding to
+ * bfloat16 at the end.  X, H: bf16 [M][K]; G: bf16 [K]; K >= 1. */
+void orc_rmsnorm(const uint16_t* X, const uint16_t* G, int64_t M, int64_t K, double eps,
+                 uint16_t* H) {
+    for (int64_t m = 0; m < M; ++m) {
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double x = orc_bf16_value(X[m * K + k]);
+            ss += x * x;
+        }
+        double inv = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k)
+            H[m * K + k] = orc_bf16_from_f64(orc_bf16_value(X[m * K + k]) *
+                                             orc_bf16_value(G[k]) * inv);
+    }
 }

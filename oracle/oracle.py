@@ -79,6 +79,10 @@ def open_lib(path):
     lib.orc_swiglu.restype = None
     lib.orc_residual_add.argtypes = [P, P, I64, P]
     lib.orc_residual_add.restype = None
+    lib.orc_bf16_from_f64.argtypes = [ctypes.c_double]
+    lib.orc_bf16_from_f64.restype = ctypes.c_uint16
+    lib.orc_rmsnorm.argtypes = [P, P, I64, I64, ctypes.c_double, P]
+    lib.orc_rmsnorm.restype = None
     return lib
 
 
@@ -112,6 +116,13 @@ def f16_from_f64(values):
     lib = load()
     v = np.asarray(values, dtype=np.float64)
     return np.array([lib.orc_f16_from_f64(float(x)) for x in v.ravel()], dtype=np.uint16).reshape(v.shape)
+
+
+def bf16_from_f64(values):
+    """Nearest bfloat16 bit patterns to fp64 values (ties to even)."""
+    lib = load()
+    v = np.asarray(values, dtype=np.float64)
+    return np.array([lib.orc_bf16_from_f64(float(x)) for x in v.ravel()], dtype=np.uint16).reshape(v.shape)
 
 
 def gemm_dense(W, X):
@@ -251,3 +262,17 @@ def residual_add(P, R):
     Y = np.empty(P.shape, dtype=np.float64)
     lib.orc_residual_add(_ptr(P), _ptr(R), P.size, _ptr(Y))
     return Y
+
+
+def rmsnorm(X, g, eps):
+    """RMSNorm of each row of X (bf16 bits [M][K]) with gain g (bf16 bits [K]):
+    bf16 bits [M][K] of x g / sqrt(mean x^2 + eps)."""
+    lib = load()
+    X = _c(X, np.uint16)
+    g = _c(g, np.uint16)
+    if X.ndim != 2 or g.shape != (X.shape[1],) or X.shape[1] < 1:
+        raise ValueError("shape mismatch")
+    M, K = X.shape
+    H = np.empty((M, K), dtype=np.uint16)
+    lib.orc_rmsnorm(_ptr(X), _ptr(g), M, K, float(eps), _ptr(H))
+    return H

@@ -1,7 +1,7 @@
 """The oracle's pins must catch plausible mistakes.  Each case below compiles a
 copy of oracle.c with one planted mistake (on the CPU, in a temporary
 directory) and checks that at least one pin in test_oracle.py,
-test_oracle_i8.py or test_oracle_epilogue.py fails on it."""
+test_oracle_i8.py, test_oracle_epilogue.py or test_oracle_norm.py fails on it."""
 import os
 import subprocess
 import tempfile
@@ -12,6 +12,7 @@ import oracle
 import test_oracle as pins
 import test_oracle_epilogue as pins_ep
 import test_oracle_i8 as pins_i8
+import test_oracle_norm as pins_norm
 
 SRC = oracle.oracle.SRC_PATH
 
@@ -62,9 +63,19 @@ MUTATIONS = [
     ("residual-dropped", "Y[i] = P[i] + (double)R[i];", "Y[i] = P[i];"),
     ("i8-dequant-scale-index", "Wd[n * K + k] = (double)Wq[n * K + k] * (double)S[n];",
      "Wd[n * K + k] = (double)Wq[n * K + k] * (double)S[k % N];"),
+    ("rms-sum-not-mean", "sqrt(ss / (double)K + eps)", "sqrt(ss + eps)"),
+    ("rms-eps-dropped", "sqrt(ss / (double)K + eps)", "sqrt(ss / (double)K)"),
+    ("rms-no-sqrt", "1.0 / sqrt(ss / (double)K + eps)", "1.0 / (ss / (double)K + eps)"),
+    ("rms-gain-dropped", "orc_bf16_value(X[m * K + k]) *\n                                             orc_bf16_value(G[k]) * inv",
+     "orc_bf16_value(X[m * K + k]) * inv"),
+    ("bf16-round-truncating", "double sig = round_half_even(ldexp(a, 7 - E));",
+     "double sig = floor(ldexp(a, 7 - E));"),
+    ("bf16-subnormal-step", "round_half_even(ldexp(a, 133))", "round_half_even(ldexp(a, 134))"),
+    ("bf16-overflow-threshold", "if (a >= ldexp(2.0 - ldexp(1.0, -8), 127))",
+     "if (a >= ldexp(2.0 - ldexp(1.0, -7), 127))"),
 ]
 
-PIN_FUNCS = [getattr(m, n) for m in (pins, pins_i8, pins_ep) for n in dir(m) if n.startswith("test_")]
+PIN_FUNCS = [getattr(m, n) for m in (pins, pins_i8, pins_ep, pins_norm) for n in dir(m) if n.startswith("test_")]
 
 
 def _run_pins():

@@ -25,7 +25,8 @@
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points
- * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemv_bf16_ep, lin_gemv_q4g64_ep, lin_gemv_i8,
+ * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemv_bf16_ep, lin_gemv_q4g64_ep,
+ * lin_gemv_bf16_norm, lin_gemv_q4g64_norm, lin_gemv_i8,
  * lin_gemm_skinny_bf16,
  * lin_gemm_skinny_q4g64, lin_quantize_q4g64, lin_quantize_i8, lin_q4g64_tile)
  * validate their arguments in O(1), enqueue kernels on `stream` (a hipStream_t;
@@ -145,6 +146,28 @@ int lin_gemv_bf16_ep(const void* W, const void* x, float* y,
                      int64_t M, int64_t N, int64_t K, int epilogue, const float* r, void* stream);
 int lin_gemv_q4g64_ep(const void* Wq, const void* S, const void* x, float* y,
                       int64_t M, int64_t N, int64_t K, int epilogue, const float* r, void* stream);
+
+/* lin_gemv_bf16_ep / lin_gemv_q4g64_ep with the RMSNorm of x folded into the
+ * product as a prologue (tinyinfer post, decode section: the normalisation
+ * moved into the projection kernels; TileInfer.jl post, "Incremental
+ * acceleration": fused norms):
+ *   h[k] = bf16(x[k] g[k] / sqrt(sum_k x[k]^2 / K + eps)),  y = W h (+ epilogue).
+ * g: bf16 [K] gain, 16-byte aligned; eps >= 0 and finite (else LIN_ERR_ARG);
+ * M == 1 and K >= 8 (bf16) or K >= 64 (int4-g64), else LIN_ERR_SHAPE; NULL g is
+ * LIN_ERR_NULL.  x itself is not modified: the kernel normalises its own staged
+ * copy of x in LDS, next to a staged copy of g, before the first product, so no
+ * normalised activation is written to memory.  The configuration is the
+ * staged-x form of the one tuned or pinned for the plain product of the same
+ * matrix.  h is formed in fp32 (the sum of squares, then x g times the
+ * reciprocal root) and rounded to bf16 to nearest-even; an entry within a few
+ * fp32 steps of a bf16 rounding boundary may round the other way, adding at
+ * most 2^-8 |W[n][k] h[k]| for that k to the bounds of the plain product. */
+int lin_gemv_bf16_norm(const void* W, const void* x, const void* g, float eps, float* y,
+                       int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
+                       void* stream);
+int lin_gemv_q4g64_norm(const void* Wq, const void* S, const void* x, const void* g, float eps,
+                        float* y, int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
+                        void* stream);
 
 /* The same product with INT8 weights and one fp32 scale per output channel
  * (TileInfer.jl post, "Pushing further with cheating: INT8 quantization": the

@@ -42,7 +42,7 @@ LIN_SKINNY_MAX_M = 256
 
 # Every symbol include/lin.h declares.
 EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemv_bf16_ep", "lin_gemv_q4g64_ep",
-           "lin_gemv_i8", "lin_gemm_skinny_bf16",
+           "lin_gemv_bf16_norm", "lin_gemv_q4g64_norm", "lin_gemv_i8", "lin_gemm_skinny_bf16",
            "lin_gemm_skinny_q4g64", "lin_quantize_i8",
            "lin_q4g64_tiled_size", "lin_q4g64_tile", "lin_autotune",
            "lin_autotune_set", "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
@@ -85,6 +85,8 @@ def _load():
         "lin_gemv_i8": [P, P, P, P, I64, I64, I64, P],
         "lin_gemv_bf16_ep": [P, P, P, I64, I64, I64, I, P, P],
         "lin_gemv_q4g64_ep": [P, P, P, P, I64, I64, I64, I, P, P],
+        "lin_gemv_bf16_norm": [P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P],
+        "lin_gemv_q4g64_norm": [P, P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P],
         "lin_quantize_i8": [P, P, P, I64, I64, P],
         "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
         "lin_gemm_skinny_q4g64": [P, P, P, P, I64, I64, I64, P],
@@ -230,6 +232,49 @@ def lin_gemv_q4g64_ep(Wq, S, x, epilogue, r=None, y=None):
     _check(_lib.lin_gemv_q4g64_ep(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, K,
                                   int(epilogue), r.data_ptr() if r is not None else None,
                                   _stream(Wq)), "lin_gemv_q4g64_ep")
+    return y
+
+
+def _norm_gain(g, K):
+    _need(g, torch.bfloat16, "g", 1)
+    if tuple(g.shape) != (K,):
+        raise ValueError("g must have shape (%d,)" % K)
+
+
+def lin_gemv_bf16_norm(W, x, g, eps, epilogue=LIN_EPI_NONE, r=None, y=None):
+    """Batch-1 bf16 product of the RMSNorm of x: h = bf16(x g / sqrt(mean x^2 + eps)),
+    y = W h, with an optional fused epilogue (see lin_gemv_bf16_ep).  x is not modified."""
+    x = _as2d(x)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    NW, K = W.shape
+    if x.shape != (1, K):
+        raise ValueError("x must be one token of K = %d" % K)
+    _norm_gain(g, K)
+    N, y = _epi_out(epilogue, NW, r, y, W.device)
+    _check(_lib.lin_gemv_bf16_norm(W.data_ptr(), x.data_ptr(), g.data_ptr(), float(eps),
+                                   y.data_ptr(), 1, N, K, int(epilogue),
+                                   r.data_ptr() if r is not None else None, _stream(W)),
+           "lin_gemv_bf16_norm")
+    return y
+
+
+def lin_gemv_q4g64_norm(Wq, S, x, g, eps, epilogue=LIN_EPI_NONE, r=None, y=None):
+    """Batch-1 int4-g64 product of the RMSNorm of x (see lin_gemv_bf16_norm)."""
+    x = _as2d(x)
+    _need(Wq, torch.uint8, "Wq", 2)
+    _need(S, torch.float16, "S", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    NW, K2 = Wq.shape
+    K = 2 * K2
+    if x.shape != (1, K) or tuple(S.shape) != (NW, K // 64):
+        raise ValueError("shape mismatch: Wq [N, K/2], S [N, K/64], x [1, K]")
+    _norm_gain(g, K)
+    N, y = _epi_out(epilogue, NW, r, y, Wq.device)
+    _check(_lib.lin_gemv_q4g64_norm(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), g.data_ptr(),
+                                    float(eps), y.data_ptr(), 1, N, K, int(epilogue),
+                                    r.data_ptr() if r is not None else None, _stream(Wq)),
+           "lin_gemv_q4g64_norm")
     return y
 
 

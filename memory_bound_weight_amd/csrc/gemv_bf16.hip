@@ -5,9 +5,9 @@
 
 namespace lin {
 
-template <int MT, int R, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
+template <int MT, int R, int U, int SPLIT, bool STAGE, int EPI = kEpiNone, bool NORM = false>
 __global__ __launch_bounds__(kBlock) void gemv_bf16_valu(KArgs a) {
-    gemv_bf16_valu_block<MT, R, U, SPLIT, STAGE, EPI>(a, blockIdx.x);
+    gemv_bf16_valu_block<MT, R, U, SPLIT, STAGE, EPI, NORM>(a, blockIdx.x);
 }
 
 template <int MT, int R, int U, int SPLIT, bool STAGE>
@@ -39,9 +39,15 @@ static void add(std::vector<Variant>& out) {
         if constexpr (MT == 1) {
             v.epi[kEpiAdd] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
             v.epi[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu>;
+            if constexpr (STAGE) {
+                v.norm[kEpiNone] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiNone, true>;
+                v.norm[kEpiAdd] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiAdd, true>;
+                v.norm[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu, true>;
+            }
         }
         out.push_back(v);
         v.epi[kEpiAdd] = v.epi[kEpiSwiglu] = nullptr;
+        v.norm[kEpiNone] = v.norm[kEpiAdd] = v.norm[kEpiSwiglu] = nullptr;
     }
     v.kind = LIN_KIND_SKINNY_BF16;
     out.push_back(v);

@@ -24,6 +24,11 @@
 // rows (gate rows, then up rows, as concatenated at load), gives each
 // wavefront the R gate rows and the R matching up rows, and writes
 // y[n] = silu(g_n) u_n, so the gated activation never makes a round trip.
+//
+// Prologue (NORM, batch 1 with x staged): the RMSNorm of x is formed on the
+// staged copy (rms_norm_lds) before the first product; its gain vector is
+// staged next to x by the same direct-to-LDS copies, so the whole prologue
+// overlaps the latency of the first weight stage, like the staging itself.
 #pragma once
 
 #include <type_traits>
@@ -33,8 +38,9 @@
 namespace lin {
 
 // One row block (R x 4/SPLIT rows) of the product, one per workgroup.
-template <int MT, int R0, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
+template <int MT, int R0, int U, int SPLIT, bool STAGE, int EPI = kEpiNone, bool NORM = false>
 __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t block) {
+    static_assert(!NORM || (STAGE && MT == 1), "the prologue works on one staged token row");
     constexpr int GROUPS = 4 / SPLIT;
     constexpr int R = EPI == kEpiSwiglu ? 2 * R0 : R0;   // weight rows per wavefront
     constexpr int V = R * MT;
@@ -48,8 +54,9 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
     const uint16_t* __restrict__ W = (const uint16_t*)a.W;
     const uint16_t* __restrict__ X = (const uint16_t*)a.X;
 
-    extern __shared__ u32x4 xs[];   // STAGE: [MT][nch] chunks of x
+    extern __shared__ u32x4 xs[];   // STAGE: [MT][nch] chunks of x; NORM: then the gain
     if constexpr (STAGE) stage_x_dma(X, M, MT, K, xs);
+    if constexpr (NORM) stage_x_dma(a.G, 1, 1, K, xs + stage_x_units(MT, K));
 
     const int64_t row0 = (block * GROUPS + grp) * R0;   // first output row
     const uint8_t* wb[R];
@@ -139,6 +146,7 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
         else
             wait_cnt<0, 15>();
         barrier_only();
+        if constexpr (NORM) rms_norm_lds(xs, xs + stage_x_units(MT, K), K, a.eps);
     }
     if (nsteps > 0) {
         for (int it = 0;;) {

@@ -5,9 +5,9 @@
 
 namespace lin {
 
-template <int MT, int R, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
+template <int MT, int R, int U, int SPLIT, bool STAGE, int EPI = kEpiNone, bool NORM = false>
 __global__ __launch_bounds__(kBlock) void gemv_q4_valu(KArgs a) {
-    gemv_q4_valu_block<MT, R, U, SPLIT, STAGE, EPI>(a, blockIdx.x);
+    gemv_q4_valu_block<MT, R, U, SPLIT, STAGE, EPI, NORM>(a, blockIdx.x);
 }
 
 template <int MT, int R, int U, int SPLIT, bool STAGE>
@@ -38,6 +38,11 @@ static void add(std::vector<Variant>& out) {
     if constexpr (MT == 1) {
         v.epi[kEpiAdd] = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
         v.epi[kEpiSwiglu] = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu>;
+        if constexpr (STAGE) {
+            v.norm[kEpiNone] = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE, kEpiNone, true>;
+            v.norm[kEpiAdd] = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE, kEpiAdd, true>;
+            v.norm[kEpiSwiglu] = (const void*)&gemv_q4_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu, true>;
+        }
     }
     out.push_back(v);
 }

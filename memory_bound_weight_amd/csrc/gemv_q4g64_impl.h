@@ -32,6 +32,8 @@
 //
 // Epilogues (EPI) as in the bf16 kernel: the residual add, or the gated
 // product silu(g) u over a matrix of 2N rows (gate rows, then up rows).
+// Prologue (NORM, batch 1 with x staged): the RMSNorm of x on the staged raw
+// copy (rms_norm_lds, gain staged beside it), before x is re-paired.
 #pragma once
 
 #include <type_traits>
@@ -113,8 +115,9 @@ __host__ __device__ inline size_t q4_stage_bytes(int MT, int K) {
 }
 
 // One row block (R x 4/SPLIT rows) of the product, one per workgroup.
-template <int MT, int R0, int U, int SPLIT, bool STAGE, int EPI = kEpiNone>
+template <int MT, int R0, int U, int SPLIT, bool STAGE, int EPI = kEpiNone, bool NORM = false>
 __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block) {
+    static_assert(!NORM || (STAGE && MT == 1), "the prologue works on one staged token row");
     constexpr int GROUPS = 4 / SPLIT;
     constexpr int R = EPI == kEpiSwiglu ? 2 * R0 : R0;   // weight rows per wavefront
     constexpr int V = R * MT;
@@ -131,11 +134,12 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
     const uint16_t* __restrict__ X = (const uint16_t*)a.X;
 
     // STAGE: [MT][4][nch] re-paired words, [MT][nch] chunk sums (padded to
-    // 16 bytes), then the raw copy of x (q4_stage_raw_offset).
+    // 16 bytes), then the raw copy of x (q4_stage_raw_offset); NORM: then the gain.
     extern __shared__ u32x4 xs[];
     float* xsum = (float*)(xs + (size_t)MT * 4 * nch);
     u32x4* xraw = xs + q4_stage_raw_offset(MT, K);
     if constexpr (STAGE) stage_x_dma(X, M, MT, K, xraw);
+    if constexpr (NORM) stage_x_dma(a.G, 1, 1, K, xraw + stage_x_units(MT, K));
 
     const int64_t row0 = (block * GROUPS + grp) * R0;   // first output row
     const uint8_t* wb[R];
@@ -238,6 +242,7 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
         else
             wait_cnt<0, 15>();
         barrier_only();
+        if constexpr (NORM) rms_norm_lds(xraw, xraw + stage_x_units(MT, K), K, a.eps);
         for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
             const int m = i / nch;
             const int c = i - m * nch;

@@ -19,6 +19,8 @@ struct KArgs {
     int splits;      // split-K factor (matrix-core path), 1 otherwise
     void* ws;        // split-K workspace: tile counters, then partial tiles
     const float* R;  // residual fp32 [M][N] of the add epilogue (may equal Y)
+    const void* G;   // bf16 [K] gain of the RMSNorm prologue
+    float eps;       // RMSNorm: added to the mean square
 };
 
 // Epilogues of the batch-1 products (the values of lin_epilogue).
@@ -205,6 +207,54 @@ __device__ __forceinline__ void for_each_reduced(const float (&v)[V], int lane, 
 #pragma unroll
     for (int s = 0; s < S; ++s)
         if (reduce_writer<V>(s, lane)) f(reduce_index<V>(s, lane), v[s]);
+}
+
+// Nearest bfloat16 pattern to a binary32 value, ties to even (finite values;
+// values beyond the largest finite bf16 round to infinity).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = fbits(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// RMSNorm prologue of a batch-1 product (tinyinfer post, decode section: the
+// normalisation folded into the projection kernel), in place on the token row
+// staged in LDS: x[k] <- bf16(x[k] g[k] / sqrt(sum_k x[k]^2 / K + eps)).  x and g
+// are K bf16 in natural order (K / 8 16-byte units each), already visible to
+// the whole workgroup.  The sum of squares is fp32 (per-thread partial sums,
+// then the wavefront tree and four wavefront totals in a fixed order), x g is
+// exact in fp32 and the product with the reciprocal is rounded once to fp32
+// and once to bf16.  Only LDS is waited for: weight loads stay in flight.
+__device__ __forceinline__ void rms_norm_lds(u32x4* x, const u32x4* g, int K, float eps) {
+    __shared__ float part[4];
+    const int n = K >> 3;
+    float ss[1] = {0.f};
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const u32x4 v = x[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = bitsf(v[j] << 16), hi = bitsf(v[j] & 0xFFFF0000u);
+            ss[0] = fmaf(lo, lo, ss[0]);
+            ss[0] = fmaf(hi, hi, ss[0]);
+        }
+    }
+    wave_reduce<1>(ss);
+    if ((threadIdx.x & 63) == 0) part[wave_id()] = ss[0];
+    wait_cnt<63, 0>();
+    barrier_only();
+    const float inv = 1.f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)K + eps);
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        const u32x4 v = x[i], gv = g[i];
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float lo = bitsf(v[j] << 16) * bitsf(gv[j] << 16) * inv;
+            const float hi = bitsf(v[j] & 0xFFFF0000u) * bitsf(gv[j] & 0xFFFF0000u) * inv;
+            o[j] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+        }
+        x[i] = o;
+    }
+    wait_cnt<63, 0>();
+    barrier_only();
 }
 
 // Matrix-core tile order.  Workgroups are dispatched round-robin over the

@@ -27,6 +27,20 @@ const std::vector<Variant>& registry() {
         register_gemm_q4_ring(*r);
         register_gemv_i8(*r);
         register_gemv_q4t(*r);
+        // staged siblings (same configuration, x staged in LDS), for the
+        // prologue entry points
+        for (auto& v : *r) {
+            if (v.cfg.algo != LIN_ALGO_VALU || v.mt != 1) continue;
+            for (int j = 0; j < (int)r->size(); ++j) {
+                const Variant& w = (*r)[j];
+                if (w.kind == v.kind && w.mt == 1 && w.cfg.algo == LIN_ALGO_VALU &&
+                    w.cfg.rows == v.cfg.rows && w.cfg.unroll == v.cfg.unroll &&
+                    w.cfg.split == v.cfg.split && w.cfg.stage_x == 1 && w.norm[0]) {
+                    v.staged = j;
+                    break;
+                }
+            }
+        }
         return r;
     }();
     return *reg;
@@ -201,15 +215,13 @@ int ensure_workspace(int dev, size_t bytes) {
 }
 
 // Dynamic LDS above the default 64 KB per workgroup must be allowed per
-// kernel first; the largest size allowed so far is kept per variant.
-bool allow_lds(int vi, size_t lds, const void* func = nullptr) {
+// kernel first; the largest size allowed so far is kept per kernel.
+bool allow_lds(size_t lds, const void* func) {
     if (lds <= 64 * 1024) return true;
-    const Variant& v = registry()[vi];
-    if (!func) func = v.func;
-    const int e = func == v.epi[kEpiAdd] ? kEpiAdd : (func == v.epi[kEpiSwiglu] ? kEpiSwiglu : 0);
-    static auto* allowed = new std::vector<size_t>(registry().size() * 3, 64 * 1024);
+    static auto* allowed = new std::map<const void*, size_t>();
     std::lock_guard<std::mutex> lk(g_mu);
-    size_t& cur = (*allowed)[(size_t)vi * 3 + e];
+    auto ins = allowed->emplace(func, (size_t)64 * 1024);
+    size_t& cur = ins.first->second;
     if (lds <= cur) return true;
     if (hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return false;
@@ -218,13 +230,15 @@ bool allow_lds(int vi, size_t lds, const void* func = nullptr) {
 }
 
 int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
-                   hipEvent_t ev1 = nullptr, const void* func = nullptr) {
+                   hipEvent_t ev1 = nullptr, const void* func = nullptr, size_t extra_lds = 0) {
     const Variant& v = registry()[vi];
     if (!func) func = v.func;
     dim3 grid;
     size_t lds = 0;
     if (!v.geometry(v, a.M, a.N, a.K, &grid, &lds)) return LIN_ERR_UNSUPPORTED;
-    if (!allow_lds(vi, lds, func)) return LIN_ERR_HIP;
+    lds += extra_lds;
+    if (lds > kMaxDynLds) return LIN_ERR_UNSUPPORTED;
+    if (!allow_lds(lds, func)) return LIN_ERR_HIP;
     KArgs args = a;
     args.splits = v.cfg.algo == LIN_ALGO_MFMA ? v.cfg.split : 1;
     args.ws = nullptr;
@@ -248,6 +262,9 @@ int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = 
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// LDS that the RMSNorm prologue adds to a staged configuration: the gain.
+size_t norm_lds(int64_t K) { return 16 * stage_x_units(1, (int)K); }
 
 // Shared argument checks.  Returns LIN_OK, a negative status, or 1 for an
 // empty call (nothing to do).
@@ -364,6 +381,46 @@ int lin_gemv_q4g64_ep(const void* Wq, const void* S, const void* x, float* y, in
     return run_epilogue(LIN_KIND_GEMV_Q4G64, Wq, S, x, y, M, N, K, epilogue, r, stream);
 }
 
+// Batch-1 product of RMSNorm(x) with an optional epilogue, in the staged form
+// of the configuration tuned or pinned for the plain product of the matrix.
+static int run_norm(int kind, const void* W, const void* S, const void* x, const void* g,
+                    float eps, float* y, int64_t M, int64_t N, int64_t K, int epilogue,
+                    const float* r, void* stream) {
+    if (epilogue < LIN_EPI_NONE || epilogue > LIN_EPI_SWIGLU) return LIN_ERR_ARG;
+    if (!(eps >= 0.f) || eps > 3.0e38f) return LIN_ERR_ARG;   // also rejects NaN
+    if (N < 0 || N > 0x3FFFFFFF) return LIN_ERR_SHAPE;
+    const int64_t NW = epilogue == LIN_EPI_SWIGLU ? 2 * N : N;   // weight rows
+    int st = check(kind, W, S, x, y, M, NW, K);
+    if (st != LIN_OK) return st > 0 ? LIN_OK : st;
+    if (M != 1 || K == 0) return LIN_ERR_SHAPE;
+    if (!g) return LIN_ERR_NULL;
+    if (!aligned(g, 16)) return LIN_ERR_ALIGN;
+    if (epilogue == LIN_EPI_ADD) {
+        if (!r) return LIN_ERR_NULL;
+        if (!aligned(r, 4)) return LIN_ERR_ALIGN;
+    }
+    const int vi = lookup(kind, M, NW, K);
+    if (vi < 0) return LIN_ERR_UNSUPPORTED;
+    const int vs = registry()[vi].staged;
+    if (vs < 0) return LIN_ERR_UNSUPPORTED;
+    const void* f = registry()[vs].norm[epilogue];
+    if (!f) return LIN_ERR_UNSUPPORTED;
+    KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr, r, g, eps};
+    return launch_variant(vs, a, (hipStream_t)stream, nullptr, nullptr, f, norm_lds(K));
+}
+
+int lin_gemv_bf16_norm(const void* W, const void* x, const void* g, float eps, float* y,
+                       int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
+                       void* stream) {
+    return run_norm(LIN_KIND_GEMV_BF16, W, nullptr, x, g, eps, y, M, N, K, epilogue, r, stream);
+}
+
+int lin_gemv_q4g64_norm(const void* Wq, const void* S, const void* x, const void* g, float eps,
+                        float* y, int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
+                        void* stream) {
+    return run_norm(LIN_KIND_GEMV_Q4G64, Wq, S, x, g, eps, y, M, N, K, epilogue, r, stream);
+}
+
 int lin_gemv_i8(const void* Wq, const void* S, const void* x, float* y, int64_t M, int64_t N,
                 int64_t K, void* stream) {
     return run(LIN_KIND_GEMV_I8, Wq, S, x, y, M, N, K, stream);
@@ -457,8 +514,19 @@ int set_config_reserving(int kind, int64_t M, int64_t N, int64_t K, const lin_co
         dim3 grid;
         size_t lds = 0;
         const Variant& v = registry()[vi];
-        if (v.geometry(v, (int)M, (int)N, (int)K, &grid, &lds) && !allow_lds(vi, lds))
-            return LIN_ERR_HIP;
+        if (v.geometry(v, (int)M, (int)N, (int)K, &grid, &lds)) {
+            for (const void* f : {v.func, v.epi[kEpiAdd], v.epi[kEpiSwiglu]})
+                if (f && !allow_lds(lds, f)) return LIN_ERR_HIP;
+        }
+        if (v.staged >= 0 && M == 1) {   // the prologue variants of this configuration
+            const Variant& w = registry()[v.staged];
+            size_t l2 = 0;
+            if (w.geometry(w, (int)M, (int)N, (int)K, &grid, &l2)) {
+                l2 += norm_lds(K);
+                for (const void* f : w.norm)
+                    if (f && l2 <= kMaxDynLds && !allow_lds(l2, f)) return LIN_ERR_HIP;
+            }
+        }
     }
     return LIN_OK;
 }

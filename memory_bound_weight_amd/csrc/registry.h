@@ -28,6 +28,12 @@ struct Variant {
     // The same configuration with a fused epilogue (index kEpiAdd, kEpiSwiglu;
     // batch-1 GEMV variants only), or nullptr.
     const void* epi[3] = {nullptr, nullptr, nullptr};
+    // Batch-1 GEMV variants with x staged: the same configuration with the
+    // RMSNorm prologue, per epilogue index, or nullptr.
+    const void* norm[3] = {nullptr, nullptr, nullptr};
+    // Index of the variant with the same configuration and x staged (itself
+    // if it stages x), -1 if there is none; set once the registry is built.
+    int staged = -1;
 };
 
 void register_gemv_bf16(std::vector<Variant>& out);

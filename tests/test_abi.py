@@ -131,6 +131,22 @@ def test_epilogue_validation():
         assert f(None, *((None,) if extra else ()), None, None, 0, 8, 64, L.LIN_EPI_SWIGLU, None, None) == L.LIN_OK
 
 
+def test_norm_validation():
+    for f, extra in ((L._lib.lin_gemv_bf16_norm, ()), (L._lib.lin_gemv_q4g64_norm, (P,))):
+        assert f(P, *extra, P, P, 1e-6, P, 1, 8, 64, 3, None, None) == L.LIN_ERR_ARG
+        assert f(P, *extra, P, P, -1.0, P, 1, 8, 64, 0, None, None) == L.LIN_ERR_ARG
+        assert f(P, *extra, P, P, float("nan"), P, 1, 8, 64, 0, None, None) == L.LIN_ERR_ARG
+        assert f(P, *extra, P, P, float("inf"), P, 1, 8, 64, 0, None, None) == L.LIN_ERR_ARG
+        assert f(P, *extra, P, None, 1e-6, P, 1, 8, 64, 0, None, None) == L.LIN_ERR_NULL
+        assert f(P, *extra, P, P + 8, 1e-6, P, 1, 8, 64, 0, None, None) == L.LIN_ERR_ALIGN
+        assert f(P, *extra, P, P, 1e-6, P, 1, 8, 64, L.LIN_EPI_ADD, None, None) == L.LIN_ERR_NULL
+        assert f(P, *extra, P, P, 1e-6, P, 2, 8, 64, 0, None, None) == L.LIN_ERR_SHAPE
+        assert f(P, *extra, P, P, 1e-6, P, 1, 8, 0, 0, None, None) == L.LIN_ERR_SHAPE
+        assert f(P, *extra, P, P, 1e-6, P, 1, 8, 60, 0, None, None) == L.LIN_ERR_SHAPE
+        assert f(None, *((None,) if extra else ()), None, None, 1e-6, None, 0, 8, 64, 0, None,
+                 None) == L.LIN_OK
+
+
 def test_stream_read_validation():
     r = L._lib.lin_stream_read
     assert r(None, 0, None) == L.LIN_OK

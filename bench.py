@@ -115,42 +115,62 @@ def tune_key(m):
     return (kind_of(m), 1, m.N, m.K)
 
 
-def autotune(mats, only=None):
-    """Load-time tuning: once per distinct (format, N, K), with lin_autotune_set
+NORM_KINDS = {"bf16": L.LIN_KIND_GEMV_BF16_NORM, "q4": L.LIN_KIND_GEMV_Q4G64_NORM}
+NORM_OF = ("q|k|v", "gate|up", "head")   # projections whose input is RMS-normalised
+
+
+def tune_keys(m, norms=False):
+    """Tuning keys a matrix is launched under: its product and, with norms, the
+    RMSNorm-prologue product of the normalised projections."""
+    keys = [tune_key(m)]
+    if norms and m.name in NORM_OF and m.fmt in NORM_KINDS:
+        keys.append((NORM_KINDS[m.fmt], 1, m.N, m.K))
+    return keys
+
+
+def autotune(mats, only=None, norms=False):
+    """Load-time tuning: once per distinct (kind, N, K), with lin_autotune_set
     over all of that shape's matrices (the layers), timed back to back the way
     the step runs them; returns {tune key: config}."""
     groups = {}
     for m in mats:
-        key = tune_key(m)
-        if only is None or key in only:
-            groups.setdefault(key, []).append(m)
+        for key in tune_keys(m, norms):
+            if only is None or key in only:
+                groups.setdefault(key, []).append(m)
     seen = {}
     for key, ms in groups.items():
         m = ms[0]
         if m.fmt == "bf16":
-            cfg = L.lin_autotune_set(L.LIN_KIND_GEMV_BF16, [g.W for g in ms], m.x, m.y)
+            cfg = L.lin_autotune_set(key[0], [g.W for g in ms], m.x, m.y)
         else:
-            cfg = L.lin_autotune_set(kind_of(m), [g.Wq for g in ms], m.x, m.y,
-                                     Ss=[g.S for g in ms])
+            cfg = L.lin_autotune_set(key[0], [g.Wq for g in ms], m.x, m.y, Ss=[g.S for g in ms])
         seen[key] = cfg
-        log("tuned %-5s %6d x %-6d over %d matrices -> %s" % (m.fmt, m.N, m.K, len(ms), cfg))
+        log("tuned kind %d %-5s %6d x %-6d over %d matrices -> %s" % (key[0], m.fmt, m.N, m.K,
+                                                                    len(ms), cfg))
     return seen
 
 
-def apply_tuning(mats, path, retune):
+def apply_tuning(mats, path, retune, norms=False, save_to=None):
     """Use the persisted tuning table (tuned once with lin_autotune on MI355X);
-    shapes it does not cover, or all shapes with retune, are tuned now."""
-    keys = {tune_key(m) for m in mats}
+    keys it does not cover, or all keys with retune, are tuned now.  save_to:
+    also write the table with the keys tuned now."""
+    keys = {k for m in mats for k in tune_keys(m, norms)}
     if retune or not os.path.exists(path):
-        entries = autotune(mats)
-        L.save_tuning(path, entries)
-        return "tuned now (%d shapes), saved to %s" % (len(entries), os.path.relpath(path, ROOT))
+        entries = autotune(mats, norms=norms)
+        L.save_tuning(save_to or path, entries)
+        return "tuned now (%d shapes), saved to %s" % (len(entries),
+                                                       os.path.relpath(save_to or path, ROOT))
     ok, stale = L.load_tuning(path)
     missing = keys - set(ok)
     if missing:
-        autotune(mats, only=missing)
+        new = autotune(mats, only=missing, norms=norms)
+        if save_to:
+            with open(path) as f:
+                old = {(e["kind"], e["M"], e["N"], e["K"]): e["cfg"] for e in json.load(f)["entries"]}
+            old.update(new)
+            L.save_tuning(save_to, old)
     return "loaded %s (%d shapes%s)" % (os.path.relpath(path, ROOT), len(keys - missing),
-                                        ", %d re-tuned" % len(missing) if missing else "")
+                                        ", %d tuned now" % len(missing) if missing else "")
 
 
 def capture(mats):
@@ -448,36 +468,96 @@ def run_skinny(args, dev, fmt):
 EPI_OF = {"o": L.LIN_EPI_ADD, "down": L.LIN_EPI_ADD, "gate|up": L.LIN_EPI_SWIGLU}
 
 
-def epilogue_step(mats, fused):
-    """Launch list of one decode pass with the elementwise steps that follow
-    the projections: the residual add after o and down, silu(gate) * up after
-    gate|up.  fused: folded into the products (lin_gemv_*_ep); otherwise the
-    plain product followed by one elementwise kernel (torch) per step."""
+NORM_EPS = 1e-6
+
+
+def _prepare(m, e, nrm):
+    if e != L.LIN_EPI_NONE and not hasattr(m, "res"):
+        n_out = m.N // 2 if e == L.LIN_EPI_SWIGLU else m.N
+        m.res = torch.zeros((1, n_out), dtype=torch.float32, device=m.y.device)
+        m.h = torch.empty((1, n_out), dtype=torch.float32, device=m.y.device)
+    if nrm and not hasattr(m, "gain"):
+        rng = np.random.default_rng(m.N * 131 + m.K)
+        gbits = ((1.0 + 0.1 * rng.standard_normal(m.K)).astype(np.float32).view(np.uint32) >> 16)
+        m.gain = synth.from_bits(gbits.astype(np.uint16), torch.bfloat16, m.y.device)
+        m.xn = torch.empty_like(m.x)
+
+
+def torch_rmsnorm(x, g, eps, out):
+    """RMSNorm as separate PyTorch ops (the unfused reference pass)."""
+    xf = x.float()
+    out.copy_(xf * torch.rsqrt(xf.pow(2).mean(-1, keepdim=True) + eps) * g.float())
+
+
+def fused_call(m, e, nrm):
+    """One launch: the product with its epilogue and, if nrm, its RMSNorm prologue."""
+    r = m.res if e == L.LIN_EPI_ADD else None
+    y = m.y if e == L.LIN_EPI_NONE else m.h
+    if nrm:
+        if m.fmt == "bf16":
+            return lambda: L.lin_gemv_bf16_norm(m.W, m.x, m.gain, NORM_EPS, e, r=r, y=y)
+        return lambda: L.lin_gemv_q4g64_norm(m.Wq, m.S, m.x, m.gain, NORM_EPS, e, r=r, y=y)
+    if e == L.LIN_EPI_NONE:
+        return lambda: launch(m)
+    if m.fmt == "bf16":
+        return lambda: L.lin_gemv_bf16_ep(m.W, m.x, e, r=r, y=y)
+    return lambda: L.lin_gemv_q4g64_ep(m.Wq, m.S, m.x, e, r=r, y=y)
+
+
+def epilogue_step(mats, fused, norms=False):
+    """Launch list of one decode pass with the elementwise steps around the
+    projections: the residual add after o and down, silu(gate) * up after
+    gate|up and, with norms, the RMSNorm of the inputs of q|k|v, gate|up and
+    the head.  fused: folded into the products (lin_gemv_*_ep, lin_gemv_*_norm);
+    otherwise the plain product with separate PyTorch ops around it."""
     fns = []
     for m in mats:
         e = EPI_OF.get(m.name, L.LIN_EPI_NONE)
-        if e == L.LIN_EPI_NONE:
-            fns.append(lambda m=m: launch(m))
-            continue
-        if not hasattr(m, "res"):
-            n_out = m.N // 2 if e == L.LIN_EPI_SWIGLU else m.N
-            m.res = torch.zeros((1, n_out), dtype=torch.float32, device=m.y.device)
-            m.h = torch.empty((1, n_out), dtype=torch.float32, device=m.y.device)
+        nrm = norms and m.name in NORM_OF
+        _prepare(m, e, nrm)
         if fused:
+            fns.append(fused_call(m, e, nrm))
+            continue
+        if nrm:
+            fns.append(lambda m=m: torch_rmsnorm(m.x, m.gain, NORM_EPS, m.xn))
             if m.fmt == "bf16":
-                f = lambda m=m, e=e: L.lin_gemv_bf16_ep(m.W, m.x, e, r=m.res if e == L.LIN_EPI_ADD else None, y=m.h)
+                fns.append(lambda m=m: L.lin_gemv_bf16(m.W, m.xn, m.y))
             else:
-                f = lambda m=m, e=e: L.lin_gemv_q4g64_ep(m.Wq, m.S, m.x, e, r=m.res if e == L.LIN_EPI_ADD else None, y=m.h)
-            fns.append(f)
+                fns.append(lambda m=m: L.lin_gemv_q4g64(m.Wq, m.S, m.xn, m.y))
         else:
             fns.append(lambda m=m: launch(m))
-            if e == L.LIN_EPI_ADD:
-                fns.append(lambda m=m: torch.add(m.y, m.res, out=m.h))
-            else:
-                half = m.N // 2
-                fns.append(lambda m=m, half=half: torch.mul(torch.nn.functional.silu(m.y[:, :half]),
-                                                            m.y[:, half:], out=m.h))
+        if e == L.LIN_EPI_ADD:
+            fns.append(lambda m=m: torch.add(m.y, m.res, out=m.h))
+        elif e == L.LIN_EPI_SWIGLU:
+            half = m.N // 2
+            fns.append(lambda m=m, half=half: torch.mul(torch.nn.functional.silu(m.y[:, :half]),
+                                                        m.y[:, half:], out=m.h))
     return fns
+
+
+def prologue_cost(mats, args):
+    """Per normalised projection shape: average launch time of the product with
+    its epilogue, without and with the RMSNorm prologue (graphs of back-to-back
+    launches over every matrix of that shape, as the step runs them)."""
+    out = {}
+    for name in NORM_OF:
+        ms = [m for m in mats if m.name == name]
+        if not ms:
+            continue
+        e = EPI_OF.get(name, L.LIN_EPI_NONE)
+        reps = max(1, 64 // len(ms))
+        res = {}
+        for nrm in (False, True):
+            for m in ms:
+                _prepare(m, e, nrm)
+            g = capture_fns([fused_call(m, e, nrm) for _ in range(reps) for m in ms])
+            _, gpu = time_graph(g, max(5, args.steps // 2), args.warmup)
+            res["norm" if nrm else "plain"] = gpu / (reps * len(ms))
+            del g
+        out["%s %dx%d" % (name, ms[0].N, ms[0].K)] = {
+            "us_without": round(res["plain"] * 1e6, 3), "us_with_norm": round(res["norm"] * 1e6, 3),
+            "GB_s_with_norm": round(ms[0].bytes / res["norm"] / 1e9, 1)}
+    return out
 
 
 def capture_fns(fns):
@@ -497,23 +577,35 @@ def capture_fns(fns):
 
 
 def run_epilogues(sets, fmts, args):
-    """Fused against unfused decode passes; returns per-format figures."""
+    """Fused against unfused decode passes (epilogues only, then epilogues and
+    RMSNorm prologues), and the per-kernel cost of the prologue; per format."""
     out = {}
     for f in fmts:
         if f not in ("bf16", "q4"):
             continue
         res = {}
-        for fused in (False, True):
-            fns = epilogue_step(sets[f], fused)
-            g = capture_fns(fns)
-            _, gpu = time_graph(g, max(5, args.steps // 2), args.warmup)
-            res["fused" if fused else "unfused"] = {"launches": len(fns), "us_per_token": round(gpu * 1e6, 2)}
-            del g
-        res["speedup"] = round(res["unfused"]["us_per_token"] / res["fused"]["us_per_token"], 4)
+        for norms in (False, True):
+            part = {}
+            for fused in (False, True):
+                fns = epilogue_step(sets[f], fused, norms)
+                g = capture_fns(fns)
+                _, gpu = time_graph(g, max(5, args.steps // 2), args.warmup)
+                part["fused" if fused else "unfused"] = {"launches": len(fns),
+                                                         "us_per_token": round(gpu * 1e6, 2)}
+                del g
+            part["speedup"] = round(part["unfused"]["us_per_token"] / part["fused"]["us_per_token"], 4)
+            log("%s %s: unfused %.1f us (%d launches), fused %.1f us (%d launches)"
+                % ("epilogues+norms" if norms else "epilogues", f, part["unfused"]["us_per_token"],
+                   part["unfused"]["launches"], part["fused"]["us_per_token"],
+                   part["fused"]["launches"]))
+            if norms:
+                res["with_norms"] = part
+            else:
+                res.update(part)
+        res["prologue_cost"] = prologue_cost(sets[f], args)
+        for k, v in res["prologue_cost"].items():
+            log("prologue %s %s: %.2f -> %.2f us" % (f, k, v["us_without"], v["us_with_norm"]))
         out[f] = res
-        log("epilogues %s: unfused %.1f us (%d launches), fused %.1f us (%d launches)"
-            % (f, res["unfused"]["us_per_token"], res["unfused"]["launches"],
-               res["fused"]["us_per_token"], res["fused"]["launches"]))
     return out
 
 
@@ -609,7 +701,10 @@ def main():
                          "bf16, q4 (int4-g64), i8 (INT8, fp32 scale per row)")
     ap.add_argument("--epilogues", action="store_true",
                     help="also time decode passes with the residual adds and the gated silu "
-                         "product, fused into the products against separate elementwise kernels")
+                         "product (and then also the RMSNorm of the projection inputs), fused "
+                         "into the products against separate PyTorch ops")
+    ap.add_argument("--save-tuning", default=None, metavar="PATH",
+                    help="write the tuning table, with any entries tuned by this run, to PATH")
     ap.add_argument("--no-fuse", action="store_true",
                     help="one launch per matrix instead of q|k|v and gate|up concatenated")
     ap.add_argument("--cpu-layers", type=int, default=16)
@@ -649,7 +744,7 @@ def main():
     default_fmts = fmts == ["bf16", "q4"]
     tname = model["name"] + ("" if default_fmts else "-" + "-".join(fmts))
     tfile = args.tuning or os.path.join(L.TUNING_DIR, "%s.json" % tname)
-    tuning = apply_tuning(allm, tfile, args.tune)
+    tuning = apply_tuning(allm, tfile, args.tune, norms=args.epilogues, save_to=args.save_tuning)
     log("tuning: " + tuning)
 
     step_bytes = sum(m.bytes for m in allm)

@@ -61,13 +61,15 @@ typedef enum lin_status {
     LIN_ERR_ARG = -6          /* unknown kind, malformed configuration, bad index */
 } lin_status;
 
-/* The five products; `kind` selects one in the tuning calls. */
+/* The products; `kind` selects one in the tuning calls. */
 typedef enum lin_kind {
-    LIN_KIND_GEMV_BF16 = 0,   /* lin_gemv_bf16 */
-    LIN_KIND_GEMV_Q4G64 = 1,  /* lin_gemv_q4g64 */
+    LIN_KIND_GEMV_BF16 = 0,   /* lin_gemv_bf16 (and lin_gemv_bf16_ep) */
+    LIN_KIND_GEMV_Q4G64 = 1,  /* lin_gemv_q4g64 (and lin_gemv_q4g64_ep) */
     LIN_KIND_SKINNY_BF16 = 2, /* lin_gemm_skinny_bf16 */
     LIN_KIND_SKINNY_Q4G64 = 3, /* lin_gemm_skinny_q4g64 (tiled int4-g64 weights) */
-    LIN_KIND_GEMV_I8 = 4       /* lin_gemv_i8 */
+    LIN_KIND_GEMV_I8 = 4,      /* lin_gemv_i8 */
+    LIN_KIND_GEMV_BF16_NORM = 5,  /* lin_gemv_bf16_norm (M == 1) */
+    LIN_KIND_GEMV_Q4G64_NORM = 6  /* lin_gemv_q4g64_norm (M == 1) */
 } lin_kind;
 
 /* Kernel families. */
@@ -137,7 +139,9 @@ typedef enum lin_epilogue {
 /* lin_gemv_bf16 / lin_gemv_q4g64 for M == 1 with a fused epilogue.  N counts
  * the outputs (the weight matrix has 2N rows for LIN_EPI_SWIGLU).  The
  * configuration is the one tuned or pinned for the plain product of the same
- * weight matrix, i.e. (kind, 1, 2N or N, K).  Error bound per output: for ADD,
+ * weight matrix, i.e. (kind, 1, 2N or N, K); with SWIGLU a wavefront keeps the
+ * configuration's `rows` weight rows (rows/2 gate rows and the matching up
+ * rows; one of each when rows is 1).  Error bound per output: for ADD,
  * 1e-3 * (sum_k |W x| + |r|); for SWIGLU, the GEMV bound propagated through
  * silu(g) u (1e-3 * (1.1 |u| sum_k |W_g x| + |silu(g)| sum_k |W_u x|)) plus a few
  * fp32 rounding steps of |y|.  M != 1 returns LIN_ERR_SHAPE; ADD with a NULL r
@@ -154,14 +158,17 @@ int lin_gemv_q4g64_ep(const void* Wq, const void* S, const void* x, float* y,
  *   h[k] = bf16(x[k] g[k] / sqrt(sum_k x[k]^2 / K + eps)),  y = W h (+ epilogue).
  * g: bf16 [K] gain, 16-byte aligned; eps >= 0 and finite (else LIN_ERR_ARG);
  * M == 1 and K >= 8 (bf16) or K >= 64 (int4-g64), else LIN_ERR_SHAPE; NULL g is
- * LIN_ERR_NULL.  x itself is not modified: the kernel normalises its own staged
- * copy of x in LDS, next to a staged copy of g, before the first product, so no
- * normalised activation is written to memory.  The configuration is the
- * staged-x form of the one tuned or pinned for the plain product of the same
- * matrix.  h is formed in fp32 (the sum of squares, then x g times the
- * reciprocal root) and rounded to bf16 to nearest-even; an entry within a few
- * fp32 steps of a bf16 rounding boundary may round the other way, adding at
- * most 2^-8 |W[n][k] h[k]| for that k to the bounds of the plain product. */
+ * LIN_ERR_NULL.  x itself is not modified: each workgroup normalises its own
+ * staged copy of x in LDS, next to a staged copy of g, before its first
+ * product, so no normalised activation is written to memory.  Since every
+ * workgroup repeats the prologue, these products are configurations of their
+ * own kinds, LIN_KIND_GEMV_BF16_NORM and LIN_KIND_GEMV_Q4G64_NORM, tuned or
+ * pinned for (kind, 1, 2N or N, K) like the plain products (the epilogue forms
+ * share that configuration).  h is formed in fp32 (the sum of squares, then
+ * x g times the reciprocal root) and rounded to bf16 to nearest-even; an entry
+ * within a few fp32 steps of a bf16 rounding boundary may round the other way,
+ * adding at most 2^-8 |W[n][k] h[k]| for that k to the bounds of the plain
+ * product. */
 int lin_gemv_bf16_norm(const void* W, const void* x, const void* g, float eps, float* y,
                        int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
                        void* stream);
@@ -221,7 +228,8 @@ int lin_q4g64_tile(const void* Wq, const void* S, void* Wt, void* St,
  * candidate configuration of `kind` for (M, N, K) on the caller's buffers,
  * which must be valid for that kind (S is used only by the int4 and INT8 kinds
  * and may be NULL otherwise; W and S are Wt and St for LIN_KIND_SKINNY_Q4G64, Wi
- * and Si for LIN_KIND_GEMV_I8; y receives scratch results).  Each timed call starts
+ * and Si for LIN_KIND_GEMV_I8; for the RMSNorm kinds M must be 1 and x also
+ * stands in for the gain; y receives scratch results).  Each timed call starts
  * from cold caches.  The fastest configuration is stored in the per-device
  * table and used by later calls with the same (kind, M, N, K); if `out` is not
  * NULL it receives it, with `us` set.  Unlike the compute calls this one

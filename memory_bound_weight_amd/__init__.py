@@ -29,6 +29,8 @@ LIN_KIND_GEMV_Q4G64 = 1
 LIN_KIND_SKINNY_BF16 = 2
 LIN_KIND_SKINNY_Q4G64 = 3
 LIN_KIND_GEMV_I8 = 4
+LIN_KIND_GEMV_BF16_NORM = 5
+LIN_KIND_GEMV_Q4G64_NORM = 6
 
 LIN_EPI_NONE = 0
 LIN_EPI_ADD = 1
@@ -417,7 +419,7 @@ def _shape_args(kind, W, S, x):
         if not isinstance(W, Q4Tiled):
             raise TypeError("LIN_KIND_SKINNY_Q4G64 takes Q4Tiled weights")
         return x, x.shape[0], W.N, W.K
-    if kind == LIN_KIND_GEMV_Q4G64:
+    if kind in (LIN_KIND_GEMV_Q4G64, LIN_KIND_GEMV_Q4G64_NORM):
         return x, x.shape[0], W.shape[0], 2 * W.shape[1]
     return x, x.shape[0], W.shape[0], W.shape[1]
 

@@ -21,8 +21,19 @@ static bool geom_bf16(const Variant&, int M, int N, int K, dim3* grid, size_t* l
     return true;
 }
 
+// The RMSNorm prologue also stages the gain next to x.
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static bool geom_bf16_norm(const Variant& v, int M, int N, int K, dim3* grid, size_t* lds) {
+    if (!geom_bf16<MT, R, U, SPLIT, STAGE>(v, M, N, K, grid, lds)) return false;
+    *lds += 16 * stage_x_units(1, K);
+    return *lds <= kMaxDynLds;
+}
+
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 static void add(std::vector<Variant>& out) {
+    // The gated form keeps R weight rows per wavefront: R/2 gate rows and the
+    // matching up rows (one of each for R = 1).
+    constexpr int RS = R >= 2 ? R / 2 : 1;
     Variant v{};
     v.cfg.algo = LIN_ALGO_VALU;
     v.cfg.rows = R;
@@ -38,16 +49,19 @@ static void add(std::vector<Variant>& out) {
         v.kind = LIN_KIND_GEMV_BF16;
         if constexpr (MT == 1) {
             v.epi[kEpiAdd] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
-            v.epi[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu>;
+            v.epi[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, RS, U, SPLIT, STAGE, kEpiSwiglu>;
             if constexpr (STAGE) {
-                v.norm[kEpiNone] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiNone, true>;
-                v.norm[kEpiAdd] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiAdd, true>;
-                v.norm[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiSwiglu, true>;
+                Variant n = v;
+                n.kind = LIN_KIND_GEMV_BF16_NORM;
+                n.func = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiNone, true>;
+                n.epi[kEpiAdd] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiAdd, true>;
+                n.epi[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, RS, U, SPLIT, STAGE, kEpiSwiglu, true>;
+                n.geometry = &geom_bf16_norm<MT, R, U, SPLIT, STAGE>;
+                out.push_back(n);
             }
         }
         out.push_back(v);
         v.epi[kEpiAdd] = v.epi[kEpiSwiglu] = nullptr;
-        v.norm[kEpiNone] = v.norm[kEpiAdd] = v.norm[kEpiSwiglu] = nullptr;
     }
     v.kind = LIN_KIND_SKINNY_BF16;
     out.push_back(v);

@@ -22,7 +22,7 @@
 // step into the product that feeds it): kEpiAdd writes y = W x + r (the
 // residual add, r may be y itself); kEpiSwiglu reads a weight matrix of 2N
 // rows (gate rows, then up rows, as concatenated at load), gives each
-// wavefront the R gate rows and the R matching up rows, and writes
+// wavefront R0 gate rows and the R0 matching up rows, and writes
 // y[n] = silu(g_n) u_n, so the gated activation never makes a round trip.
 //
 // Prologue (NORM, batch 1 with x staged): the RMSNorm of x is formed on the
@@ -137,20 +137,28 @@ __device__ __forceinline__ void gemv_bf16_valu_block(const KArgs& a, int64_t blo
     int cb = cbeg;
     Stage s0, s1;
     if (nsteps > 0) load(s0, cb);
+    bool s1_early = false;
     if constexpr (STAGE) {
-        // The x copies were issued before the U R loads of stage 0, and loads
-        // complete in order: waiting down to U R leaves stage 0 in flight.
-        // The barrier makes every wavefront's copies visible.
-        if (nsteps > 0)
+        // Both weight stages are issued before waiting for the x copies, so
+        // that they stream while x lands (and is normalised).  The copies were
+        // issued first and loads complete in order: waiting down to the weight
+        // loads leaves them in flight.  The barrier makes every wavefront's
+        // copies visible.
+        if (nsteps > 1) {
+            load(s1, cb + STEP);
+            s1_early = true;
+            wait_cnt<2 * U * R, 15>();
+        } else if (nsteps > 0) {
             wait_cnt<U * R, 15>();
-        else
+        } else {
             wait_cnt<0, 15>();
+        }
         barrier_only();
         if constexpr (NORM) rms_norm_lds(xs, xs + stage_x_units(MT, K), K, a.eps);
     }
     if (nsteps > 0) {
         for (int it = 0;;) {
-            if (it + 1 < nsteps) load(s1, cb + STEP);
+            if (it + 1 < nsteps && !(it == 0 && s1_early)) load(s1, cb + STEP);
             step(s0, cb);
             cb += STEP;
             if (++it >= nsteps) break;

@@ -233,14 +233,22 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
     int cb = cbeg;
     Stage s0, s1;
     if (nsteps > 0) load(s0, cb);
+    bool s1_early = false;
     if constexpr (STAGE) {
-        // The x copies were issued before the 2 U R loads of stage 0, and
-        // loads complete in order: waiting down to 2 U R leaves stage 0 in
+        // Both weight stages (2 U R loads each: codes and scales) are issued
+        // before waiting for the x copies, so that they stream while x lands,
+        // is normalised and re-paired.  The copies were issued first and loads
+        // complete in order: waiting down to the weight loads leaves them in
         // flight.  The barrier makes every wavefront's copies visible.
-        if (nsteps > 0)
+        if (nsteps > 1) {
+            load(s1, cb + STEP);
+            s1_early = true;
+            wait_cnt<4 * U * R, 15>();
+        } else if (nsteps > 0) {
             wait_cnt<2 * U * R, 15>();
-        else
+        } else {
             wait_cnt<0, 15>();
+        }
         barrier_only();
         if constexpr (NORM) rms_norm_lds(xraw, xraw + stage_x_units(MT, K), K, a.eps);
         for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
@@ -259,7 +267,7 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
     }
     if (nsteps > 0) {
         for (int it = 0;;) {
-            if (it + 1 < nsteps) load(s1, cb + STEP);
+            if (it + 1 < nsteps && !(it == 0 && s1_early)) load(s1, cb + STEP);
             step(s0, cb);
             cb += STEP;
             if (++it >= nsteps) break;

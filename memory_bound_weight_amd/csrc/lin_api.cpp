@@ -27,23 +27,14 @@ const std::vector<Variant>& registry() {
         register_gemm_q4_ring(*r);
         register_gemv_i8(*r);
         register_gemv_q4t(*r);
-        // staged siblings (same configuration, x staged in LDS), for the
-        // prologue entry points
-        for (auto& v : *r) {
-            if (v.cfg.algo != LIN_ALGO_VALU || v.mt != 1) continue;
-            for (int j = 0; j < (int)r->size(); ++j) {
-                const Variant& w = (*r)[j];
-                if (w.kind == v.kind && w.mt == 1 && w.cfg.algo == LIN_ALGO_VALU &&
-                    w.cfg.rows == v.cfg.rows && w.cfg.unroll == v.cfg.unroll &&
-                    w.cfg.split == v.cfg.split && w.cfg.stage_x == 1 && w.norm[0]) {
-                    v.staged = j;
-                    break;
-                }
-            }
-        }
         return r;
     }();
     return *reg;
+}
+
+bool valid_kind(int kind) { return kind >= LIN_KIND_GEMV_BF16 && kind <= LIN_KIND_GEMV_Q4G64_NORM; }
+bool norm_kind(int kind) {
+    return kind == LIN_KIND_GEMV_BF16_NORM || kind == LIN_KIND_GEMV_Q4G64_NORM;
 }
 
 using Key = std::tuple<int, int, int64_t, int64_t, int64_t>;   // device, kind, M, N, K
@@ -109,6 +100,17 @@ int default_variant(int kind, int64_t M, int64_t N, int64_t K) {
         for (int i : candidates(kind, M, N, K))
             if (workspace_need(registry()[i], M, N, K) == 0) return i;
         return -1;
+    }
+    if (norm_kind(kind)) {
+        // every workgroup repeats the prologue: several rows per workgroup
+        want.rows = N >= 4096 ? 4 : 2;
+        want.unroll = kind == LIN_KIND_GEMV_BF16_NORM ? 2 : 1;
+        want.split = N >= 4096 ? 1 : 2;
+        want.stage_x = 1;
+        int i = find_variant(kind, M, N, K, want);
+        if (i >= 0) return i;
+        auto c = candidates(kind, M, N, K);
+        return c.empty() ? -1 : c.front();
     }
     if (kind == LIN_KIND_GEMV_I8) {
         want.rows = 2;
@@ -229,15 +231,16 @@ bool allow_lds(size_t lds, const void* func) {
     return true;
 }
 
+// geom_n: the row count the launch grid is sized for, when it differs from a.N
+// (the gated epilogue).
 int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
-                   hipEvent_t ev1 = nullptr, const void* func = nullptr, size_t extra_lds = 0) {
+                   hipEvent_t ev1 = nullptr, const void* func = nullptr, int64_t geom_n = -1) {
     const Variant& v = registry()[vi];
     if (!func) func = v.func;
     dim3 grid;
     size_t lds = 0;
-    if (!v.geometry(v, a.M, a.N, a.K, &grid, &lds)) return LIN_ERR_UNSUPPORTED;
-    lds += extra_lds;
-    if (lds > kMaxDynLds) return LIN_ERR_UNSUPPORTED;
+    if (!v.geometry(v, a.M, geom_n >= 0 ? (int)geom_n : a.N, a.K, &grid, &lds))
+        return LIN_ERR_UNSUPPORTED;
     if (!allow_lds(lds, func)) return LIN_ERR_HIP;
     KArgs args = a;
     args.splits = v.cfg.algo == LIN_ALGO_MFMA ? v.cfg.split : 1;
@@ -263,28 +266,36 @@ int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = 
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// LDS that the RMSNorm prologue adds to a staged configuration: the gain.
-size_t norm_lds(int64_t K) { return 16 * stage_x_units(1, (int)K); }
+// Grid rows of a gated-epilogue launch with N outputs: a wavefront of a
+// configuration with `rows` >= 2 weight rows takes rows/2 outputs (gate and up
+// rows), so the grid is sized as for 2N rows; with rows == 1 it takes one
+// output (two weight rows), as for N rows.
+int64_t swiglu_grid_rows(const Variant& v, int64_t N) { return v.cfg.rows >= 2 ? 2 * N : N; }
+
+
 
 // Shared argument checks.  Returns LIN_OK, a negative status, or 1 for an
 // empty call (nothing to do).
 int check(int kind, const void* W, const void* S, const void* x, const float* y, int64_t M,
           int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K < 0) return LIN_ERR_SHAPE;
-    const bool q4 = kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64;
+    const bool q4 = kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64 ||
+                    kind == LIN_KIND_GEMV_Q4G64_NORM;
     const bool i8 = kind == LIN_KIND_GEMV_I8;
     const int64_t maxm = (kind == LIN_KIND_SKINNY_BF16 || kind == LIN_KIND_SKINNY_Q4G64)
                              ? LIN_SKINNY_MAX_M
-                             : LIN_GEMV_MAX_M;
+                             : (norm_kind(kind) ? 1 : LIN_GEMV_MAX_M);
     if (M > maxm || N > 0x7FFFFFFF || K > LIN_MAX_K) return LIN_ERR_SHAPE;
     if (q4 ? (K % 64) : (i8 ? (K % 16) : (K % 8))) return LIN_ERR_SHAPE;
     if (M == 0 || N == 0) return 1;
+    if (norm_kind(kind) && K == 0) return LIN_ERR_SHAPE;   // the mean square needs K >= 1
     if (!y) return LIN_ERR_NULL;
     if (K > 0 && (!W || !x || ((q4 || i8) && !S))) return LIN_ERR_NULL;
     if (!aligned(y, 4)) return LIN_ERR_ALIGN;
     if (K > 0) {
         if (!aligned(W, 16) || !aligned(x, 16)) return LIN_ERR_ALIGN;
-        if (kind == LIN_KIND_GEMV_Q4G64 && !aligned(S, 2)) return LIN_ERR_ALIGN;
+        if ((kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_GEMV_Q4G64_NORM) && !aligned(S, 2))
+            return LIN_ERR_ALIGN;
         if (kind == LIN_KIND_SKINNY_Q4G64 && !aligned(S, 16)) return LIN_ERR_ALIGN;
         if (i8 && !aligned(S, 4)) return LIN_ERR_ALIGN;
     }
@@ -368,7 +379,8 @@ static int run_epilogue(int kind, const void* W, const void* S, const void* x, f
     const void* f = epilogue == LIN_EPI_NONE ? v.func : v.epi[epilogue];
     if (!f) return LIN_ERR_UNSUPPORTED;
     KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr, r};
-    return launch_variant(vi, a, (hipStream_t)stream, nullptr, nullptr, f);
+    return launch_variant(vi, a, (hipStream_t)stream, nullptr, nullptr, f,
+                          epilogue == LIN_EPI_SWIGLU ? swiglu_grid_rows(v, N) : -1);
 }
 
 int lin_gemv_bf16_ep(const void* W, const void* x, float* y, int64_t M, int64_t N, int64_t K,
@@ -381,18 +393,18 @@ int lin_gemv_q4g64_ep(const void* Wq, const void* S, const void* x, float* y, in
     return run_epilogue(LIN_KIND_GEMV_Q4G64, Wq, S, x, y, M, N, K, epilogue, r, stream);
 }
 
-// Batch-1 product of RMSNorm(x) with an optional epilogue, in the staged form
-// of the configuration tuned or pinned for the plain product of the matrix.
+// Batch-1 product of RMSNorm(x) with an optional epilogue, in the configuration
+// tuned or pinned for the matrix under the prologue kind.
 static int run_norm(int kind, const void* W, const void* S, const void* x, const void* g,
                     float eps, float* y, int64_t M, int64_t N, int64_t K, int epilogue,
                     const float* r, void* stream) {
     if (epilogue < LIN_EPI_NONE || epilogue > LIN_EPI_SWIGLU) return LIN_ERR_ARG;
     if (!(eps >= 0.f) || eps > 3.0e38f) return LIN_ERR_ARG;   // also rejects NaN
     if (N < 0 || N > 0x3FFFFFFF) return LIN_ERR_SHAPE;
+    if (M != 0 && M != 1) return LIN_ERR_SHAPE;
     const int64_t NW = epilogue == LIN_EPI_SWIGLU ? 2 * N : N;   // weight rows
     int st = check(kind, W, S, x, y, M, NW, K);
     if (st != LIN_OK) return st > 0 ? LIN_OK : st;
-    if (M != 1 || K == 0) return LIN_ERR_SHAPE;
     if (!g) return LIN_ERR_NULL;
     if (!aligned(g, 16)) return LIN_ERR_ALIGN;
     if (epilogue == LIN_EPI_ADD) {
@@ -401,24 +413,26 @@ static int run_norm(int kind, const void* W, const void* S, const void* x, const
     }
     const int vi = lookup(kind, M, NW, K);
     if (vi < 0) return LIN_ERR_UNSUPPORTED;
-    const int vs = registry()[vi].staged;
-    if (vs < 0) return LIN_ERR_UNSUPPORTED;
-    const void* f = registry()[vs].norm[epilogue];
+    const Variant& v = registry()[vi];
+    const void* f = epilogue == LIN_EPI_NONE ? v.func : v.epi[epilogue];
     if (!f) return LIN_ERR_UNSUPPORTED;
     KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr, r, g, eps};
-    return launch_variant(vs, a, (hipStream_t)stream, nullptr, nullptr, f, norm_lds(K));
+    return launch_variant(vi, a, (hipStream_t)stream, nullptr, nullptr, f,
+                          epilogue == LIN_EPI_SWIGLU ? swiglu_grid_rows(v, N) : -1);
 }
 
 int lin_gemv_bf16_norm(const void* W, const void* x, const void* g, float eps, float* y,
                        int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
                        void* stream) {
-    return run_norm(LIN_KIND_GEMV_BF16, W, nullptr, x, g, eps, y, M, N, K, epilogue, r, stream);
+    return run_norm(LIN_KIND_GEMV_BF16_NORM, W, nullptr, x, g, eps, y, M, N, K, epilogue, r,
+                    stream);
 }
 
 int lin_gemv_q4g64_norm(const void* Wq, const void* S, const void* x, const void* g, float eps,
                         float* y, int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
                         void* stream) {
-    return run_norm(LIN_KIND_GEMV_Q4G64, Wq, S, x, g, eps, y, M, N, K, epilogue, r, stream);
+    return run_norm(LIN_KIND_GEMV_Q4G64_NORM, Wq, S, x, g, eps, y, M, N, K, epilogue, r,
+                    stream);
 }
 
 int lin_gemv_i8(const void* Wq, const void* S, const void* x, float* y, int64_t M, int64_t N,
@@ -450,7 +464,7 @@ int lin_q4g64_tile(const void* Wq, const void* S, void* Wt, void* St, int64_t N,
 }
 
 int lin_num_candidates(int kind, int64_t M, int64_t N, int64_t K) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_GEMV_I8) return LIN_ERR_ARG;
+    if (!valid_kind(kind)) return LIN_ERR_ARG;
     int st = check(kind, (void*)16, (void*)16, (void*)16, (float*)16, M, N, K);
     if (st < 0) return st;
     if (st > 0) return 0;
@@ -518,15 +532,6 @@ int set_config_reserving(int kind, int64_t M, int64_t N, int64_t K, const lin_co
             for (const void* f : {v.func, v.epi[kEpiAdd], v.epi[kEpiSwiglu]})
                 if (f && !allow_lds(lds, f)) return LIN_ERR_HIP;
         }
-        if (v.staged >= 0 && M == 1) {   // the prologue variants of this configuration
-            const Variant& w = registry()[v.staged];
-            size_t l2 = 0;
-            if (w.geometry(w, (int)M, (int)N, (int)K, &grid, &l2)) {
-                l2 += norm_lds(K);
-                for (const void* f : w.norm)
-                    if (f && l2 <= kMaxDynLds && !allow_lds(l2, f)) return LIN_ERR_HIP;
-            }
-        }
     }
     return LIN_OK;
 }
@@ -570,7 +575,7 @@ int lin_quantize_i8(const void* W, void* Wq, void* S, int64_t N, int64_t K, void
 
 int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y, int64_t M,
                  int64_t N, int64_t K, void* stream, lin_config* out) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_GEMV_I8) return LIN_ERR_ARG;
+    if (!valid_kind(kind)) return LIN_ERR_ARG;
     int st = check(kind, W, S, x, y, M, N, K);
     if (st < 0) return st;
     if (st > 0) return LIN_OK;
@@ -604,7 +609,8 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
         (void)hipEventDestroy(e0);
         return LIN_ERR_HIP;
     }
-    KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr};
+    // the RMSNorm kinds time the prologue with x standing in for the gain
+    KArgs a{W, S, x, y, (int)M, (int)N, (int)K, 1, nullptr, nullptr, x, 1e-6f};
     const int reps = 7;
     int best = -1;
     float best_us = 0.f;
@@ -655,10 +661,10 @@ int lin_autotune(int kind, const void* W, const void* S, const void* x, float* y
 int lin_autotune_set(int kind, const void* const* W, const void* const* S, int count,
                      const void* x, float* y, int64_t M, int64_t N, int64_t K, void* stream,
                      lin_config* out) {
-    if (kind < LIN_KIND_GEMV_BF16 || kind > LIN_KIND_GEMV_I8) return LIN_ERR_ARG;
+    if (!valid_kind(kind)) return LIN_ERR_ARG;
     if (count < 1) return LIN_ERR_ARG;
     if (!W || ((kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64 ||
-                kind == LIN_KIND_GEMV_I8) && !S))
+                kind == LIN_KIND_GEMV_I8 || kind == LIN_KIND_GEMV_Q4G64_NORM) && !S))
         return LIN_ERR_NULL;
     for (int j = 0; j < count; ++j) {
         const int st = check(kind, W[j], S ? S[j] : nullptr, x, y, M, N, K);
@@ -689,7 +695,7 @@ int lin_autotune_set(int kind, const void* const* W, const void* const* S, int c
         const int vi = cand[ci];
         auto args = [&](int j) {
             return KArgs{W[j % count], S ? S[j % count] : nullptr, x, y,
-                         (int)M, (int)N, (int)K, 1, nullptr};
+                         (int)M, (int)N, (int)K, 1, nullptr, nullptr, x, 1e-6f};
         };
         // warm-up outside the capture (code load, LDS attribute)
         if ((rc = launch_variant(vi, args(0), ts)) != LIN_OK) break;

@@ -27,13 +27,9 @@ struct Variant {
     int block = 0;     // threads per workgroup (0: kBlock)
     // The same configuration with a fused epilogue (index kEpiAdd, kEpiSwiglu;
     // batch-1 GEMV variants only), or nullptr.
+    // For the RMSNorm kinds, func is the prologue kernel without an epilogue
+    // and epi[] the prologue kernels with one.
     const void* epi[3] = {nullptr, nullptr, nullptr};
-    // Batch-1 GEMV variants with x staged: the same configuration with the
-    // RMSNorm prologue, per epilogue index, or nullptr.
-    const void* norm[3] = {nullptr, nullptr, nullptr};
-    // Index of the variant with the same configuration and x staged (itself
-    // if it stages x), -1 if there is none; set once the registry is built.
-    int staged = -1;
 };
 
 void register_gemv_bf16(std::vector<Variant>& out);

@@ -186,7 +186,8 @@ def test_candidate_enumeration():
     for kind, M, N, K in [(0, 1, 2048, 2048), (0, 8, 512, 3584), (1, 1, 2048, 2048),
                           (1, 3, 512, 18944), (2, 8, 4096, 4096), (2, 17, 1024, 4096),
                           (3, 1, 4096, 4096), (3, 64, 14336, 4096), (3, 256, 300, 4160),
-                          (4, 1, 2048, 2048), (4, 8, 300, 4112)]:
+                          (4, 1, 2048, 2048), (4, 8, 300, 4112), (5, 1, 4608, 3584),
+                          (6, 1, 37888, 3584)]:
         n = L.lin_num_candidates(kind, M, N, K)
         assert n > 0
         cands = L.lin_candidates(kind, M, N, K)
@@ -204,7 +205,26 @@ def test_candidate_enumeration():
     with pytest.raises(L.LinError):
         L.lin_candidate(0, 1, 8, 8, 10 ** 6)
     assert L._lib.lin_num_candidates(0, 1, 8, 12) == L.LIN_ERR_SHAPE
-    assert L._lib.lin_num_candidates(5, 1, 8, 8) == L.LIN_ERR_ARG
+    assert L._lib.lin_num_candidates(7, 1, 8, 8) == L.LIN_ERR_ARG
+    assert L._lib.lin_num_candidates(-1, 1, 8, 8) == L.LIN_ERR_ARG
+
+
+def test_norm_kind_candidates():
+    """The RMSNorm kinds offer only staged-x batch-1 configurations, refuse
+    M > 1 and K == 0, and drop configurations whose x + gain copies do not fit
+    in LDS."""
+    for kind, base in ((L.LIN_KIND_GEMV_BF16_NORM, L.LIN_KIND_GEMV_BF16),
+                       (L.LIN_KIND_GEMV_Q4G64_NORM, L.LIN_KIND_GEMV_Q4G64)):
+        for N, K in ((2560, 2048), (37888, 3584), (152064, 3584)):
+            cands = L.lin_candidates(kind, 1, N, K)
+            assert cands and all(c["stage_x"] == 1 and c["tile_m"] == 1 for c in cands)
+            staged = [c for c in L.lin_candidates(base, 1, N, K) if c["stage_x"] == 1]
+            assert len(cands) == len(staged)
+            assert L.lin_get_config(kind, 1, N, K)["stage_x"] == 1
+        assert L._lib.lin_num_candidates(kind, 2, 2048, 2048) == L.LIN_ERR_SHAPE
+        assert L._lib.lin_num_candidates(kind, 1, 2048, 0) == L.LIN_ERR_SHAPE
+        big = L.lin_candidates(kind, 1, 64, 65536)
+        assert len(big) < len(L.lin_candidates(kind, 1, 64, 4096))
 
 
 def test_default_skinny_config_needs_no_workspace():

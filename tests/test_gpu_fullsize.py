@@ -160,3 +160,54 @@ def test_maximum_k():
         Yi, Bi = oracle.gemm_i8(Wi_o, Si_o, u16(x))
         assert_within_bound(yi, Yi, Bi, "i8 K=2^22")
         assert_within_bound(yt, Y4, B4, "skinny q4 K=2^22")
+
+
+@pytest.mark.parametrize("model", [synth.TINYLLAMA, synth.QWEN7B], ids=lambda m: m["name"])
+def test_norm_prologue_sampled(model):
+    """RMSNorm folded into the normalised projections (q|k|v, gate|up with the
+    gated epilogue, head) at full size, bf16 and int4-g64, in the tuned
+    configurations; bound as in test_gpu_norm."""
+    from test_gpu_norm import _gain, _near_boundary
+    _tuned(model["name"])
+    eps = 1e-6
+    shapes = _shapes(model)
+    named = {"q|k|v": shapes[0], "gate|up": shapes[2], "head": shapes[-1]}
+    for name, (NW, K) in named.items():
+        print("case fullsize norm %s %s %dx%d" % (model["name"], name, NW, K), flush=True)
+        W = synth.weight(model["seed"], 0, 98, NW, K, device=DEV)
+        x = synth.activation(model["seed"], 0, 98, 1, K, device=DEV)
+        g = _gain(K, NW)
+        gd = synth.from_bits(g, torch.bfloat16, DEV)
+        h = oracle.rmsnorm(u16(x), g, eps)
+        hw = np.where(_near_boundary(u16(x)[0], g, eps), h[0], 0).astype(np.uint16)[None, :]
+        swiglu = name == "gate|up"
+        N = NW // 2 if swiglu else NW
+        out = _sample_rows(N)
+        rows = np.concatenate([out, out + N]) if swiglu else out
+        Wr = u16(W[torch.from_numpy(rows).to(DEV)])
+        Wq, S = L.lin_quantize_q4g64(W)
+        idx = torch.from_numpy(rows).to(DEV)
+        Wq_o, S_o = oracle.quantize_q4g64(Wr)
+        for fmt in ("bf16", "q4"):
+            if fmt == "bf16":
+                Y, B = oracle.gemm_dense(Wr, h)
+                _, Bw = oracle.gemm_dense(Wr, hw)
+                y = L.lin_gemv_bf16_norm(W, x, gd, eps, L.LIN_EPI_SWIGLU if swiglu else L.LIN_EPI_NONE)
+            else:
+                Y, B = oracle.gemm_q4g64(Wq_o, S_o, h)
+                _, Bw = oracle.gemm_q4g64(Wq_o, S_o, hw)
+                y = L.lin_gemv_q4g64_norm(Wq, S, x, gd, eps, L.LIN_EPI_SWIGLU if swiglu else L.LIN_EPI_NONE)
+            torch.cuda.synchronize()
+            got = y[0, torch.from_numpy(out).to(DEV)].cpu().numpy().astype(np.float64)
+            bound = 1e-3 * B[0] + 2.0 ** -8 * Bw[0]
+            if swiglu:
+                n = len(out)
+                gate, up, bg, bu = Y[0, :n], Y[0, n:], bound[:n], bound[n:]
+                expect = oracle.swiglu(gate, up)
+                silu = oracle.swiglu(gate, np.ones_like(gate))
+                bound = 1.1 * np.abs(up) * bg + np.abs(silu) * bu + 1e-6 * np.abs(expect)
+            else:
+                expect = Y[0]
+            d = np.abs(got - expect)
+            assert np.all(d <= bound), "%s %s: worst %.3g" % (fmt, name, np.max(d / bound))
+        del W, Wq, S

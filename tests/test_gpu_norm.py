@@ -1,7 +1,6 @@
 """GPU parity of the RMSNorm prologue (lin_gemv_bf16_norm, lin_gemv_q4g64_norm)
 against the oracle's RMSNorm followed by the oracle's product (and epilogue),
-through the C ABI, for every staged configuration of the plain product of the
-same matrix and for the staged form of an unstaged one.
+through the C ABI, for every candidate configuration of the prologue kinds.
 
 Bound per output: the product's bound on the oracle's h (1e-3 * sum_k |W h|,
 propagated through the epilogue as in the epilogue tests) plus 2^-8 |W[n][k]
@@ -51,22 +50,20 @@ def _case(fmt, NW, K, seed):
     if fmt == "bf16":
         Y, B = oracle.gemm_dense(u16(W), h)
         _, Bw = oracle.gemm_dense(u16(W), hw)
-        Wt, kind, fn = (W.to(DEV),), L.LIN_KIND_GEMV_BF16, L.lin_gemv_bf16_norm
+        Wt, kind, fn = (W.to(DEV),), L.LIN_KIND_GEMV_BF16_NORM, L.lin_gemv_bf16_norm
     else:
         Wq, S = oracle.quantize_q4g64(u16(W))
         Y, B = oracle.gemm_q4g64(Wq, S, h)
         _, Bw = oracle.gemm_q4g64(Wq, S, hw)
         Wt = (torch.from_numpy(Wq).to(DEV), synth.from_bits(S, torch.float16, DEV))
-        kind, fn = L.LIN_KIND_GEMV_Q4G64, L.lin_gemv_q4g64_norm
+        kind, fn = L.LIN_KIND_GEMV_Q4G64_NORM, L.lin_gemv_q4g64_norm
     gd = synth.from_bits(g, torch.bfloat16, DEV)
     return Wt, x.to(DEV), gd, Y[0], 1e-3 * B[0] + 2.0 ** -8 * Bw[0], kind, fn
 
 
 def _configs(kind, NW, K):
-    """Every staged candidate, plus one unstaged one (run in its staged form)."""
-    cands = L.lin_candidates(kind, 1, NW, K)
-    staged = [c for c in cands if c["stage_x"] == 1]
-    return staged + [c for c in cands if c["stage_x"] == 0][:1]
+    """Every candidate of the prologue kind."""
+    return L.lin_candidates(kind, 1, NW, K)
 
 
 def _check(y, expect, bound, what):

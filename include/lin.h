@@ -21,7 +21,10 @@
  *   x/X bf16    [M][K]     activations, one row per token
  *   y/Y fp32    [M][N]     outputs, overwritten (no accumulation into y)
  * Accumulation is fp32.  The result of every configuration is within
- * 1e-3 * sum_k |W[n][k] * x[m][k]| of the exact product, per output.
+ * 1e-3 * sum_k |W[n][k] * x[m][k]| of the exact product, per output.  (The
+ * int4 products multiply the codes as 136 + q and remove 136 * sum x per 32 or
+ * 64 weights in fp32, which adds up to about 2.7e-4 * sum |x| per 32 weights:
+ * inside the bound unless most codes of a group are zero.)
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points

@@ -23,8 +23,8 @@
  * Accumulation is fp32.  The result of every configuration is within
  * 1e-3 * sum_k |W[n][k] * x[m][k]| of the exact product, per output.  (The
  * int4 products multiply the codes as 136 + q and remove 136 * sum x per 32 or
- * 64 weights in fp32, which adds up to about 2.7e-4 * sum |x| per 32 weights:
- * inside the bound unless most codes of a group are zero.)
+ * 64 weights in fp32, which adds up to about 2.7e-4 * s * sum |x| per 32
+ * weights of scale s: inside the bound unless most codes of a group are zero.)
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points

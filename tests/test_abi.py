@@ -225,6 +225,12 @@ def test_norm_kind_candidates():
         assert L._lib.lin_num_candidates(kind, 1, 2048, 0) == L.LIN_ERR_SHAPE
         big = L.lin_candidates(kind, 1, 64, 65536)
         assert len(big) < len(L.lin_candidates(kind, 1, 64, 4096))
+    # x and gain copies beyond LDS: no configuration, the call is refused
+    assert L.lin_candidates(L.LIN_KIND_GEMV_Q4G64_NORM, 1, 9, 32768) == []
+    assert L._lib.lin_gemv_q4g64_norm(P, P, P, P, 1e-6, P, 1, 9, 32768, 0, None, None) == \
+        L.LIN_ERR_UNSUPPORTED
+    assert L._lib.lin_gemv_bf16_norm(P, P, P, 1e-6, P, 1, 9, 65536, 0, None, None) == \
+        L.LIN_ERR_UNSUPPORTED
 
 
 def test_default_skinny_config_needs_no_workspace():

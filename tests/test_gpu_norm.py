@@ -127,6 +127,28 @@ def test_norm_with_epilogues(fmt, N, K):
             L.lin_set_config(kind, 1, 2 * N, K, None)
 
 
+@pytest.mark.parametrize("fmt,N,K", [("bf16", 3, 8), ("bf16", 17, 520), ("bf16", 9, 32768),
+                                     ("q4", 7, 64), ("q4", 17, 576), ("q4", 9, 16384)])
+def test_norm_edge_shapes(fmt, N, K):
+    """The smallest K of each format, K not a multiple of the 512 (bf16) or
+    2048 (int4) weights a wavefront step covers, and K near the largest whose
+    x and gain copies fit in LDS; every candidate, with and without the gated
+    epilogue."""
+    print("case norm edge %s N=%d K=%d" % (fmt, N, K), flush=True)
+    Wt, x, g, Y, bound, kind, fn = _case(fmt, N, K, 14000 + N + K)
+    cands = _configs(kind, N, K)
+    assert cands
+    for cfg in cands:
+        L.lin_set_config(kind, 1, N, K, cfg)
+        try:
+            y = torch.full((1, N), float("nan"), device=DEV)
+            fn(*Wt, x, g, EPS, y=y)
+            torch.cuda.synchronize()
+            _check(y, Y, bound, "norm edge %s %s" % (fmt, cfg))
+        finally:
+            L.lin_set_config(kind, 1, N, K, None)
+
+
 def test_identity_weights_return_the_normalised_row():
     """W = I in bf16: y[k] = h[k] exactly (one exact product per output), so the
     kernel's h is compared with the oracle's entry by entry; entries away from a

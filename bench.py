@@ -9,7 +9,7 @@ the value is the achieved HBM rate over the algorithmic bytes of the step.
 Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line (see the keys below).  --gpus N with N > 1 is refused:
-this build measures one GPU.
+the benchmark measures one GPU.
 """
 import argparse
 import concurrent.futures

@@ -230,10 +230,32 @@ def variant_key(m):
                                    c["stage_x"])
 
 
+def replay_times(g, reps, warmup):
+    """Durations (s) of `reps` replays of a graph, each bracketed by its own HIP
+    events on the stream the replays run on."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) / 1000.0 for a, b in ev]
+
+
+def quartiles(ts):
+    q1, q2, q3 = np.percentile(np.asarray(ts, dtype=np.float64), [25, 50, 75])
+    return q2, q3 - q1
+
+
 def kernel_times(mats, reps):
-    """Average duration per launch of each kernel (variant and shape), measured
-    live with HIP events around graph replays that hold only that kernel's
-    launches (at least 64, in step order).  Queued kernels start as the
+    """Duration per launch of each kernel (variant and shape), measured live with
+    HIP events around each of `reps` graph replays that hold only that kernel's
+    launches (at least 64, in step order): mean over the replays, and median and
+    interquartile range of the per-replay figures.  Queued kernels start as the
     previous one ends, so elapsed time / launches is the kernel's own duration."""
     by = {}
     for m in mats:
@@ -242,20 +264,13 @@ def kernel_times(mats, reps):
     for (variant, shape), ms in by.items():
         rep = max(1, -(-64 // len(ms)))   # at least 64 launches per replay
         g = capture(ms * rep)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        per_launch = e0.elapsed_time(e1) / 1000.0 / (reps * rep * len(ms))
+        ts = [t / (rep * len(ms)) for t in replay_times(g, reps, 2)]
+        per_launch = float(np.mean(ts))
+        med, iqr = quartiles(ts)
         out["%s %s" % (variant, shape)] = {
-            "variant": variant, "shape": shape, "avg_s": per_launch, "launches": len(ms),
-            "bytes_per_launch": ms[0].bytes, "step_s": per_launch * len(ms)}
+            "variant": variant, "shape": shape, "avg_s": per_launch, "median_s": med,
+            "iqr_s": iqr, "launches": len(ms), "bytes_per_launch": ms[0].bytes,
+            "step_s": per_launch * len(ms)}
         del g
     return out
 
@@ -407,15 +422,17 @@ def run_skinny(args, dev, fmt):
         fn = L.lin_gemm_skinny_bf16 if fmt == "bf16" else L.lin_gemm_skinny_q4g64
         return lambda: fn(Wc[i % len(Wc)], X[(c.M, c.K)], Y[c.key])
 
-    reps = max(5, args.steps // 2)
+    reps = max(30, args.steps)
     per_case = {}
     for c in cases:
         n = max(32, 2 * len(weights[(c.N, c.K)]))
         g = graph_of([call(c, i) for i in range(n)])
-        _, gpu = time_graph(g, reps, 2)
-        us = gpu / n * 1e6
+        ts = [t / n for t in replay_times(g, reps, 2)]
+        us = float(np.mean(ts)) * 1e6
+        med, iqr = quartiles(ts)
         floor_us = max(c.bytes / (HBM_PEAK_GBS * 1e3), c.flop / (MFMA_PEAK_TFS * 1e6))
         per_case[c.name] = {"variant": skinny_variant(c), "us": round(us, 3),
+                            "median_us": round(med * 1e6, 3), "iqr_us": round(iqr * 1e6, 3),
                             "GB_s": round(c.bytes / us / 1e3, 1),
                             "TFLOP_s": round(c.flop / us / 1e6, 1),
                             "hbm_frac": round(c.bytes / us / 1e3 / HBM_PEAK_GBS, 4),
@@ -754,17 +771,25 @@ def main():
     graphs = {f: capture(sets[f]) for f in sets}
     per_fmt = {}
     for f in fmts:
-        _, gpu_f = time_graph(graphs[f], max(5, args.steps // 2), args.warmup)
+        ts = replay_times(graphs[f], max(30, args.steps), args.warmup)
+        gpu_f = float(np.mean(ts))
+        med, iqr = quartiles(ts)
+        # the same pass without the graph: one host call per matrix
+        eager, _ = time_runs([lambda f=f: [launch(m) for m in sets[f]]], max(10, args.steps // 2),
+                             args.warmup)
         per_fmt[f] = {"ms_per_token": round(gpu_f * 1e3, 4), "equiv_tok_s": round(1.0 / gpu_f, 1),
-                      "GB_s": round(fmt_bytes[f] / gpu_f / 1e9, 1), "bytes": fmt_bytes[f]}
-        log("%s step: %.1f us, %.1f GB/s, %.0f tok/s" % (f, gpu_f * 1e6, fmt_bytes[f] / gpu_f / 1e9,
-                                                        1 / gpu_f))
+                      "GB_s": round(fmt_bytes[f] / gpu_f / 1e9, 1), "bytes": fmt_bytes[f],
+                      "median_ms": round(med * 1e3, 4), "iqr_ms": round(iqr * 1e3, 4),
+                      "no_graph_ms_per_token": round(eager * 1e3, 4)}
+        log("%s step: %.1f us (median %.1f, IQR %.1f), %.1f GB/s, %.0f tok/s; without the graph "
+            "%.1f us" % (f, gpu_f * 1e6, med * 1e6, iqr * 1e6, fmt_bytes[f] / gpu_f / 1e9, 1 / gpu_f,
+                         eager * 1e6))
     # the timed region: K steps of the whole path (one decode pass per format, in order)
     torch.cuda.synchronize()
     wall, gpu = time_runs([graphs[f].replay for f in fmts], args.steps, args.warmup)
     gbs = step_bytes / wall / 1e9
 
-    kt = kernel_times(allm, reps=max(5, args.steps // 2))
+    kt = kernel_times(allm, reps=max(30, args.steps))
     dom_key = max(kt, key=lambda k: kt[k]["step_s"])
     dom = kt[dom_key]
     achieved = dom["bytes_per_launch"] / dom["avg_s"] / 1e9
@@ -779,7 +804,8 @@ def main():
                 "avg_launch_us": round(dom["avg_s"] * 1e6, 3),
                 "bytes_per_launch": int(dom["bytes_per_launch"]),
                 "share_of_step": round(dom["step_s"] / gpu, 3)}
-    kernels = {k: {"avg_us": round(v["avg_s"] * 1e6, 3), "launches": v["launches"],
+    kernels = {k: {"avg_us": round(v["avg_s"] * 1e6, 3), "median_us": round(v["median_s"] * 1e6, 3),
+                   "iqr_us": round(v["iqr_s"] * 1e6, 3), "launches": v["launches"],
                    "GB_s": round(v["bytes_per_launch"] / v["avg_s"] / 1e9, 1),
                    "read_ceiling_GB_s": round(ceil[k], 1)}
                for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["step_s"])}

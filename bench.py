@@ -657,21 +657,48 @@ def cpu_baseline(model, layers, threads, fmts=("bf16", "q4")):
         else:
             oracle.gemm_i8(A[lo:hi], S[lo:hi], x)
 
-    jobs = []
-    for item in work:
-        N = item[1].shape[0]
-        step = max(1, N // (4 * threads))
-        jobs += [(item, lo, min(N, lo + step)) for lo in range(0, N, step)]
-    t0 = time.perf_counter()
-    with concurrent.futures.ThreadPoolExecutor(threads) as ex:
-        list(ex.map(lambda j: run_rows(*j), jobs))
-    dt = time.perf_counter() - t0
-    return {"value": round(total_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+    def timed(items, nthreads):
+        jobs = []
+        for item in items:
+            N = item[1].shape[0]
+            step = max(1, N // (4 * nthreads))
+            jobs += [(item, lo, min(N, lo + step)) for lo in range(0, N, step)]
+        t0 = time.perf_counter()
+        with concurrent.futures.ThreadPoolExecutor(nthreads) as ex:
+            list(ex.map(lambda j: run_rows(*j), jobs))
+        return time.perf_counter() - t0
+
+    dt = timed(work, threads)
+    # one thread on the first layer's matrices (a shorter sample of the same work)
+    first = work[:len(fmts) * len(model["layer"])]
+    dt1 = timed(first, 1)
+    b1 = sum(w[4] for w in first)
+    step_bytes = sum((bytes_bf16 if f == "bf16" else bytes_q4 if f == "q4" else bytes_i8)(N, K)
+                     for f in fmts for _, _, _, N, K in synth.decode_matrices(model))
+    gbs = total_bytes / dt / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "%s layers 0-%d (%d matrices), %s, %.1f MB of weights, "
                       "batch 1, fp64 sequential sums, %.2f s wall"
                       % (model["name"], layers - 1, len(work) // len(fmts),
-                         " and ".join(FORMAT_NAMES[f] for f in fmts), total_bytes / 1e6, dt)}
+                         " and ".join(FORMAT_NAMES[f] for f in fmts), total_bytes / 1e6, dt),
+            "s_per_step": round(step_bytes / (gbs * 1e9), 3),
+            "equiv_tok_s": round(gbs * 1e9 / step_bytes, 4),
+            "one_thread": {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s",
+                           "sample": "layer 0 (%d matrices), %.1f MB, %.2f s wall"
+                                     % (len(first) // len(fmts), b1 / 1e6, dt1)},
+            "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline_skinny(threads, fmt="bf16", rows=96):

@@ -851,6 +851,10 @@ def main():
            "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
            "gpu_ms_per_step": round(gpu * 1e3, 4),
            "per_format": per_fmt, "kernels": kernels, "roofline": roofline}
+    # context: what a plain read of 4 GB reaches on this part (not the metric's denominator)
+    big = read_ceiling(4 << 30, dev, 5)
+    out["achievable_read"] = {"bytes": 4 << 30, "GB_s": round(big, 1),
+                              "frac_of_peak": round(big / HBM_PEAK_GBS, 4)}
     if args.epilogues:
         if not fused:
             print("--epilogues needs the concatenated gate|up projections (no --no-fuse)", file=sys.stderr)

@@ -9,6 +9,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <utility>
 #include <vector>
 
 #include "../../include/lin.h"
@@ -217,12 +218,15 @@ int ensure_workspace(int dev, size_t bytes) {
 }
 
 // Dynamic LDS above the default 64 KB per workgroup must be allowed per
-// kernel first; the largest size allowed so far is kept per kernel.
+// kernel and device first; the largest size allowed so far is kept per
+// (device, kernel).
 bool allow_lds(size_t lds, const void* func) {
     if (lds <= 64 * 1024) return true;
-    static auto* allowed = new std::map<const void*, size_t>();
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    static auto* allowed = new std::map<std::pair<int, const void*>, size_t>();
     std::lock_guard<std::mutex> lk(g_mu);
-    auto ins = allowed->emplace(func, (size_t)64 * 1024);
+    auto ins = allowed->emplace(std::make_pair(dev, func), (size_t)64 * 1024);
     size_t& cur = ins.first->second;
     if (lds <= cur) return true;
     if (hipFuncSetAttribute(func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)

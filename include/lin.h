@@ -43,7 +43,8 @@
  * LIN_ERR_HIP means the HIP runtime reported an error (for example a launch
  * failure); the stream may then hold partial work.  No C++ exception crosses
  * this interface.  M == 0 or N == 0 is a valid empty call (nothing is enqueued;
- * pointers may be NULL).  K == 0 writes zeros to y (W and x may be NULL).
+ * pointers may be NULL).  K == 0 writes zeros to y (W and x may be NULL), except
+ * for the RMSNorm products, which need K >= 1 (LIN_ERR_SHAPE).
  */
 #ifndef LIN_H
 #define LIN_H

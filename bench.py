@@ -443,7 +443,7 @@ def run_skinny(args, dev, fmt):
         fn = L.lin_gemm_skinny_bf16 if fmt == "bf16" else L.lin_gemm_skinny_q4g64
         return lambda: fn(Wc[i % len(Wc)], X[(c.M, c.K)], Y[c.key])
 
-    reps = max(30, args.steps)
+    reps = max(1, args.kernel_reps)
     per_case = {}
     for c in cases:
         n = max(32, 2 * len(weights[(c.N, c.K)]))
@@ -768,6 +768,9 @@ def main():
                     help="also time decode passes with the residual adds and the gated silu "
                          "product (and then also the RMSNorm of the projection inputs), fused "
                          "into the products against separate PyTorch ops")
+    ap.add_argument("--kernel-reps", type=int, default=30, metavar="N",
+                    help="graph replays per kernel variant for the per-kernel timings (default 30; "
+                         "counter passes under a profiler use 1)")
     ap.add_argument("--save-tuning", default=None, metavar="PATH",
                     help="write the tuning table, with any entries tuned by this run, to PATH")
     ap.add_argument("--no-fuse", action="store_true",
@@ -837,11 +840,12 @@ def main():
     wall, gpu = time_runs([graphs[f].replay for f in fmts], args.steps, args.warmup)
     gbs = step_bytes / wall / 1e9
 
-    kt = kernel_times(allm, reps=max(30, args.steps))
+    kt = kernel_times(allm, reps=args.kernel_reps)
     dom_key = max(kt, key=lambda k: kt[k]["step_s"])
     dom = kt[dom_key]
     achieved = dom["bytes_per_launch"] / dom["avg_s"] / 1e9
-    ceil = {k: read_ceiling(v["bytes_per_launch"], dev, max(5, args.steps // 2)) for k, v in kt.items()}
+    ceil = {k: read_ceiling(v["bytes_per_launch"], dev, max(1, min(5, args.kernel_reps)))
+            for k, v in kt.items()}
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom["variant"], {dom["shape"]: 1}),
@@ -873,7 +877,7 @@ def main():
            "gpu_ms_per_step": round(gpu * 1e3, 4),
            "per_format": per_fmt, "kernels": kernels, "roofline": roofline}
     # context: what a plain read of 4 GB reaches on this part (not the metric's denominator)
-    big = read_ceiling(4 << 30, dev, 5)
+    big = read_ceiling(4 << 30, dev, max(1, min(5, args.kernel_reps)))
     out["achievable_read"] = {"bytes": 4 << 30, "GB_s": round(big, 1),
                               "frac_of_peak": round(big / HBM_PEAK_GBS, 4)}
     if args.epilogues:

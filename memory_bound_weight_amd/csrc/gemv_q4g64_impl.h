@@ -67,6 +67,21 @@ __device__ __forceinline__ void pair_x(const u32x4 (&xd)[4], XChunk& out) {
     out.negsum = -136.f * s;
 }
 
+// One 16-byte unit of x (natural dwords d0..d3 = x[8d+0..7] of a chunk's unit
+// d) re-paired as pair_x does for it, and the unit's sum of its 8 values.
+__device__ __forceinline__ u32x4 pair_unit(const u32x4& a, float& s) {
+    u32x4 o;
+    o[0] = __builtin_amdgcn_perm(a[2], a[0], 0x05040100u);
+    o[1] = __builtin_amdgcn_perm(a[2], a[0], 0x07060302u);
+    o[2] = __builtin_amdgcn_perm(a[3], a[1], 0x05040100u);
+    o[3] = __builtin_amdgcn_perm(a[3], a[1], 0x07060302u);
+    s = dot2(a[0], 0x3F803F80u, 0.f);
+    s = dot2(a[1], 0x3F803F80u, s);
+    s = dot2(a[2], 0x3F803F80u, s);
+    s = dot2(a[3], 0x3F803F80u, s);
+    return o;
+}
+
 // Sum over one chunk of 32 codes times re-paired x, minus the code offset.
 // ((w >> 4i) & 0x000F000F) ^ 0x43084308 equals ((w ^ 0x88888888) >> 4i &
 // 0x000F000F) | 0x43004300: the sign flip and the bf16 exponent bits go in with
@@ -250,17 +265,26 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
             wait_cnt<0, 15>();
         }
         barrier_only();
-        if constexpr (NORM) rms_norm_lds(xraw, xraw + stage_x_units(MT, K), K, a.eps);
-        for (int i = threadIdx.x; i < MT * nch; i += kBlock) {
-            const int m = i / nch;
-            const int c = i - m * nch;
-            const u32x4* src = xraw + (size_t)m * (K >> 3) + 4 * c;
-            const u32x4 xd[4] = {src[0], src[1], src[2], src[3]};
-            XChunk xc;
-            pair_x(xd, xc);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) xs[(m * 4 + t) * nch + c] = xc.v[t];
-            xsum[m * nch + c] = xc.negsum;
+        // One thread per 16-byte unit: re-pair it (with NORM, normalise it
+        // first) and sum its values; the four units of a chunk sit in the
+        // four lanes of a quad (K / 8 is a multiple of 4), which add their
+        // sums with two DPP steps.
+        float inv = 1.f;
+        if constexpr (NORM) inv = rms_inv_lds(xraw, K, a.eps);
+        const u32x4* graw = xraw + stage_x_units(MT, K);
+        const int upr = K >> 3;   // 16-byte units per token row
+        for (int u = threadIdx.x; u < MT * upr; u += kBlock) {
+            const int m = u / upr;
+            const int j = u - m * upr;
+            const int c = j >> 2, d = j & 3;
+            u32x4 v = xraw[u];
+            if constexpr (NORM) v = rms_scale_unit(v, graw[j], inv);
+            float sum;
+            const u32x4 p = pair_unit(v, sum);
+            sum += dpp<0xB1>(sum);   // quad_perm [1,0,3,2]
+            sum += dpp<0x4E>(sum);   // quad_perm [2,3,0,1]
+            xs[(m * 4 + d) * nch + c] = p;
+            if (d == 0) xsum[m * nch + c] = -136.f * sum;
         }
         wait_cnt<63, 0>();   // LDS writes done, weight loads still in flight
         barrier_only();

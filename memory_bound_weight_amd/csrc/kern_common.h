@@ -217,14 +217,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 // RMSNorm prologue of a batch-1 product (tinyinfer post, decode section: the
-// normalisation folded into the projection kernel), in place on the token row
-// staged in LDS: x[k] <- bf16(x[k] g[k] / sqrt(sum_k x[k]^2 / K + eps)).  x and g
-// are K bf16 in natural order (K / 8 16-byte units each), already visible to
-// the whole workgroup.  The sum of squares is fp32 (per-thread partial sums,
-// then the wavefront tree and four wavefront totals in a fixed order), x g is
-// exact in fp32 and the product with the reciprocal is rounded once to fp32
-// and once to bf16.  Only LDS is waited for: weight loads stay in flight.
-__device__ __forceinline__ void rms_norm_lds(u32x4* x, const u32x4* g, int K, float eps) {
+// normalisation folded into the projection kernel), on the token row staged in
+// LDS: h[k] = bf16(x[k] g[k] / sqrt(sum_k x[k]^2 / K + eps)).  x and g are K bf16
+// in natural order (K / 8 16-byte units each), already visible to the whole
+// workgroup.  Only LDS is waited for: weight loads stay in flight.
+//
+// rms_inv_lds: 1 / sqrt(sum_k x[k]^2 / K + eps), the same value in every
+// thread.  The sum of squares is fp32: per-thread partial sums, the wavefront
+// tree, then the four wavefront totals in a fixed order.  Ends with a barrier.
+__device__ __forceinline__ float rms_inv_lds(const u32x4* x, int K, float eps) {
     __shared__ float part[4];
     const int n = K >> 3;
     float ss[1] = {0.f};
@@ -241,18 +242,26 @@ __device__ __forceinline__ void rms_norm_lds(u32x4* x, const u32x4* g, int K, fl
     if ((threadIdx.x & 63) == 0) part[wave_id()] = ss[0];
     wait_cnt<63, 0>();
     barrier_only();
-    const float inv = 1.f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)K + eps);
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        const u32x4 v = x[i], gv = g[i];
-        u32x4 o;
+    return 1.f / sqrtf(((part[0] + part[1]) + (part[2] + part[3])) / (float)K + eps);
+}
+
+// h for one 16-byte unit of x and the matching unit of g: x g is exact in
+// fp32, the product with inv is rounded once to fp32 and once to bf16.
+__device__ __forceinline__ u32x4 rms_scale_unit(const u32x4& v, const u32x4& gv, float inv) {
+    u32x4 o;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float lo = bitsf(v[j] << 16) * bitsf(gv[j] << 16) * inv;
-            const float hi = bitsf(v[j] & 0xFFFF0000u) * bitsf(gv[j] & 0xFFFF0000u) * inv;
-            o[j] = bf16_rne(lo) | (bf16_rne(hi) << 16);
-        }
-        x[i] = o;
+    for (int j = 0; j < 4; ++j) {
+        const float lo = bitsf(v[j] << 16) * bitsf(gv[j] << 16) * inv;
+        const float hi = bitsf(v[j] & 0xFFFF0000u) * bitsf(gv[j] & 0xFFFF0000u) * inv;
+        o[j] = bf16_rne(lo) | (bf16_rne(hi) << 16);
     }
+    return o;
+}
+
+// The whole prologue in place on the staged row (the bf16 products read it as is).
+__device__ __forceinline__ void rms_norm_lds(u32x4* x, const u32x4* g, int K, float eps) {
+    const float inv = rms_inv_lds(x, K, eps);
+    for (int i = threadIdx.x; i < (K >> 3); i += kBlock) x[i] = rms_scale_unit(x[i], g[i], inv);
     wait_cnt<63, 0>();
     barrier_only();
 }

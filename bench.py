@@ -115,7 +115,8 @@ def tune_key(m):
     return (kind_of(m), 1, m.N, m.K)
 
 
-NORM_KINDS = {"bf16": L.LIN_KIND_GEMV_BF16_NORM, "q4": L.LIN_KIND_GEMV_Q4G64_NORM}
+NORM_KINDS = {"bf16": L.LIN_KIND_GEMV_BF16_NORM, "q4": L.LIN_KIND_GEMV_Q4G64_NORM,
+              "i8": L.LIN_KIND_GEMV_I8_NORM}
 NORM_OF = ("q|k|v", "gate|up", "head")   # projections whose input is RMS-normalised
 
 
@@ -534,11 +535,15 @@ def fused_call(m, e, nrm):
     if nrm:
         if m.fmt == "bf16":
             return lambda: L.lin_gemv_bf16_norm(m.W, m.x, m.gain, NORM_EPS, e, r=r, y=y)
+        if m.fmt == "i8":
+            return lambda: L.lin_gemv_i8_norm(m.Wq, m.S, m.x, m.gain, NORM_EPS, e, r=r, y=y)
         return lambda: L.lin_gemv_q4g64_norm(m.Wq, m.S, m.x, m.gain, NORM_EPS, e, r=r, y=y)
     if e == L.LIN_EPI_NONE:
         return lambda: launch(m)
     if m.fmt == "bf16":
         return lambda: L.lin_gemv_bf16_ep(m.W, m.x, e, r=r, y=y)
+    if m.fmt == "i8":
+        return lambda: L.lin_gemv_i8_ep(m.Wq, m.S, m.x, e, r=r, y=y)
     return lambda: L.lin_gemv_q4g64_ep(m.Wq, m.S, m.x, e, r=r, y=y)
 
 
@@ -560,6 +565,8 @@ def epilogue_step(mats, fused, norms=False):
             fns.append(lambda m=m: torch_rmsnorm(m.x, m.gain, NORM_EPS, m.xn))
             if m.fmt == "bf16":
                 fns.append(lambda m=m: L.lin_gemv_bf16(m.W, m.xn, m.y))
+            elif m.fmt == "i8":
+                fns.append(lambda m=m: L.lin_gemv_i8(m.Wq, m.S, m.xn, m.y))
             else:
                 fns.append(lambda m=m: L.lin_gemv_q4g64(m.Wq, m.S, m.xn, m.y))
         else:
@@ -619,8 +626,6 @@ def run_epilogues(sets, fmts, args):
     RMSNorm prologues), and the per-kernel cost of the prologue; per format."""
     out = {}
     for f in fmts:
-        if f not in ("bf16", "q4"):
-            continue
         res = {}
         for norms in (False, True):
             part = {}

@@ -29,7 +29,7 @@
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points
  * (lin_gemv_bf16, lin_gemv_q4g64, lin_gemv_bf16_ep, lin_gemv_q4g64_ep,
- * lin_gemv_bf16_norm, lin_gemv_q4g64_norm, lin_gemv_i8,
+ * lin_gemv_bf16_norm, lin_gemv_q4g64_norm, lin_gemv_i8, lin_gemv_i8_ep, lin_gemv_i8_norm,
  * lin_gemm_skinny_bf16,
  * lin_gemm_skinny_q4g64, lin_quantize_q4g64, lin_quantize_i8, lin_q4g64_tile)
  * validate their arguments in O(1), enqueue kernels on `stream` (a hipStream_t;
@@ -73,7 +73,8 @@ typedef enum lin_kind {
     LIN_KIND_SKINNY_Q4G64 = 3, /* lin_gemm_skinny_q4g64 (tiled int4-g64 weights) */
     LIN_KIND_GEMV_I8 = 4,      /* lin_gemv_i8 */
     LIN_KIND_GEMV_BF16_NORM = 5,  /* lin_gemv_bf16_norm (M == 1) */
-    LIN_KIND_GEMV_Q4G64_NORM = 6  /* lin_gemv_q4g64_norm (M == 1) */
+    LIN_KIND_GEMV_Q4G64_NORM = 6, /* lin_gemv_q4g64_norm (M == 1) */
+    LIN_KIND_GEMV_I8_NORM = 7     /* lin_gemv_i8_norm (M == 1) */
 } lin_kind;
 
 /* Kernel families. */
@@ -188,6 +189,17 @@ int lin_gemv_q4g64_norm(const void* Wq, const void* S, const void* x, const void
 int lin_gemv_i8(const void* Wi, const void* Si, const void* x, float* y,
                 int64_t M, int64_t N, int64_t K, void* stream);
 
+/* lin_gemv_i8 for M == 1 with a fused epilogue (as lin_gemv_bf16_ep; the gated
+ * product applies each row's scale before the gate: silu(Si[n] g_n) Si[N+n] u_n,
+ * with Si holding the 2N scales of the gate|up rows), and with the RMSNorm
+ * prologue as well (as lin_gemv_bf16_norm; kind LIN_KIND_GEMV_I8_NORM, K >= 16).
+ * Same argument rules and bounds as those entry points. */
+int lin_gemv_i8_ep(const void* Wi, const void* Si, const void* x, float* y,
+                   int64_t M, int64_t N, int64_t K, int epilogue, const float* r, void* stream);
+int lin_gemv_i8_norm(const void* Wi, const void* Si, const void* x, const void* g, float eps,
+                     float* y, int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
+                     void* stream);
+
 /* Batched-token product Y = X . W^T for 1 <= M <= LIN_SKINNY_MAX_M tokens,
  * K % 8 == 0.  Small M streams W once through the vector ALUs; larger M runs on
  * the matrix cores; the crossover is part of the tuned configuration. */
@@ -232,7 +244,7 @@ int lin_q4g64_tile(const void* Wq, const void* S, void* Wt, void* St,
  * candidate configuration of `kind` for (M, N, K) on the caller's buffers,
  * which must be valid for that kind (S is used only by the int4 and INT8 kinds
  * and may be NULL otherwise; W and S are Wt and St for LIN_KIND_SKINNY_Q4G64, Wi
- * and Si for LIN_KIND_GEMV_I8; for the RMSNorm kinds M must be 1 and x also
+ * and Si for LIN_KIND_GEMV_I8 and LIN_KIND_GEMV_I8_NORM; for the RMSNorm kinds M must be 1 and x also
  * stands in for the gain; y receives scratch results).  Each timed call starts
  * from cold caches.  The fastest configuration is stored in the per-device
  * table and used by later calls with the same (kind, M, N, K); if `out` is not

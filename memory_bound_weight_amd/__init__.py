@@ -31,6 +31,7 @@ LIN_KIND_SKINNY_Q4G64 = 3
 LIN_KIND_GEMV_I8 = 4
 LIN_KIND_GEMV_BF16_NORM = 5
 LIN_KIND_GEMV_Q4G64_NORM = 6
+LIN_KIND_GEMV_I8_NORM = 7
 
 LIN_EPI_NONE = 0
 LIN_EPI_ADD = 1
@@ -44,7 +45,8 @@ LIN_SKINNY_MAX_M = 256
 
 # Every symbol include/lin.h declares.
 EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemv_bf16_ep", "lin_gemv_q4g64_ep",
-           "lin_gemv_bf16_norm", "lin_gemv_q4g64_norm", "lin_gemv_i8", "lin_gemm_skinny_bf16",
+           "lin_gemv_bf16_norm", "lin_gemv_q4g64_norm", "lin_gemv_i8", "lin_gemv_i8_ep",
+           "lin_gemv_i8_norm", "lin_gemm_skinny_bf16",
            "lin_gemm_skinny_q4g64", "lin_quantize_i8",
            "lin_q4g64_tiled_size", "lin_q4g64_tile", "lin_autotune",
            "lin_autotune_set", "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
@@ -89,6 +91,8 @@ def _load():
         "lin_gemv_q4g64_ep": [P, P, P, P, I64, I64, I64, I, P, P],
         "lin_gemv_bf16_norm": [P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P],
         "lin_gemv_q4g64_norm": [P, P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P],
+        "lin_gemv_i8_ep": [P, P, P, P, I64, I64, I64, I, P, P],
+        "lin_gemv_i8_norm": [P, P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P],
         "lin_quantize_i8": [P, P, P, I64, I64, P],
         "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
         "lin_gemm_skinny_q4g64": [P, P, P, P, I64, I64, I64, P],
@@ -293,6 +297,40 @@ def lin_gemv_i8(Wq, S, x, y=None):
     y = _out(y, M, N, Wq.device)
     _check(_lib.lin_gemv_i8(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K,
                             _stream(Wq)), "lin_gemv_i8")
+    return y
+
+
+def _i8_args(Wq, S, x):
+    x = _as2d(x)
+    _need(Wq, torch.int8, "Wq", 2)
+    _need(S, torch.float32, "S", 1)
+    _need(x, torch.bfloat16, "x", 2)
+    NW, K = Wq.shape
+    if x.shape != (1, K) or tuple(S.shape) != (NW,):
+        raise ValueError("shape mismatch: Wq [N, K], S [N], x [1, K]")
+    return x, NW, K
+
+
+def lin_gemv_i8_ep(Wq, S, x, epilogue, r=None, y=None):
+    """Batch-1 INT8 product with a fused epilogue (see lin_gemv_bf16_ep); with the
+    gated epilogue, each row's scale is applied before the gate."""
+    x, NW, K = _i8_args(Wq, S, x)
+    N, y = _epi_out(epilogue, NW, r, y, Wq.device)
+    _check(_lib.lin_gemv_i8_ep(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, K,
+                               int(epilogue), r.data_ptr() if r is not None else None, _stream(Wq)),
+           "lin_gemv_i8_ep")
+    return y
+
+
+def lin_gemv_i8_norm(Wq, S, x, g, eps, epilogue=LIN_EPI_NONE, r=None, y=None):
+    """Batch-1 INT8 product of the RMSNorm of x (see lin_gemv_bf16_norm)."""
+    x, NW, K = _i8_args(Wq, S, x)
+    _norm_gain(g, K)
+    N, y = _epi_out(epilogue, NW, r, y, Wq.device)
+    _check(_lib.lin_gemv_i8_norm(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), g.data_ptr(), float(eps),
+                                 y.data_ptr(), 1, N, K, int(epilogue),
+                                 r.data_ptr() if r is not None else None, _stream(Wq)),
+           "lin_gemv_i8_norm")
     return y
 
 

@@ -5,9 +5,9 @@
 
 namespace lin {
 
-template <int MT, int R, int U, int SPLIT, bool STAGE>
+template <int MT, int R, int U, int SPLIT, bool STAGE, int EPI = kEpiNone, bool NORM = false>
 __global__ __launch_bounds__(kBlock) void gemv_i8_valu(KArgs a) {
-    gemv_i8_valu_block<MT, R, U, SPLIT, STAGE>(a, blockIdx.x);
+    gemv_i8_valu_block<MT, R, U, SPLIT, STAGE, EPI, NORM>(a, blockIdx.x);
 }
 
 template <int MT, int R, int U, int SPLIT, bool STAGE>
@@ -21,8 +21,18 @@ static bool geom_i8(const Variant&, int M, int N, int K, dim3* grid, size_t* lds
     return true;
 }
 
+// The RMSNorm prologue also stages the gain next to x.
+template <int MT, int R, int U, int SPLIT, bool STAGE>
+static bool geom_i8_norm(const Variant& v, int M, int N, int K, dim3* grid, size_t* lds) {
+    if (!geom_i8<MT, R, U, SPLIT, STAGE>(v, M, N, K, grid, lds)) return false;
+    *lds += 16 * stage_x_units(1, K);
+    return *lds <= kMaxDynLds;
+}
+
 template <int MT, int R, int U, int SPLIT, bool STAGE>
 static void add(std::vector<Variant>& out) {
+    // The gated form keeps R weight rows per wavefront (see gemv_bf16.hip).
+    constexpr int RS = R >= 2 ? R / 2 : 1;
     Variant v{};
     v.kind = LIN_KIND_GEMV_I8;
     v.cfg.algo = LIN_ALGO_VALU;
@@ -35,6 +45,19 @@ static void add(std::vector<Variant>& out) {
     v.min_m = MT / 2 + 1;
     v.func = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE>;
     v.geometry = &geom_i8<MT, R, U, SPLIT, STAGE>;
+    if constexpr (MT == 1) {
+        v.epi[kEpiAdd] = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
+        v.epi[kEpiSwiglu] = (const void*)&gemv_i8_valu<MT, RS, U, SPLIT, STAGE, kEpiSwiglu>;
+        if constexpr (STAGE) {
+            Variant n = v;
+            n.kind = LIN_KIND_GEMV_I8_NORM;
+            n.func = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE, kEpiNone, true>;
+            n.epi[kEpiAdd] = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE, kEpiAdd, true>;
+            n.epi[kEpiSwiglu] = (const void*)&gemv_i8_valu<MT, RS, U, SPLIT, STAGE, kEpiSwiglu, true>;
+            n.geometry = &geom_i8_norm<MT, R, U, SPLIT, STAGE>;
+            out.push_back(n);
+        }
+    }
     out.push_back(v);
 }
 

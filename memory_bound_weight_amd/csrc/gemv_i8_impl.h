@@ -17,6 +17,11 @@
 // row at the end: acc - 128 * sum(x), with sum(x) over the lane's chunks shared
 // by all rows.  The wavefront then reduces as usual and one lane per output
 // multiplies by the row's scale.
+//
+// Epilogues and prologue (batch 1) as in the bf16 kernel: EPI adds the
+// residual, or forms silu(s_g g) (s_u u) over the gate|up rows (each row's
+// own scale applied before the gate); NORM normalises the staged x in place
+// (RMSNorm, gain staged beside x) before the first product.
 #pragma once
 
 #include <type_traits>
@@ -25,9 +30,11 @@
 
 namespace lin {
 
-template <int MT, int R, int U, int SPLIT, bool STAGE>
+template <int MT, int R0, int U, int SPLIT, bool STAGE, int EPI = kEpiNone, bool NORM = false>
 __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block) {
+    static_assert(!NORM || (STAGE && MT == 1), "the prologue works on one staged token row");
     constexpr int GROUPS = 4 / SPLIT;
+    constexpr int R = EPI == kEpiSwiglu ? 2 * R0 : R0;   // weight rows per wavefront
     constexpr int V = R * MT;
     constexpr int STEP = kWave * U;   // chunks per pipeline step
     const int lane = threadIdx.x & 63;
@@ -41,15 +48,17 @@ __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block
     const float* __restrict__ S = (const float*)a.S;
     const uint16_t* __restrict__ X = (const uint16_t*)a.X;
 
-    extern __shared__ u32x4 xs[];   // STAGE: [MT][K/8] units of x
+    extern __shared__ u32x4 xs[];   // STAGE: [MT][K/8] units of x; NORM: then the gain
     if constexpr (STAGE) stage_x_dma(X, M, MT, K, xs);
+    if constexpr (NORM) stage_x_dma(a.G, 1, 1, K, xs + stage_x_units(MT, K));
 
-    const int64_t row0 = (block * GROUPS + grp) * R;
+    const int64_t row0 = (block * GROUPS + grp) * R0;   // first output row
     const uint8_t* wb[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        int64_t row = row0 + r;
+        int64_t row = row0 + r % R0;
         row = row < N ? row : N - 1;   // rows past N recompute row N-1; never stored
+        if (r >= R0) row += N;         // the up row of a gated product
         wb[r] = (const uint8_t*)(W + row * (int64_t)K);
     }
     const uint8_t* xb[MT];
@@ -143,17 +152,24 @@ __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block
     int cb = cbeg;
     Stage s0, s1;
     if (nsteps > 0) load(s0, cb);
+    bool s1_early = false;
     if constexpr (STAGE) {
-        // x copies were issued before the U R loads of stage 0 (see the bf16 kernel)
-        if (nsteps > 0)
+        // both weight stages stream while the x copies land (see the bf16 kernel)
+        if (nsteps > 1) {
+            load(s1, cb + STEP);
+            s1_early = true;
+            wait_cnt<2 * U * R, 15>();
+        } else if (nsteps > 0) {
             wait_cnt<U * R, 15>();
-        else
+        } else {
             wait_cnt<0, 15>();
+        }
         barrier_only();
+        if constexpr (NORM) rms_norm_lds(xs, xs + stage_x_units(MT, K), K, a.eps);
     }
     if (nsteps > 0) {
         for (int it = 0;;) {
-            if (it + 1 < nsteps) load(s1, cb + STEP);
+            if (it + 1 < nsteps && !(it == 0 && s1_early)) load(s1, cb + STEP);
             step(s0, cb);
             cb += STEP;
             if (++it >= nsteps) break;
@@ -170,10 +186,37 @@ __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block
         for (int m = 0; m < MT; ++m) acc[r * MT + m] = fmaf(-128.f, xsum[m], acc[r * MT + m]);
 
     wave_reduce<V>(acc);
-    if constexpr (SPLIT == 1) {
+    // y = scale * total (no scale read when K == 0), then the epilogue
+    if constexpr (EPI == kEpiSwiglu) {
+        // gate and up totals land in different lanes: meet in LDS
+        __shared__ float red[4][V];
+        for_each_reduced<V>(acc, lane, [&](int idx, float val) { red[wave][idx] = val; });
+        __syncthreads();
+        if (part == 0) {
+            for (int j = lane; j < R0 * MT; j += kWave) {
+                const int r = j / MT, m = j - (j / MT) * MT;
+                float g = red[wave][j], u = red[wave][R0 * MT + j];
+#pragma unroll
+                for (int p = 1; p < SPLIT; ++p) {
+                    g += red[wave + p][j];
+                    u += red[wave + p][R0 * MT + j];
+                }
+                if (m < M && row0 + r < N) {
+                    const float sg = K > 0 ? S[row0 + r] : 0.f;
+                    const float su = K > 0 ? S[N + row0 + r] : 0.f;
+                    a.Y[(int64_t)m * N + row0 + r] = silu_mul(sg * g, su * u);
+                }
+            }
+        }
+        __syncthreads();
+    } else if constexpr (SPLIT == 1) {
         for_each_reduced<V>(acc, lane, [&](int idx, float val) {
             const int r = idx / MT, m = idx - (idx / MT) * MT;
-            if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = K > 0 ? S[row0 + r] * val : 0.f;
+            const int64_t o = (int64_t)m * N + row0 + r;
+            if (m < M && row0 + r < N) {
+                const float v = K > 0 ? S[row0 + r] * val : 0.f;
+                a.Y[o] = EPI == kEpiAdd ? v + a.R[o] : v;
+            }
         });
     } else {
         __shared__ float red[4][V];
@@ -185,7 +228,11 @@ __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block
                 float t = red[wave][idx];
 #pragma unroll
                 for (int p = 1; p < SPLIT; ++p) t += red[wave + p][idx];
-                if (m < M && row0 + r < N) a.Y[(int64_t)m * N + row0 + r] = K > 0 ? S[row0 + r] * t : 0.f;
+                const int64_t o = (int64_t)m * N + row0 + r;
+                if (m < M && row0 + r < N) {
+                    const float v = K > 0 ? S[row0 + r] * t : 0.f;
+                    a.Y[o] = EPI == kEpiAdd ? v + a.R[o] : v;
+                }
             });
         }
         __syncthreads();

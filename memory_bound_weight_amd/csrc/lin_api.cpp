@@ -33,9 +33,10 @@ const std::vector<Variant>& registry() {
     return *reg;
 }
 
-bool valid_kind(int kind) { return kind >= LIN_KIND_GEMV_BF16 && kind <= LIN_KIND_GEMV_Q4G64_NORM; }
+bool valid_kind(int kind) { return kind >= LIN_KIND_GEMV_BF16 && kind <= LIN_KIND_GEMV_I8_NORM; }
 bool norm_kind(int kind) {
-    return kind == LIN_KIND_GEMV_BF16_NORM || kind == LIN_KIND_GEMV_Q4G64_NORM;
+    return kind == LIN_KIND_GEMV_BF16_NORM || kind == LIN_KIND_GEMV_Q4G64_NORM ||
+           kind == LIN_KIND_GEMV_I8_NORM;
 }
 
 using Key = std::tuple<int, int, int64_t, int64_t, int64_t>;   // device, kind, M, N, K
@@ -285,7 +286,7 @@ int check(int kind, const void* W, const void* S, const void* x, const float* y,
     if (M < 0 || N < 0 || K < 0) return LIN_ERR_SHAPE;
     const bool q4 = kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64 ||
                     kind == LIN_KIND_GEMV_Q4G64_NORM;
-    const bool i8 = kind == LIN_KIND_GEMV_I8;
+    const bool i8 = kind == LIN_KIND_GEMV_I8 || kind == LIN_KIND_GEMV_I8_NORM;
     const int64_t maxm = (kind == LIN_KIND_SKINNY_BF16 || kind == LIN_KIND_SKINNY_Q4G64)
                              ? LIN_SKINNY_MAX_M
                              : (norm_kind(kind) ? 1 : LIN_GEMV_MAX_M);
@@ -442,6 +443,17 @@ int lin_gemv_q4g64_norm(const void* Wq, const void* S, const void* x, const void
 int lin_gemv_i8(const void* Wq, const void* S, const void* x, float* y, int64_t M, int64_t N,
                 int64_t K, void* stream) {
     return run(LIN_KIND_GEMV_I8, Wq, S, x, y, M, N, K, stream);
+}
+
+int lin_gemv_i8_ep(const void* Wq, const void* S, const void* x, float* y, int64_t M, int64_t N,
+                   int64_t K, int epilogue, const float* r, void* stream) {
+    return run_epilogue(LIN_KIND_GEMV_I8, Wq, S, x, y, M, N, K, epilogue, r, stream);
+}
+
+int lin_gemv_i8_norm(const void* Wq, const void* S, const void* x, const void* g, float eps,
+                     float* y, int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
+                     void* stream) {
+    return run_norm(LIN_KIND_GEMV_I8_NORM, Wq, S, x, g, eps, y, M, N, K, epilogue, r, stream);
 }
 
 int lin_gemm_skinny_q4g64(const void* Wt, const void* St, const void* X, float* Y, int64_t M,
@@ -668,7 +680,8 @@ int lin_autotune_set(int kind, const void* const* W, const void* const* S, int c
     if (!valid_kind(kind)) return LIN_ERR_ARG;
     if (count < 1) return LIN_ERR_ARG;
     if (!W || ((kind == LIN_KIND_GEMV_Q4G64 || kind == LIN_KIND_SKINNY_Q4G64 ||
-                kind == LIN_KIND_GEMV_I8 || kind == LIN_KIND_GEMV_Q4G64_NORM) && !S))
+                kind == LIN_KIND_GEMV_I8 || kind == LIN_KIND_GEMV_Q4G64_NORM ||
+                kind == LIN_KIND_GEMV_I8_NORM) && !S))
         return LIN_ERR_NULL;
     for (int j = 0; j < count; ++j) {
         const int st = check(kind, W[j], S ? S[j] : nullptr, x, y, M, N, K);

@@ -122,7 +122,8 @@ def test_quantize_i8_validation():
 
 
 def test_epilogue_validation():
-    for f, extra in ((L._lib.lin_gemv_bf16_ep, ()), (L._lib.lin_gemv_q4g64_ep, (P,))):
+    for f, extra in ((L._lib.lin_gemv_bf16_ep, ()), (L._lib.lin_gemv_q4g64_ep, (P,)),
+                     (L._lib.lin_gemv_i8_ep, (P,))):
         assert f(P, *extra, P, P, 1, 8, 64, 3, None, None) == L.LIN_ERR_ARG
         assert f(P, *extra, P, P, 1, 8, 64, L.LIN_EPI_ADD, None, None) == L.LIN_ERR_NULL
         assert f(P, *extra, P, P, 2, 8, 64, L.LIN_EPI_NONE, None, None) == L.LIN_ERR_SHAPE
@@ -132,7 +133,8 @@ def test_epilogue_validation():
 
 
 def test_norm_validation():
-    for f, extra in ((L._lib.lin_gemv_bf16_norm, ()), (L._lib.lin_gemv_q4g64_norm, (P,))):
+    for f, extra in ((L._lib.lin_gemv_bf16_norm, ()), (L._lib.lin_gemv_q4g64_norm, (P,)),
+                     (L._lib.lin_gemv_i8_norm, (P,))):
         assert f(P, *extra, P, P, 1e-6, P, 1, 8, 64, 3, None, None) == L.LIN_ERR_ARG
         assert f(P, *extra, P, P, -1.0, P, 1, 8, 64, 0, None, None) == L.LIN_ERR_ARG
         assert f(P, *extra, P, P, float("nan"), P, 1, 8, 64, 0, None, None) == L.LIN_ERR_ARG
@@ -159,7 +161,7 @@ def test_stream_read_validation():
 def test_autotune_validation():
     cfg = L.LinConfig()
     t = L._lib.lin_autotune
-    assert t(7, P, P, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
+    assert t(8, P, P, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
     assert t(0, P, None, P, P, 9, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_SHAPE
     assert t(1, P, None, P, P, 1, 8, 64, None, ctypes.byref(cfg)) == L.LIN_ERR_NULL
     assert t(0, None, None, None, None, 0, 8, 8, None, ctypes.byref(cfg)) == L.LIN_OK
@@ -170,7 +172,7 @@ def test_autotune_set_validation():
     t = L._lib.lin_autotune_set
     two = (ctypes.c_void_p * 2)(P, P)
     null2 = (ctypes.c_void_p * 2)(None, None)
-    assert t(7, two, None, 2, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
+    assert t(8, two, None, 2, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
     assert t(0, two, None, 0, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_ARG
     assert t(0, None, None, 2, P, P, 1, 8, 8, None, ctypes.byref(cfg)) == L.LIN_ERR_NULL
     assert t(1, two, None, 2, P, P, 1, 8, 64, None, ctypes.byref(cfg)) == L.LIN_ERR_NULL
@@ -205,7 +207,7 @@ def test_candidate_enumeration():
     with pytest.raises(L.LinError):
         L.lin_candidate(0, 1, 8, 8, 10 ** 6)
     assert L._lib.lin_num_candidates(0, 1, 8, 12) == L.LIN_ERR_SHAPE
-    assert L._lib.lin_num_candidates(7, 1, 8, 8) == L.LIN_ERR_ARG
+    assert L._lib.lin_num_candidates(8, 1, 8, 8) == L.LIN_ERR_ARG
     assert L._lib.lin_num_candidates(-1, 1, 8, 8) == L.LIN_ERR_ARG
 
 
@@ -214,7 +216,8 @@ def test_norm_kind_candidates():
     M > 1 and K == 0, and drop configurations whose x + gain copies do not fit
     in LDS."""
     for kind, base in ((L.LIN_KIND_GEMV_BF16_NORM, L.LIN_KIND_GEMV_BF16),
-                       (L.LIN_KIND_GEMV_Q4G64_NORM, L.LIN_KIND_GEMV_Q4G64)):
+                       (L.LIN_KIND_GEMV_Q4G64_NORM, L.LIN_KIND_GEMV_Q4G64),
+                       (L.LIN_KIND_GEMV_I8_NORM, L.LIN_KIND_GEMV_I8)):
         for N, K in ((2560, 2048), (37888, 3584), (152064, 3584)):
             cands = L.lin_candidates(kind, 1, N, K)
             assert cands and all(c["stage_x"] == 1 and c["tile_m"] == 1 for c in cands)

@@ -1,4 +1,4 @@
-"""GPU parity of the fused epilogues (lin_gemv_bf16_ep, lin_gemv_q4g64_ep)
+"""GPU parity of the fused epilogues (lin_gemv_bf16_ep, lin_gemv_q4g64_ep, lin_gemv_i8_ep)
 against the oracle's product followed by the oracle's epilogue, for every
 candidate configuration of the plain product of the same weight matrix.
 
@@ -25,6 +25,11 @@ def _weights(fmt, NW, K, seed):
     if fmt == "bf16":
         Y, B = oracle.gemm_dense(u16(W), u16(x))
         return (W.to(DEV),), x.to(DEV), Y[0], B[0], L.LIN_KIND_GEMV_BF16, L.lin_gemv_bf16_ep
+    if fmt == "i8":
+        Wq, S = oracle.quantize_i8(u16(W))
+        Y, B = oracle.gemm_i8(Wq, S, u16(x))
+        return ((torch.from_numpy(Wq).to(DEV), torch.from_numpy(S).to(DEV)), x.to(DEV),
+                Y[0], B[0], L.LIN_KIND_GEMV_I8, L.lin_gemv_i8_ep)
     Wq, S = oracle.quantize_q4g64(u16(W))
     Y, B = oracle.gemm_q4g64(Wq, S, u16(x))
     return ((torch.from_numpy(Wq).to(DEV), synth.from_bits(S, torch.float16, DEV)), x.to(DEV),
@@ -36,7 +41,7 @@ def _check(y, expect, bound, what):
     assert np.all(d <= bound), "%s: worst |err|/bound = %.3g" % (what, np.max(d / np.maximum(bound, 1e-300)))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "q4"])
+@pytest.mark.parametrize("fmt", ["bf16", "q4", "i8"])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_residual_add_every_candidate(fmt, N, K):
     print("case epilogue add %s N=%d K=%d" % (fmt, N, K), flush=True)
@@ -60,7 +65,7 @@ def test_residual_add_every_candidate(fmt, N, K):
             L.lin_set_config(kind, 1, N, K, None)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "q4"])
+@pytest.mark.parametrize("fmt", ["bf16", "q4", "i8"])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_swiglu_every_candidate(fmt, N, K):
     print("case epilogue swiglu %s N=%d K=%d" % (fmt, N, K), flush=True)

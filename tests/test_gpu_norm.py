@@ -1,4 +1,5 @@
-"""GPU parity of the RMSNorm prologue (lin_gemv_bf16_norm, lin_gemv_q4g64_norm)
+"""GPU parity of the RMSNorm prologue (lin_gemv_bf16_norm, lin_gemv_q4g64_norm,
+lin_gemv_i8_norm)
 against the oracle's RMSNorm followed by the oracle's product (and epilogue),
 through the C ABI, for every candidate configuration of the prologue kinds.
 
@@ -51,6 +52,12 @@ def _case(fmt, NW, K, seed):
         Y, B = oracle.gemm_dense(u16(W), h)
         _, Bw = oracle.gemm_dense(u16(W), hw)
         Wt, kind, fn = (W.to(DEV),), L.LIN_KIND_GEMV_BF16_NORM, L.lin_gemv_bf16_norm
+    elif fmt == "i8":
+        Wq, S = oracle.quantize_i8(u16(W))
+        Y, B = oracle.gemm_i8(Wq, S, h)
+        _, Bw = oracle.gemm_i8(Wq, S, hw)
+        Wt = (torch.from_numpy(Wq).to(DEV), torch.from_numpy(S).to(DEV))
+        kind, fn = L.LIN_KIND_GEMV_I8_NORM, L.lin_gemv_i8_norm
     else:
         Wq, S = oracle.quantize_q4g64(u16(W))
         Y, B = oracle.gemm_q4g64(Wq, S, h)
@@ -71,7 +78,7 @@ def _check(y, expect, bound, what):
     assert np.all(d <= bound), "%s: worst |err|/bound = %.3g" % (what, np.max(d / np.maximum(bound, 1e-300)))
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "q4"])
+@pytest.mark.parametrize("fmt", ["bf16", "q4", "i8"])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_norm_every_configuration(fmt, N, K):
     print("case norm %s N=%d K=%d" % (fmt, N, K), flush=True)
@@ -92,7 +99,7 @@ def test_norm_every_configuration(fmt, N, K):
     assert torch.equal(x, x0)                                # x is not written
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "q4"])
+@pytest.mark.parametrize("fmt", ["bf16", "q4", "i8"])
 @pytest.mark.parametrize("N,K", SHAPES[1:3])
 def test_norm_with_epilogues(fmt, N, K):
     print("case norm+epilogues %s N=%d K=%d" % (fmt, N, K), flush=True)
@@ -128,7 +135,8 @@ def test_norm_with_epilogues(fmt, N, K):
 
 
 @pytest.mark.parametrize("fmt,N,K", [("bf16", 3, 8), ("bf16", 17, 520), ("bf16", 9, 32768),
-                                     ("q4", 7, 64), ("q4", 17, 576), ("q4", 9, 16384)])
+                                     ("q4", 7, 64), ("q4", 17, 576), ("q4", 9, 16384),
+                                     ("i8", 5, 16), ("i8", 17, 528), ("i8", 9, 32768)])
 def test_norm_edge_shapes(fmt, N, K):
     """The smallest K of each format, K not a multiple of the 512 (bf16) or
     2048 (int4) weights a wavefront step covers, and K near the largest whose

@@ -165,10 +165,11 @@ def test_maximum_k():
 @pytest.mark.parametrize("model", [synth.TINYLLAMA, synth.QWEN7B], ids=lambda m: m["name"])
 def test_norm_prologue_sampled(model):
     """RMSNorm folded into the normalised projections (q|k|v, gate|up with the
-    gated epilogue, head) at full size, bf16 and int4-g64, in the tuned
+    gated epilogue, head) at full size, bf16, int4-g64 and INT8, in the tuned
     configurations; bound as in test_gpu_norm."""
     from test_gpu_norm import _gain, _near_boundary
     _tuned(model["name"])
+    _tuned(model["name"] + "-i8")
     eps = 1e-6
     shapes = _shapes(model)
     named = {"q|k|v": shapes[0], "gate|up": shapes[2], "head": shapes[-1]}
@@ -186,13 +187,21 @@ def test_norm_prologue_sampled(model):
         rows = np.concatenate([out, out + N]) if swiglu else out
         Wr = u16(W[torch.from_numpy(rows).to(DEV)])
         Wq, S = L.lin_quantize_q4g64(W)
+        Wi, Si = L.lin_quantize_i8(W)
         idx = torch.from_numpy(rows).to(DEV)
         Wq_o, S_o = oracle.quantize_q4g64(Wr)
-        for fmt in ("bf16", "q4"):
+        Wi_o, Si_o = oracle.quantize_i8(Wr)
+        assert np.array_equal(Wi[idx].cpu().numpy(), Wi_o)
+        assert np.array_equal(Si[idx].cpu().numpy().view(np.uint32), Si_o.view(np.uint32))
+        for fmt in ("bf16", "q4", "i8"):
             if fmt == "bf16":
                 Y, B = oracle.gemm_dense(Wr, h)
                 _, Bw = oracle.gemm_dense(Wr, hw)
                 y = L.lin_gemv_bf16_norm(W, x, gd, eps, L.LIN_EPI_SWIGLU if swiglu else L.LIN_EPI_NONE)
+            elif fmt == "i8":
+                Y, B = oracle.gemm_i8(Wi_o, Si_o, h)
+                _, Bw = oracle.gemm_i8(Wi_o, Si_o, hw)
+                y = L.lin_gemv_i8_norm(Wi, Si, x, gd, eps, L.LIN_EPI_SWIGLU if swiglu else L.LIN_EPI_NONE)
             else:
                 Y, B = oracle.gemm_q4g64(Wq_o, S_o, h)
                 _, Bw = oracle.gemm_q4g64(Wq_o, S_o, hw)
@@ -210,4 +219,4 @@ def test_norm_prologue_sampled(model):
                 expect = Y[0]
             d = np.abs(got - expect)
             assert np.all(d <= bound), "%s %s: worst %.3g" % (fmt, name, np.max(d / bound))
-        del W, Wq, S
+        del W, Wq, S, Wi, Si

@@ -135,13 +135,14 @@ int lin_gemv_q4g64(const void* Wq, const void* S, const void* x, float* y,
  * product silu(w1 x) * w3 x formed by the kernel that computes both products). */
 typedef enum lin_epilogue {
     LIN_EPI_NONE = 0,    /* y = W x */
-    LIN_EPI_ADD = 1,     /* y = W x + r; r fp32 [1][N], may be y itself (accumulate in place) */
+    LIN_EPI_ADD = 1,     /* y = W x + r; r fp32 [M][N], may be y itself (accumulate in place) */
     LIN_EPI_SWIGLU = 2   /* W has 2N rows, gate rows 0..N-1 then up rows N..2N-1 (as
                             concatenated at load); y[n] = silu(g_n) * u_n with g = W[0:N] x,
                             u = W[N:2N] x and silu(g) = g / (1 + exp(-g)); r unused */
 } lin_epilogue;
 
-/* lin_gemv_bf16 / lin_gemv_q4g64 for M == 1 with a fused epilogue.  N counts
+/* lin_gemv_bf16 / lin_gemv_q4g64 (1 <= M <= LIN_GEMV_MAX_M) with a fused
+ * epilogue, applied to every token row (r and y are [M][N]).  N counts
  * the outputs (the weight matrix has 2N rows for LIN_EPI_SWIGLU).  The
  * configuration is the one tuned or pinned for the plain product of the same
  * weight matrix, i.e. (kind, 1, 2N or N, K); with SWIGLU a wavefront keeps the
@@ -149,8 +150,8 @@ typedef enum lin_epilogue {
  * rows; one of each when rows is 1).  Error bound per output: for ADD,
  * 1e-3 * (sum_k |W x| + |r|); for SWIGLU, the GEMV bound propagated through
  * silu(g) u (1e-3 * (1.1 |u| sum_k |W_g x| + |silu(g)| sum_k |W_u x|)) plus a few
- * fp32 rounding steps of |y|.  M != 1 returns LIN_ERR_SHAPE; ADD with a NULL r
- * LIN_ERR_NULL; an unknown epilogue LIN_ERR_ARG. */
+ * fp32 rounding steps of |y|.  M beyond LIN_GEMV_MAX_M returns LIN_ERR_SHAPE;
+ * ADD with a NULL r LIN_ERR_NULL; an unknown epilogue LIN_ERR_ARG. */
 int lin_gemv_bf16_ep(const void* W, const void* x, float* y,
                      int64_t M, int64_t N, int64_t K, int epilogue, const float* r, void* stream);
 int lin_gemv_q4g64_ep(const void* Wq, const void* S, const void* x, float* y,
@@ -189,7 +190,7 @@ int lin_gemv_q4g64_norm(const void* Wq, const void* S, const void* x, const void
 int lin_gemv_i8(const void* Wi, const void* Si, const void* x, float* y,
                 int64_t M, int64_t N, int64_t K, void* stream);
 
-/* lin_gemv_i8 for M == 1 with a fused epilogue (as lin_gemv_bf16_ep; the gated
+/* lin_gemv_i8 with a fused epilogue (as lin_gemv_bf16_ep; the gated
  * product applies each row's scale before the gate: silu(Si[n] g_n) Si[N+n] u_n,
  * with Si holding the 2N scales of the gate|up rows), and with the RMSNorm
  * prologue as well (as lin_gemv_bf16_norm; kind LIN_KIND_GEMV_I8_NORM, K >= 16).

@@ -195,7 +195,7 @@ def lin_gemv_q4g64(Wq, S, x, y=None):
     return y
 
 
-def _epi_out(epilogue, NW, r, y, dev):
+def _epi_out(epilogue, NW, r, y, dev, M=1):
     if epilogue not in (LIN_EPI_NONE, LIN_EPI_ADD, LIN_EPI_SWIGLU):
         raise ValueError("unknown epilogue %r" % (epilogue,))
     N = NW // 2 if epilogue == LIN_EPI_SWIGLU else NW
@@ -203,22 +203,23 @@ def _epi_out(epilogue, NW, r, y, dev):
         raise ValueError("the gated product needs an even number of weight rows")
     if epilogue == LIN_EPI_ADD:
         _need(r, torch.float32, "r", 2)
-        if tuple(r.shape) != (1, N):
-            raise ValueError("r must have shape (1, %d)" % N)
-    return N, _out(y, 1, N, dev)
+        if tuple(r.shape) != (M, N):
+            raise ValueError("r must have shape (%d, %d)" % (M, N))
+    return N, _out(y, M, N, dev)
 
 
 def lin_gemv_bf16_ep(W, x, epilogue, r=None, y=None):
-    """Batch-1 bf16 product with a fused epilogue: LIN_EPI_ADD (y = W x + r, r may
-    be y) or LIN_EPI_SWIGLU (W has 2N rows: y = silu(W[:N] x) * W[N:] x)."""
+    """bf16 product of up to 8 tokens with a fused epilogue: LIN_EPI_ADD (y = W x + r,
+    r [M, N] may be y) or LIN_EPI_SWIGLU (W has 2N rows: y = silu(W[:N] x) * W[N:] x)."""
     x = _as2d(x)
     _need(W, torch.bfloat16, "W", 2)
     _need(x, torch.bfloat16, "x", 2)
     NW, K = W.shape
-    if x.shape != (1, K):
-        raise ValueError("x must be one token of K = %d" % K)
-    N, y = _epi_out(epilogue, NW, r, y, W.device)
-    _check(_lib.lin_gemv_bf16_ep(W.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, K, int(epilogue),
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must have K = %d columns" % K)
+    N, y = _epi_out(epilogue, NW, r, y, W.device, M)
+    _check(_lib.lin_gemv_bf16_ep(W.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K, int(epilogue),
                                  r.data_ptr() if r is not None else None, _stream(W)),
            "lin_gemv_bf16_ep")
     return y
@@ -232,10 +233,11 @@ def lin_gemv_q4g64_ep(Wq, S, x, epilogue, r=None, y=None):
     _need(x, torch.bfloat16, "x", 2)
     NW, K2 = Wq.shape
     K = 2 * K2
-    if x.shape != (1, K) or tuple(S.shape) != (NW, K // 64):
-        raise ValueError("shape mismatch: Wq [N, K/2], S [N, K/64], x [1, K]")
-    N, y = _epi_out(epilogue, NW, r, y, Wq.device)
-    _check(_lib.lin_gemv_q4g64_ep(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, K,
+    M = x.shape[0]
+    if x.shape[1] != K or tuple(S.shape) != (NW, K // 64):
+        raise ValueError("shape mismatch: Wq [N, K/2], S [N, K/64], x [M, K]")
+    N, y = _epi_out(epilogue, NW, r, y, Wq.device, M)
+    _check(_lib.lin_gemv_q4g64_ep(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K,
                                   int(epilogue), r.data_ptr() if r is not None else None,
                                   _stream(Wq)), "lin_gemv_q4g64_ep")
     return y
@@ -300,23 +302,24 @@ def lin_gemv_i8(Wq, S, x, y=None):
     return y
 
 
-def _i8_args(Wq, S, x):
+def _i8_args(Wq, S, x, one_token=True):
     x = _as2d(x)
     _need(Wq, torch.int8, "Wq", 2)
     _need(S, torch.float32, "S", 1)
     _need(x, torch.bfloat16, "x", 2)
     NW, K = Wq.shape
-    if x.shape != (1, K) or tuple(S.shape) != (NW,):
-        raise ValueError("shape mismatch: Wq [N, K], S [N], x [1, K]")
+    if x.shape[1] != K or (one_token and x.shape[0] != 1) or tuple(S.shape) != (NW,):
+        raise ValueError("shape mismatch: Wq [N, K], S [N], x [%s, K]" % ("1" if one_token else "M"))
     return x, NW, K
 
 
 def lin_gemv_i8_ep(Wq, S, x, epilogue, r=None, y=None):
     """Batch-1 INT8 product with a fused epilogue (see lin_gemv_bf16_ep); with the
     gated epilogue, each row's scale is applied before the gate."""
-    x, NW, K = _i8_args(Wq, S, x)
-    N, y = _epi_out(epilogue, NW, r, y, Wq.device)
-    _check(_lib.lin_gemv_i8_ep(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), 1, N, K,
+    x, NW, K = _i8_args(Wq, S, x, one_token=False)
+    M = x.shape[0]
+    N, y = _epi_out(epilogue, NW, r, y, Wq.device, M)
+    _check(_lib.lin_gemv_i8_ep(Wq.data_ptr(), S.data_ptr(), x.data_ptr(), y.data_ptr(), M, N, K,
                                int(epilogue), r.data_ptr() if r is not None else None, _stream(Wq)),
            "lin_gemv_i8_ep")
     return y

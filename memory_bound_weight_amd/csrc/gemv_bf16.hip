@@ -47,10 +47,10 @@ static void add(std::vector<Variant>& out) {
     v.geometry = &geom_bf16<MT, R, U, SPLIT, STAGE>;
     if (MT <= LIN_GEMV_MAX_M) {
         v.kind = LIN_KIND_GEMV_BF16;
-        if constexpr (MT == 1) {
+        if constexpr (MT <= LIN_GEMV_MAX_M) {
             v.epi[kEpiAdd] = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
             v.epi[kEpiSwiglu] = (const void*)&gemv_bf16_valu<MT, RS, U, SPLIT, STAGE, kEpiSwiglu>;
-            if constexpr (STAGE) {
+            if constexpr (STAGE && MT == 1) {
                 Variant n = v;
                 n.kind = LIN_KIND_GEMV_BF16_NORM;
                 n.func = (const void*)&gemv_bf16_valu<MT, R, U, SPLIT, STAGE, kEpiNone, true>;

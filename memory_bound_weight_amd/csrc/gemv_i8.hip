@@ -45,10 +45,10 @@ static void add(std::vector<Variant>& out) {
     v.min_m = MT / 2 + 1;
     v.func = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE>;
     v.geometry = &geom_i8<MT, R, U, SPLIT, STAGE>;
-    if constexpr (MT == 1) {
+    if constexpr (MT <= LIN_GEMV_MAX_M) {
         v.epi[kEpiAdd] = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE, kEpiAdd>;
         v.epi[kEpiSwiglu] = (const void*)&gemv_i8_valu<MT, RS, U, SPLIT, STAGE, kEpiSwiglu>;
-        if constexpr (STAGE) {
+        if constexpr (STAGE && MT == 1) {
             Variant n = v;
             n.kind = LIN_KIND_GEMV_I8_NORM;
             n.func = (const void*)&gemv_i8_valu<MT, R, U, SPLIT, STAGE, kEpiNone, true>;

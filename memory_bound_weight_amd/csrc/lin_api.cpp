@@ -363,17 +363,17 @@ int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y, int64_t M, int6
     return run(LIN_KIND_SKINNY_BF16, W, nullptr, X, Y, M, N, K, stream);
 }
 
-// Batch-1 product with a fused epilogue, in the configuration tuned or pinned
-// for the plain product of the same weight matrix (2N rows for the gated one).
+// Product of up to LIN_GEMV_MAX_M tokens with a fused epilogue, in the
+// configuration tuned or pinned for the plain product of the same weight
+// matrix (2N rows for the gated one).
 static int run_epilogue(int kind, const void* W, const void* S, const void* x, float* y,
                         int64_t M, int64_t N, int64_t K, int epilogue, const float* r,
                         void* stream) {
     if (epilogue < LIN_EPI_NONE || epilogue > LIN_EPI_SWIGLU) return LIN_ERR_ARG;
     if (N < 0 || N > 0x3FFFFFFF) return LIN_ERR_SHAPE;
     const int64_t NW = epilogue == LIN_EPI_SWIGLU ? 2 * N : N;   // weight rows
-    int st = check(kind, W, S, x, y, M, NW, K);
+    int st = check(kind, W, S, x, y, M, NW, K);   // 1 <= M <= LIN_GEMV_MAX_M
     if (st != LIN_OK) return st > 0 ? LIN_OK : st;
-    if (M != 1) return LIN_ERR_SHAPE;
     if (epilogue == LIN_EPI_ADD) {
         if (!r) return LIN_ERR_NULL;
         if (!aligned(r, 4)) return LIN_ERR_ALIGN;

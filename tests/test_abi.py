@@ -126,7 +126,7 @@ def test_epilogue_validation():
                      (L._lib.lin_gemv_i8_ep, (P,))):
         assert f(P, *extra, P, P, 1, 8, 64, 3, None, None) == L.LIN_ERR_ARG
         assert f(P, *extra, P, P, 1, 8, 64, L.LIN_EPI_ADD, None, None) == L.LIN_ERR_NULL
-        assert f(P, *extra, P, P, 2, 8, 64, L.LIN_EPI_NONE, None, None) == L.LIN_ERR_SHAPE
+        assert f(P, *extra, P, P, 9, 8, 64, L.LIN_EPI_NONE, None, None) == L.LIN_ERR_SHAPE
         assert f(P, *extra, P, P, 1, 1 << 30, 64, L.LIN_EPI_SWIGLU, None, None) == L.LIN_ERR_SHAPE
         assert f(P, *extra, P, P, 1, 8, 64, L.LIN_EPI_ADD, P + 2, None) == L.LIN_ERR_ALIGN
         assert f(None, *((None,) if extra else ()), None, None, 0, 8, 64, L.LIN_EPI_SWIGLU, None, None) == L.LIN_OK

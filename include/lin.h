@@ -20,11 +20,24 @@
  *   Si  fp32    [N]        one scale per output channel (row); w = q * s
  *   x/X bf16    [M][K]     activations, one row per token
  *   y/Y fp32    [M][N]     outputs, overwritten (no accumulation into y)
- * Accumulation is fp32.  The result of every configuration is within
- * 1e-3 * sum_k |W[n][k] * x[m][k]| of the exact product, per output.  (The
- * int4 products multiply the codes as 136 + q and remove 136 * sum x per 32 or
- * 64 weights in fp32, which adds up to about 2.7e-4 * s * sum |x| per 32
- * weights of scale s: inside the bound unless most codes of a group are zero.)
+ * Accumulation is fp32.  bf16 and INT8 weights: every product w x is exact in
+ * fp32 and only the sums round, so every configuration is within
+ * 1e-3 * sum_k |W[n][k] * x[m][k]| of the exact product, per output (the sums
+ * contribute at most about (K / 2048 + 8) * 2^-24 of that term).
+ * int4-g64 weights: the kernels multiply the exact bf16 codes 24 + q (no
+ * conversion instruction per weight) and remove 24 * sum x per 16, 32 or 64
+ * weights in fp32.  That removal adds rounding that is not proportional to
+ * |q x|, so for int4 the guaranteed bound per output is
+ *     |y - exact| <= 1e-4 * sum_k |W[n][k] x[m][k]|
+ *                  + 4e-4 * sum_g s[n][g] * sum_{k in g} |x[m][k]|,
+ * g over the row's scale groups.  It implies the 1e-3 * sum_k |W x| bound
+ * whenever sum_k |q x| >= 0.45 * sum_k |x| over the row's groups (weighted by
+ * their scales), i.e. the codes average at least about 0.45 in magnitude where
+ * x is large: quantised Gaussian weights average about 2.  Rows dominated by
+ * one outlier per group (most codes 0) typically stay far inside the 1e-3
+ * bound as well, since the removal's roundings are random in sign; an input
+ * built so that x vanishes exactly where a row's nonzero codes are can exceed
+ * it, but never the bound above.
  *
  * Ownership and execution.  Every pointer is a device pointer owned by the
  * caller; the library never frees or retains them.  The compute entry points
@@ -37,6 +50,11 @@
  * never synchronise and are safe inside HIP graph capture.  Results are
  * deterministic: the same configuration on the same inputs gives the same bits.
  * Calls may be made from several host threads; the tuning table is guarded.
+ * One exception to running calls concurrently: product calls whose
+ * configuration splits K across workgroups (matrix-core configurations with
+ * `split` > 1, chosen only by tuning or pinning) share their device's split-K
+ * workspace, so two such calls must not overlap on different streams of one
+ * device.  Every other call is reentrant.
  *
  * Errors.  Every entry point returns LIN_OK or a negative lin_status.  Argument
  * errors are detected before anything is enqueued, so nothing has run.
@@ -288,7 +306,9 @@ int lin_get_config(int kind, int64_t M, int64_t N, int64_t K, lin_config* out);
  * LDS has that limit raised for its kernel here as well (otherwise on its
  * first launch).  Product calls that use split-K share the device's
  * workspace, so such calls on one device must not run concurrently on
- * different streams. */
+ * different streams.  The library never frees a workspace (a grown one keeps
+ * the old buffer allocated until the process ends), so a graph captured with a
+ * split-K configuration stays valid after later calls grow the workspace. */
 int lin_set_config(int kind, int64_t M, int64_t N, int64_t K, const lin_config* cfg);
 
 /* Load-time weight preparation: quantise bf16 W [N][K] (K % 64 == 0) to the

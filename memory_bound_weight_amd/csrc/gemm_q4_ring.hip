@@ -14,12 +14,12 @@
 //    scale group).  Inside a dword the codes of k0 + 2i and k0 + 2i + 1 sit at
 //    bits 4i and 16 + 4i.  Scales are rearranged so that one 64-byte unit
 //    holds the two groups of a 128-k block for 16 rows.
-//  - Unpacking.  As in the GEMV: ((w >> 4i) & 0x000F000F) ^ 0x43084308 turns a
-//    dword of codes into bf16 pairs 136 + q (exact); with the nibble order of
-//    the tiles the pairs come out in natural k order, so X is used as loaded.
+//  - Unpacking.  As in the GEMV (q4_unpack2): a dword of codes becomes bf16
+//    pairs 24 + q (exact); with the nibble order of the tiles the pairs come
+//    out in natural k order, so X is used as loaded.
 //  - The offset and the scales.  The products of one scale group start from
-//    C = -136 * sum(x) over the group, itself a matrix-core product of the X
-//    operands with a constant operand of -136 (exact products, fp32 sums), so
+//    C = -24 * sum(x) over the group, itself a matrix-core product of the X
+//    operands with a constant operand of -24 (exact products, fp32 sums), so
 //    D = sum(q x) for the group; then acc += s * D, one fma per output and
 //    group.  Every product is exact in fp32 and the scale is applied in fp32:
 //    nothing is rounded to bf16 on the way, unlike a dequantise-to-bf16 GEMM.
@@ -39,8 +39,8 @@ namespace {
 
 constexpr int kQB = 128;   // k per ring stage and per tiled unit
 
-// bf16 pairs (-136, -136): the constant operand of the offset products.
-constexpr uint32_t kNeg136 = 0xC308C308u;
+// bf16 pairs (-24, -24): the constant operand of the offset products.
+constexpr uint32_t kNegOff = kQ4NegOffsetPair;
 
 // Wave tile of a workgroup tile: NW wavefronts as WR x WC (as the bf16 ring).
 template <int BN, int TM, int NW>
@@ -58,27 +58,16 @@ struct Q4Shape {
     static_assert(FW * 64 <= 1024, "the scales of a stage fit one unit");
 };
 
-template <int SH>
-__device__ __forceinline__ uint64_t shr64(uint64_t v) {
-    uint64_t r;
-    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "I"(SH), "v"(v));
-    return r;
-}
-
 // Two dwords of codes (two consecutive 8-k slices) to two B operands of bf16
-// codes 136 + q; one v_bitop3 per pair, the shifts on both dwords at once.
+// codes 24 + q; one v_bitop3 per pair, the shifts on both dwords at once.
 __device__ __forceinline__ void unpack2(uint32_t w0, uint32_t w1, u32x4& b0, u32x4& b1) {
-    constexpr uint32_t MK = 0x000F000Fu, C = 0x43084308u;
-    const uint64_t w = (uint64_t)w0 | ((uint64_t)w1 << 32);
-    const uint64_t t1 = shr64<4>(w), t2 = shr64<8>(w), t3 = shr64<12>(w);
-    b0[0] = (w0 & MK) ^ C;
-    b0[1] = ((uint32_t)t1 & MK) ^ C;
-    b0[2] = ((uint32_t)t2 & MK) ^ C;
-    b0[3] = ((uint32_t)t3 & MK) ^ C;
-    b1[0] = (w1 & MK) ^ C;
-    b1[1] = ((uint32_t)(t1 >> 32) & MK) ^ C;
-    b1[2] = ((uint32_t)(t2 >> 32) & MK) ^ C;
-    b1[3] = ((uint32_t)(t3 >> 32) & MK) ^ C;
+    uint32_t o[8];
+    q4_unpack2((uint64_t)w0 | ((uint64_t)w1 << 32), o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        b0[i] = o[i];
+        b1[i] = o[4 + i];
+    }
 }
 
 __device__ __forceinline__ float half_lo(uint32_t v) {
@@ -206,7 +195,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
     for (int d = 0; d < D - 1; ++d)
         if (d < nkb) issue(kb0 + d, d);
 
-    const u32x4 neg = {kNeg136, kNeg136, kNeg136, kNeg136};
+    const u32x4 neg = {kNegOff, kNegOff, kNegOff, kNegOff};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < nkb; ++i) {
         wait_stages_q4<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)

@@ -9,14 +9,13 @@
 // row with a two-stage register pipeline, SPLIT wavefronts may share rows
 // along K, x comes through the caches or is staged in LDS once per workgroup.
 //
-// Conversion.  q + 128 is an unsigned byte (one XOR with 0x80 per byte, four
-// bytes per instruction), and v_cvt_f32_ubyte0..3 turn each byte into an fp32
-// directly, so a weight costs one conversion and one fp32 fma with x, whose
-// bf16 values become fp32 by a shift (shared by the R rows).  The products of
-// (q + 128) with x are exact in fp32; the offset is removed once per lane and
-// row at the end: acc - 128 * sum(x), with sum(x) over the lane's chunks shared
-// by all rows.  The wavefront then reduces as usual and one lane per output
-// multiplies by the row's scale.
+// Conversion.  Each code byte becomes an fp32 with one v_cvt_f32_i32 that
+// reads the byte in place, sign-extended (a sub-dword operand select), so a
+// weight costs one conversion and one fp32 fma with x, whose bf16 values
+// become fp32 by a shift (shared by the R rows).  Every product q x is exact
+// in fp32 and there is no offset to remove, so the rounding of the sums is
+// relative to sum_k |q x|.  The wavefront then reduces as usual and one lane
+// per output multiplies by the row's scale.
 //
 // Epilogues and prologue (batch 1) as in the bf16 kernel: EPI adds the
 // residual, or forms silu(s_g g) (s_u u) over the gate|up rows (each row's
@@ -72,16 +71,13 @@ __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
-    float xsum[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) xsum[m] = 0.f;
 
     struct Stage {
         u32x4 w[U][R];
         u32x4 x[U][MT][STAGE ? 1 : 2];   // the chunk's 16 x values (unstaged x only)
     };
     // As in the bf16 kernel, a partial last step re-loads chunk cend - 1 in
-    // the lanes past cend and drops its products and its x sum.
+    // the lanes past cend and drops its products.
     auto load = [&](Stage& s, int cb) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -114,24 +110,25 @@ __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block
                     x1 = s.x[u][m][1];
                 }
                 float xf[16];
-                float t = 0.f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
                     const uint32_t d = i < 4 ? x0[i] : x1[i - 4];
-                    t = dot2(d, 0x3F803F80u, t);   // bf16 (1, 1): sum of the pair
                     xf[2 * i] = bitsf(d << 16);
                     xf[2 * i + 1] = bitsf(d & 0xFFFF0000u);
                 }
-                xsum[m] += (MASK && c >= cend) ? 0.f : t;
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
                     float p = MASK ? 0.f : acc[r * MT + m];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const uint32_t wu = s.w[u][r][j] ^ 0x80808080u;   // q + 128 per byte
+                        // In the partial last step the lanes past cend convert
+                        // zero codes: their results differ from the full steps',
+                        // so the compiler cannot hoist a stage's conversions
+                        // above the step branch (which would keep them all live).
+                        const uint32_t wj = (MASK && c >= cend) ? 0u : s.w[u][r][j];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            p = fmaf((float)((wu >> (8 * e)) & 0xFFu), xf[4 * j + e], p);
+                        for (int e = 0; e < 4; ++e)   // the signed byte e of wj, exactly
+                            p = fmaf((float)(int8_t)(wj >> (8 * e)), xf[4 * j + e], p);
                     }
                     if constexpr (MASK)
                         acc[r * MT + m] += c < cend ? p : 0.f;
@@ -179,12 +176,6 @@ __device__ __forceinline__ void gemv_i8_valu_block(const KArgs& a, int64_t block
             if (++it >= nsteps) break;
         }
     }
-    // remove the +128 offset: sum_k (q + 128) x - 128 sum_k x
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[r * MT + m] = fmaf(-128.f, xsum[m], acc[r * MT + m]);
-
     wave_reduce<V>(acc);
     // y = scale * total (no scale read when K == 0), then the epilogue
     if constexpr (EPI == kEpiSwiglu) {

@@ -8,16 +8,15 @@
 // R rows, each lane reads consecutive 16-byte chunks = 32 codes = half a scale
 // group, so lanes 2i and 2i+1 share one scale.
 //
-// Unpacking without conversions.  Flipping bit 3 of a nibble turns the two's
-// complement code q into n' = q + 8 in [0, 15], and (n' | 0x4300) read as bf16
-// is exactly 128 + n' = q + 136, so one 3-input bitwise operation per pair of
-// nibbles yields two bf16 "codes" that go straight into v_dot2_f32_bf16.  Masking 0x000F000F after shifting a dword by
-// 0, 4, 8, 12 pairs nibble i with nibble i+4, i.e. k = 8d+i with k = 8d+i+4,
-// so x is re-paired the same way (one v_perm per pair).  The offset is removed
-// per chunk: sum_k q x = dot(codes, x) - 136 * sum_k x, where sum_k x over the
-// chunk is shared by all rows; the dot chain starts from -136 * sum x.  Then
-// acc += s * chunk sum.  Per 32 weights and row: 22 unpack + 16 dot2 + 1 for
-// the scale, about 1.2 vector operations per weight.
+// Unpacking without conversions (q4_unpack2): one 3-input bitwise operation
+// per pair of nibbles yields two exact bf16 "codes" 24 + q that go straight
+// into v_dot2_f32_bf16.  Nibble i of a dword is paired with nibble i+4, i.e.
+// k = 8d+i with k = 8d+i+4, so x is re-paired the same way (one v_perm per
+// pair).  The offset is removed per chunk: sum_k q x = dot(codes, x) - 24 *
+// sum_k x, where sum_k x over the chunk is shared by all rows; the dot chain
+// starts from -24 * sum x.  Then acc += s * chunk sum.  Per 32 weights and
+// row: 24 unpack + 16 dot2 + 1 for the scale, about 1.3 vector operations per
+// weight.
 //
 // x handling: either re-paired from cached global loads per chunk (cost shared
 // by the R rows), or, with STAGE, staged once per workgroup.  Per chunk a lane
@@ -45,7 +44,7 @@ namespace lin {
 // 16 re-paired x dwords of one 32-k chunk: pair (x[8d+i], x[8d+i+4]) at 4d+i.
 struct XChunk {
     u32x4 v[4];
-    float negsum;   // -136 * sum of the 32 x values
+    float negsum;   // -24 * sum of the 32 x values
 };
 
 __device__ __forceinline__ void pair_x(const u32x4 (&xd)[4], XChunk& out) {
@@ -64,7 +63,7 @@ __device__ __forceinline__ void pair_x(const u32x4 (&xd)[4], XChunk& out) {
         s = dot2(a2, 0x3F803F80u, s);
         s = dot2(a3, 0x3F803F80u, s);
     }
-    out.negsum = -136.f * s;
+    out.negsum = -kQ4Offset * s;
 }
 
 // One 16-byte unit of x (natural dwords d0..d3 = x[8d+0..7] of a chunk's unit
@@ -82,35 +81,18 @@ __device__ __forceinline__ u32x4 pair_unit(const u32x4& a, float& s) {
     return o;
 }
 
-// Sum over one chunk of 32 codes times re-paired x, minus the code offset.
-// ((w >> 4i) & 0x000F000F) ^ 0x43084308 equals ((w ^ 0x88888888) >> 4i &
-// 0x000F000F) | 0x43004300: the sign flip and the bf16 exponent bits go in with
-// one 3-input bitwise operation (v_bitop3_b32).  The shifts are done on two
-// dwords at once with one v_lshrrev_b64 (bits that cross from the high dword
-// land in bits 20..31 of the low one, outside the mask), which halves them:
-// per 32 codes 6 shifts + 16 bitwise operations + 16 dot products.
-template <int S>
-__device__ __forceinline__ uint64_t shr64(uint64_t v) {
-    uint64_t r;
-    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "I"(S), "v"(v));
-    return r;
-}
-
+// Sum over one chunk of 32 codes times re-paired x, minus the code offset:
+// 16 bitwise operations, 8 64-bit shifts and 16 dot products per 32 codes.
 __device__ __forceinline__ float chunk_dot(const u32x4& wq, const XChunk& xc) {
-    constexpr uint32_t M = 0x000F000Fu, C = 0x43084308u;
     float acc = xc.negsum;
 #pragma unroll
     for (int d = 0; d < 4; d += 2) {
-        const uint64_t w = (uint64_t)wq[d] | ((uint64_t)wq[d + 1] << 32);
-        const uint64_t t1 = shr64<4>(w), t2 = shr64<8>(w), t3 = shr64<12>(w);
-        acc = dot2(((uint32_t)w & M) ^ C, xc.v[d][0], acc);
-        acc = dot2(((uint32_t)t1 & M) ^ C, xc.v[d][1], acc);
-        acc = dot2(((uint32_t)t2 & M) ^ C, xc.v[d][2], acc);
-        acc = dot2(((uint32_t)t3 & M) ^ C, xc.v[d][3], acc);
-        acc = dot2(((uint32_t)(w >> 32) & M) ^ C, xc.v[d + 1][0], acc);
-        acc = dot2(((uint32_t)(t1 >> 32) & M) ^ C, xc.v[d + 1][1], acc);
-        acc = dot2(((uint32_t)(t2 >> 32) & M) ^ C, xc.v[d + 1][2], acc);
-        acc = dot2(((uint32_t)(t3 >> 32) & M) ^ C, xc.v[d + 1][3], acc);
+        uint32_t o[8];
+        q4_unpack2((uint64_t)wq[d] | ((uint64_t)wq[d + 1] << 32), o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = dot2(o[i], xc.v[d][i], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = dot2(o[4 + i], xc.v[d + 1][i], acc);
     }
     return acc;
 }
@@ -226,7 +208,12 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
                 get_x(s, u, m, cc, xc);
 #pragma unroll
                 for (int r = 0; r < R; ++r) {
-                    const float v = fmaf(half_to_float(s.sc[u][r]), chunk_dot(s.w[u][r], xc),
+                    // lanes past cend unpack zero codes in the partial step (the
+                    // result is dropped): the two step forms then differ, so the
+                    // compiler does not hoist a whole stage's unpacking above
+                    // the step branch and keep it live
+                    const u32x4 wq = (MASK && c >= cend) ? u32x4{0u, 0u, 0u, 0u} : s.w[u][r];
+                    const float v = fmaf(half_to_float(s.sc[u][r]), chunk_dot(wq, xc),
                                          acc[r * MT + m]);
                     if constexpr (MASK)
                         acc[r * MT + m] = c < cend ? v : acc[r * MT + m];
@@ -284,7 +271,7 @@ __device__ __forceinline__ void gemv_q4_valu_block(const KArgs& a, int64_t block
             sum += dpp<0xB1>(sum);   // quad_perm [1,0,3,2]
             sum += dpp<0x4E>(sum);   // quad_perm [2,3,0,1]
             xs[(m * 4 + d) * nch + c] = p;
-            if (d == 0) xsum[m * nch + c] = -136.f * sum;
+            if (d == 0) xsum[m * nch + c] = -kQ4Offset * sum;
         }
         wait_cnt<63, 0>();   // LDS writes done, weight loads still in flight
         barrier_only();

@@ -10,10 +10,10 @@
 // for the four k-slices k0 = 128 j + 32 t + 8 (l / 16), t < 4, already in
 // natural bf16 pair order (see the tiled layout); x of those slices comes
 // through the caches (four 16-byte loads per token, shared by the R tiles).
-// Unpacking is the GEMV's: ((w >> 4i) & 0x000F000F) ^ 0x43084308 = bf16 codes
-// 136 + q.  The offset is removed per scale group: the lane's sum of x over
-// the group's two slices (shared by all rows of the wavefront) times -136
-// seeds the dot chain of each row.  The four lanes of a row (l, l + 16, l + 32,
+// Unpacking is the GEMV's (q4_unpack2): exact bf16 codes 24 + q.  The offset
+// is removed per scale group: the lane's sum of x over the group's two slices
+// (shared by all rows of the wavefront) times -24 seeds the dot chain of each
+// row.  The four lanes of a row (l, l + 16, l + 32,
 // l + 48) are summed with permlane32/16 swaps; SPLIT wavefronts of a
 // workgroup take parts of K and combine through LDS.
 #pragma once
@@ -23,13 +23,6 @@
 #include "kern_common.h"
 
 namespace lin {
-
-template <int SH>
-__device__ __forceinline__ uint64_t q4t_shr64(uint64_t v) {
-    uint64_t r;
-    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "I"(SH), "v"(v));
-    return r;
-}
 
 template <int MT, int R, int U, int SPLIT>
 __device__ __forceinline__ void gemv_q4t_valu_block(const KArgs& a, int64_t block) {
@@ -102,8 +95,7 @@ __device__ __forceinline__ void gemv_q4t_valu_block(const KArgs& a, int64_t bloc
         for (int u = 0; u < U; ++u) load_unit(st.u[u], min(j + u, jend - 1));
     };
     auto compute_unit = [&](const Unit& st) {
-        constexpr uint32_t MK = 0x000F000Fu, C = 0x43084308u;
-        // -136 x the lane's sum of x over each scale group (t = 0, 1 and t = 2, 3)
+        // -24 x the lane's sum of x over each scale group (t = 0, 1 and t = 2, 3)
         float neg[MT][2];
 #pragma unroll
         for (int m = 0; m < MT; ++m)
@@ -114,24 +106,20 @@ __device__ __forceinline__ void gemv_q4t_valu_block(const KArgs& a, int64_t bloc
                 for (int t = 2 * h; t < 2 * h + 2; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) s = dot2(st.x[m][t][i], 0x3F803F80u, s);
-                neg[m][h] = -136.f * s;
+                neg[m][h] = -kQ4Offset * s;
             }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             uint32_t c[4][4];   // bf16 code pairs of slice t: natural k pairs i
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                const uint32_t w0 = st.w[r][2 * p], w1 = st.w[r][2 * p + 1];
-                const uint64_t w = (uint64_t)w0 | ((uint64_t)w1 << 32);
-                const uint64_t t1 = q4t_shr64<4>(w), t2 = q4t_shr64<8>(w), t3 = q4t_shr64<12>(w);
-                c[2 * p][0] = (w0 & MK) ^ C;
-                c[2 * p][1] = ((uint32_t)t1 & MK) ^ C;
-                c[2 * p][2] = ((uint32_t)t2 & MK) ^ C;
-                c[2 * p][3] = ((uint32_t)t3 & MK) ^ C;
-                c[2 * p + 1][0] = (w1 & MK) ^ C;
-                c[2 * p + 1][1] = ((uint32_t)(t1 >> 32) & MK) ^ C;
-                c[2 * p + 1][2] = ((uint32_t)(t2 >> 32) & MK) ^ C;
-                c[2 * p + 1][3] = ((uint32_t)(t3 >> 32) & MK) ^ C;
+                uint32_t o[8];
+                q4_unpack2((uint64_t)st.w[r][2 * p] | ((uint64_t)st.w[r][2 * p + 1] << 32), o);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    c[2 * p][i] = o[i];
+                    c[2 * p + 1][i] = o[4 + i];
+                }
             }
             const float s0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(st.s[r] & 0xFFFFu));
             const float s1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(st.s[r] >> 16));

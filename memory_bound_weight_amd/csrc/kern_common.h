@@ -127,6 +127,52 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
                                            __builtin_bit_cast(bf16x2, b), acc, false);
 }
 
+// int4 codes as exact bf16 values.  Flipping bit 3 of a 4-bit two's
+// complement code q gives n = q + 8 in [0, 15]; placed in the top four mantissa
+// bits of a bf16 whose exponent is 4 (value 16), the pattern reads 16 + n =
+// 24 + q exactly.  (w >> s) & 0x00780078 ^ 0x41C041C0 does this for the
+// nibbles at bits 3 + s .. 6 + s and 19 + s .. 22 + s of w with one 3-input
+// bitwise operation (v_bitop3_b32): two codes per dword, each exact in the
+// products with bf16 x.  The products then carry 24 sum x, removed in fp32;
+// the offset of 24 code steps (the smallest that keeps every code's exponent
+// equal) bounds the rounding that removal adds.
+constexpr uint32_t kQ4Mask = 0x00780078u, kQ4Code = 0x41C041C0u;
+constexpr float kQ4Offset = 24.f;
+constexpr uint32_t kQ4NegOffsetPair = 0xC1C0C1C0u;   // bf16 pair (-24, -24)
+
+template <int S>
+__device__ __forceinline__ uint64_t q4_shr64(uint64_t v) {
+    uint64_t r;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(r) : "I"(S), "v"(v));
+    return r;
+}
+template <int S>
+__device__ __forceinline__ uint64_t q4_shl64(uint64_t v) {
+    uint64_t r;
+    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "I"(S), "v"(v));
+    return r;
+}
+
+// Codes of two dwords lo = (uint32_t)w, hi = w >> 32, whose nibble i sits at
+// bits 4i .. 4i + 3.  o[i] (i < 4) pairs nibble i of lo with nibble i + 4 of lo
+// (low and high bf16 halves), o[4 + i] the same for hi.  Every dword needs
+// nibble i moved to bit 3 (a shift right by 4i - 3, left by 3 for i = 0); the
+// shifts act on both dwords at once with 64-bit shifts, and the bits that cross
+// from one dword into the other land outside the mask.  12 operations for 16
+// codes.
+__device__ __forceinline__ void q4_unpack2(uint64_t w, uint32_t (&o)[8]) {
+    const uint64_t t0 = q4_shl64<3>(w), t1 = q4_shr64<1>(w), t2 = q4_shr64<5>(w),
+                   t3 = q4_shr64<9>(w);
+    o[0] = ((uint32_t)t0 & kQ4Mask) ^ kQ4Code;
+    o[1] = ((uint32_t)t1 & kQ4Mask) ^ kQ4Code;
+    o[2] = ((uint32_t)t2 & kQ4Mask) ^ kQ4Code;
+    o[3] = ((uint32_t)t3 & kQ4Mask) ^ kQ4Code;
+    o[4] = ((uint32_t)(t0 >> 32) & kQ4Mask) ^ kQ4Code;
+    o[5] = ((uint32_t)(t1 >> 32) & kQ4Mask) ^ kQ4Code;
+    o[6] = ((uint32_t)(t2 >> 32) & kQ4Mask) ^ kQ4Code;
+    o[7] = ((uint32_t)(t3 >> 32) & kQ4Mask) ^ kQ4Code;
+}
+
 __device__ __forceinline__ uint32_t fbits(float v) { return __builtin_bit_cast(uint32_t, v); }
 __device__ __forceinline__ float bitsf(uint32_t v) { return __builtin_bit_cast(float, v); }
 

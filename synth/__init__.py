@@ -110,3 +110,24 @@ def from_bits(a, dtype=torch.bfloat16, device="cpu"):
     """Tensor of the given 16-bit float dtype holding the uint16 bit patterns a."""
     a = np.ascontiguousarray(a, dtype=np.uint16)
     return torch.from_numpy(a.view(np.int16)).view(dtype).to(device)
+
+
+def outlier_weight(seed, n, k, lo=30.0, hi=50.0, shared=False, group=64):
+    """bf16 [n, k] weights dominated by one outlier per group of `group`
+    consecutive k: N(0, W_STD^2) draws, with one entry per group replaced by
+    +-U(lo, hi) * W_STD.  Quantised with one scale per group, such a group has
+    a single code of magnitude 7 and almost every other code 0.  shared: the
+    outlier sits at the same position of a group in every row.  Returns the
+    tensor (CPU) and the outlier positions, an int64 [n, k / group] array of k
+    indices."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) & ((1 << 63) - 1))
+    t = torch.randn((n, k), generator=g, dtype=torch.float32) * W_STD
+    G = k // group
+    rows = 1 if shared else n
+    pos = torch.randint(0, group, (rows, G), generator=g) + torch.arange(G) * group
+    mag = (torch.rand((rows, G), generator=g) * (hi - lo) + lo) * W_STD
+    sign = torch.where(torch.rand((rows, G), generator=g) < 0.5, -1.0, 1.0)
+    pos, val = pos.expand(n, G), (mag * sign).expand(n, G)
+    t.scatter_(1, pos, val)
+    return t.to(torch.bfloat16), pos.numpy().astype(np.int64)

@@ -540,24 +540,38 @@ def lin_set_config(kind, M, N, K, cfg):
 TUNING_DIR = os.path.join(_HERE, "tuning")
 
 
+def device_arch(index=0):
+    """The gfx architecture name of a GPU (e.g. "gfx950"), without feature flags."""
+    return torch.cuda.get_device_properties(index).gcnArchName.split(":")[0]
+
+
 def save_tuning(path, entries):
-    """Persist tuned configurations: entries = {(kind, M, N, K): cfg dict}."""
+    """Persist tuned configurations: entries = {(kind, M, N, K): cfg dict}.  The
+    table records the architecture and compute-unit count it was tuned on."""
     rows = [dict(kind=k[0], M=k[1], N=k[2], K=k[3], cfg={f: v.get(f, 0) for f in
             ("algo", "rows", "unroll", "split", "stage_x", "tile_m", "waves", "us")})
             for k, v in sorted(entries.items())]
+    props = torch.cuda.get_device_properties(0)
     with open(path, "w") as f:
-        json.dump({"device": torch.cuda.get_device_name(0) if torch.cuda.is_available() else "",
+        json.dump({"device": props.name, "arch": device_arch(0),
+                   "compute_units": props.multi_processor_count,
                    "version": lin_version(), "entries": rows}, f, indent=1)
 
 
 def load_tuning(path):
     """Pin every configuration of a tuning file that this library still offers;
-    returns the keys applied and the keys that no longer match a candidate."""
+    returns the keys applied and the keys that no longer match a candidate.  A
+    table tuned on another architecture or compute-unit count applies nothing
+    (every key is returned as stale)."""
     with open(path) as f:
         data = json.load(f)
+    keys = [(e["kind"], e["M"], e["N"], e["K"]) for e in data["entries"]]
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    if data.get("arch") != device_arch(torch.cuda.current_device()) or \
+            data.get("compute_units") != props.multi_processor_count:
+        return [], keys
     ok, stale = [], []
-    for e in data["entries"]:
-        key = (e["kind"], e["M"], e["N"], e["K"])
+    for e, key in zip(data["entries"], keys):
         try:
             lin_set_config(*key, e["cfg"])
             ok.append(key)

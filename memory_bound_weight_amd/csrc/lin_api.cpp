@@ -184,10 +184,15 @@ int lookup(int kind, int64_t M, int64_t N, int64_t K) {
 
 // Split-K workspace per device.  Grown only by the load-time calls
 // (lin_autotune, lin_set_config), after a device synchronisation, and zeroed so
-// that every tile counter starts at 0; kernels leave the counters at 0.
+// that every tile counter starts at 0; kernels leave the counters at 0.  A
+// launch bakes the workspace address into its arguments, and a graph captured
+// from it keeps that address, so a workspace is never freed: when it grows,
+// the old buffer stays allocated (and its counters at 0) until the process
+// ends, and graphs captured before the growth keep working on it.
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
+    std::vector<void*> retired;   // earlier, smaller buffers (never freed)
 };
 std::map<int, Workspace>& workspaces() {
     static auto* w = new std::map<int, Workspace>();
@@ -204,16 +209,15 @@ int ensure_workspace(int dev, size_t bytes) {
     Workspace& w = workspaces()[dev];
     if (w.bytes >= bytes) return LIN_OK;
     if (hipDeviceSynchronize() != hipSuccess) return LIN_ERR_HIP;
-    if (w.ptr) (void)hipFree(w.ptr);
-    w.ptr = nullptr;
-    w.bytes = 0;
     const size_t want = bytes + (bytes >> 2);   // headroom for nearby shapes
-    if (hipMalloc(&w.ptr, want) != hipSuccess) {
-        w.ptr = nullptr;
+    void* p = nullptr;
+    if (hipMalloc(&p, want) != hipSuccess) return LIN_ERR_HIP;
+    if (hipMemset(p, 0, want) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        w.retired.push_back(p);   // not handed out; kept like the others
         return LIN_ERR_HIP;
     }
-    if (hipMemset(w.ptr, 0, want) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
-        return LIN_ERR_HIP;
+    if (w.ptr) w.retired.push_back(w.ptr);
+    w.ptr = p;
     w.bytes = want;
     return LIN_OK;
 }

@@ -3,9 +3,10 @@
 One step = one batch-1 decode pass over a model's linear weights: every matrix
 y = W . x once, in model order (q|k|v and gate|up concatenated at load), each
 format's pass captured as a HIP graph and replayed.  The
-default workload is the TinyLlama-1.1B-shaped weight set (22 layers x {q, k,
-v, o, gate, up, down} + output head), run once in bf16 and once in int4-g64;
-the value is the achieved HBM rate over the algorithmic bytes of the step.
+default workload is the Qwen2.5-7B-shaped weight set (28 layers x {q, k, v,
+o, gate, up, down} + output head, 14.1 GB in bf16), run once in bf16 and once
+in int4-g64; the value is the achieved HBM rate over the algorithmic bytes of
+the step.  --workload tinyllama runs the TinyLlama-1.1B-shaped set.
 Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line (see the keys below).  --gpus N with N > 1 is refused:
@@ -28,6 +29,8 @@ import memory_bound_weight_amd as L  # noqa: E402
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, 8 TB/s
+# worker threads of the oracle's timed sample: the host's share for one GPU
+CPU_THREADS = min(16, os.cpu_count() or 1)
 METRIC = "achieved HBM GB/s (% of MI355X peak) + equiv. decode tok/s, batch 1"
 
 
@@ -498,7 +501,7 @@ def run_skinny(args, dev, fmt):
            "pct_of_hbm_peak": round(100.0 * step_bytes / wall / 1e9 / HBM_PEAK_GBS, 2),
            "gpu_ms_per_step": round(gpu * 1e3, 4), "cases": per_case, "roofline": roofline}
     if not args.skip_cpu:
-        out["cpu_baseline"] = cpu_baseline_skinny(min(16, os.cpu_count() or 1), fmt)
+        out["cpu_baseline"] = cpu_baseline_skinny(CPU_THREADS, fmt)
     print(json.dumps(out), flush=True)
 
 
@@ -656,7 +659,8 @@ def run_epilogues(sets, fmts, args):
 
 def cpu_baseline(model, layers, threads, fmts=("bf16", "q4")):
     """The oracle, as it stands, on the host cores: a bounded sample (the first
-    `layers` layers, in the same formats), rows split over `threads` threads."""
+    `layers` layers, in the same formats), rows split over `threads` threads;
+    then one thread over the attention projections of layer 0."""
     import oracle
     work = []
     for layer, idx, name, N, K in synth.decode_matrices(model):
@@ -665,17 +669,17 @@ def cpu_baseline(model, layers, threads, fmts=("bf16", "q4")):
         W = synth.bits(synth.weight(model["seed"], layer, idx, N, K))
         x = synth.bits(synth.activation(model["seed"], layer, idx, 1, K))
         if "bf16" in fmts:
-            work.append(("bf16", W, None, x, bytes_bf16(N, K)))
+            work.append(("bf16", W, None, x, bytes_bf16(N, K), layer, name))
         if "q4" in fmts:
             Wq, S = oracle.quantize_q4g64(W)
-            work.append(("q4", Wq, S, x, bytes_q4(N, K)))
+            work.append(("q4", Wq, S, x, bytes_q4(N, K), layer, name))
         if "i8" in fmts:
             Wq, S = oracle.quantize_i8(W)
-            work.append(("i8", Wq, S, x, bytes_i8(N, K)))
+            work.append(("i8", Wq, S, x, bytes_i8(N, K), layer, name))
     total_bytes = sum(w[4] for w in work)
 
     def run_rows(item, lo, hi):
-        fmt, A, S, x, _ = item
+        fmt, A, S, x = item[:4]
         if fmt == "bf16":
             oracle.gemm_dense(A[lo:hi], x)
         elif fmt == "q4":
@@ -695,23 +699,25 @@ def cpu_baseline(model, layers, threads, fmts=("bf16", "q4")):
         return time.perf_counter() - t0
 
     dt = timed(work, threads)
-    # one thread on the first layer's matrices (a shorter sample of the same work)
-    first = work[:len(fmts) * len(model["layer"])]
+    # one thread on the attention projections of layer 0 (a shorter sample)
+    first = [w for w in work if w[5] == 0 and w[6] in ("q", "k", "v", "o")]
     dt1 = timed(first, 1)
     b1 = sum(w[4] for w in first)
     step_bytes = sum((bytes_bf16 if f == "bf16" else bytes_q4 if f == "q4" else bytes_i8)(N, K)
                      for f in fmts for _, _, _, N, K in synth.decode_matrices(model))
     gbs = total_bytes / dt / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads,
+            "host_cores": os.cpu_count(),
             "kind": "oracle",
             "sample": "%s layers 0-%d (%d matrices), %s, %.1f MB of weights, "
-                      "batch 1, fp64 sequential sums, %.2f s wall"
+                      "batch 1, fp64 sequential sums, %d threads, %.2f s wall"
                       % (model["name"], layers - 1, len(work) // len(fmts),
-                         " and ".join(FORMAT_NAMES[f] for f in fmts), total_bytes / 1e6, dt),
-            "s_per_step": round(step_bytes / (gbs * 1e9), 3),
-            "equiv_tok_s": round(gbs * 1e9 / step_bytes, 4),
+                         " and ".join(FORMAT_NAMES[f] for f in fmts), total_bytes / 1e6,
+                         threads, dt),
+            "s_per_step_extrapolated": round(step_bytes / (gbs * 1e9), 3),
+            "equiv_tok_s_extrapolated": round(gbs * 1e9 / step_bytes, 4),
             "one_thread": {"value": round(b1 / dt1 / 1e9, 4), "unit": "GB/s",
-                           "sample": "layer 0 (%d matrices), %.1f MB, %.2f s wall"
+                           "sample": "layer 0 q, k, v, o (%d matrices), %.1f MB, %.2f s wall"
                                      % (len(first) // len(fmts), b1 / 1e6, dt1)},
             "cpu_model": cpu_model()}
 
@@ -749,7 +755,7 @@ def cpu_baseline_skinny(threads, fmt="bf16", rows=96):
         list(ex.map(lambda j: fn(*j[0], j[1]), jobs))
     dt = time.perf_counter() - t0
     return {"value": round(total / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "host_cores": os.cpu_count(), "kind": "oracle",
             "sample": "first %d rows of each of the %d shapes x M in %s, fp64 sequential sums, "
                       "%.2f s wall" % (rows, len(synth.MISTRAL_SHAPES), list(synth.MISTRAL_M), dt)}
 
@@ -761,7 +767,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="tinyllama",
+    ap.add_argument("--workload", default="qwen7b",
                     choices=["tinyllama", "qwen7b", "mistral-skinny", "mistral-skinny-q4"])
     ap.add_argument("--tune", action="store_true",
                     help="re-run lin_autotune for every shape and rewrite the tuning table")
@@ -780,7 +786,9 @@ def main():
                     help="write the tuning table, with any entries tuned by this run, to PATH")
     ap.add_argument("--no-fuse", action="store_true",
                     help="one launch per matrix instead of q|k|v and gate|up concatenated")
-    ap.add_argument("--cpu-layers", type=int, default=16)
+    ap.add_argument("--cpu-layers", type=int, default=None,
+                    help="layers in the oracle's timed sample (default: 8 for qwen7b, 16 for "
+                         "tinyllama)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES three times (scales the HBM "
@@ -891,7 +899,8 @@ def main():
             sys.exit(2)
         out["epilogues"] = run_epilogues(sets, fmts, args)
     if not args.skip_cpu:
-        out["cpu_baseline"] = cpu_baseline(model, args.cpu_layers, min(16, os.cpu_count() or 1), fmts)
+        layers = args.cpu_layers or (16 if model is synth.TINYLLAMA else 8)
+        out["cpu_baseline"] = cpu_baseline(model, layers, CPU_THREADS, fmts)
     print(json.dumps(out), flush=True)
 
 

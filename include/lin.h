@@ -80,7 +80,9 @@ typedef enum lin_status {
     LIN_ERR_ALIGN = -3,       /* W, Wq, Wi, Wt, St, x or X not 16-byte aligned; y, Y, Si not 4-byte; S not 2-byte */
     LIN_ERR_UNSUPPORTED = -4, /* the requested configuration cannot run this shape */
     LIN_ERR_HIP = -5,         /* the HIP runtime reported an error */
-    LIN_ERR_ARG = -6          /* unknown kind, malformed configuration, bad index */
+    LIN_ERR_ARG = -6,         /* unknown kind, malformed configuration, bad index */
+    LIN_ERR_SCRATCH = -7      /* lin_gemm_skinny_bf16_noalloc: the configuration needs more
+                                 split-K scratch than LIN_STATIC_SCRATCH_BYTES */
 } lin_status;
 
 /* The products; `kind` selects one in the tuning calls. */
@@ -224,6 +226,28 @@ int lin_gemv_i8_norm(const void* Wi, const void* Si, const void* x, const void* 
  * the matrix cores; the crossover is part of the tuned configuration. */
 int lin_gemm_skinny_bf16(const void* W, const void* X, float* Y,
                          int64_t M, int64_t N, int64_t K, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc): the product of
+ * lin_gemm_skinny_bf16, in configuration *cfg (one of the candidates of
+ * (LIN_KIND_SKINNY_BF16, M, N, K); NULL: the configuration lin_get_config
+ * reports), where a split-K configuration keeps its partial tiles and tile
+ * counters in a static device array of LIN_STATIC_SCRATCH_BYTES instead of the
+ * library's workspace, so it needs no earlier lin_set_config or lin_autotune
+ * to reserve one.  Allocates no device memory and never synchronises.  The
+ * array is part of the library's code object: each GPU the library runs on
+ * holds one copy until the process ends.  The first call on a device looks up
+ * the array's address and clears its tile counters with a small kernel on
+ * `stream`; split-K kernels leave the counters cleared.  Every call on a GPU
+ * shares that GPU's array: calls whose configurations use split-K must not
+ * overlap on one GPU (different streams or host threads race on it).  A
+ * configuration needing more than the array returns LIN_ERR_SCRATCH, an
+ * unknown one LIN_ERR_UNSUPPORTED; the other argument rules are those of
+ * lin_gemm_skinny_bf16. */
+#define LIN_STATIC_SCRATCH_BYTES (16u << 20)
+int lin_gemm_skinny_bf16_noalloc(const void* W, const void* X, float* Y,
+                                 int64_t M, int64_t N, int64_t K, const lin_config* cfg,
+                                 void* stream);
 
 /* Batched-token product with int4-g64 weights, for 1 <= M <= LIN_SKINNY_MAX_M
  * tokens: Y[m][n] = sum_k q[n][k] * S[n][k/64] * X[m][k], fp32 Y [M][N], bf16 X

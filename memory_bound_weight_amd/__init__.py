@@ -23,6 +23,8 @@ LIN_ERR_ALIGN = -3
 LIN_ERR_UNSUPPORTED = -4
 LIN_ERR_HIP = -5
 LIN_ERR_ARG = -6
+LIN_ERR_SCRATCH = -7
+LIN_STATIC_SCRATCH_BYTES = 16 << 20
 
 LIN_KIND_GEMV_BF16 = 0
 LIN_KIND_GEMV_Q4G64 = 1
@@ -47,7 +49,7 @@ LIN_SKINNY_MAX_M = 256
 EXPORTS = ("lin_gemv_bf16", "lin_gemv_q4g64", "lin_gemv_bf16_ep", "lin_gemv_q4g64_ep",
            "lin_gemv_bf16_norm", "lin_gemv_q4g64_norm", "lin_gemv_i8", "lin_gemv_i8_ep",
            "lin_gemv_i8_norm", "lin_gemm_skinny_bf16",
-           "lin_gemm_skinny_q4g64", "lin_quantize_i8",
+           "lin_gemm_skinny_bf16_noalloc", "lin_gemm_skinny_q4g64", "lin_quantize_i8",
            "lin_q4g64_tiled_size", "lin_q4g64_tile", "lin_autotune",
            "lin_autotune_set", "lin_num_candidates", "lin_candidate", "lin_get_config", "lin_set_config",
            "lin_quantize_q4g64", "lin_stream_read", "lin_status_string", "lin_version")
@@ -95,6 +97,7 @@ def _load():
         "lin_gemv_i8_norm": [P, P, P, P, ctypes.c_float, P, I64, I64, I64, I, P, P],
         "lin_quantize_i8": [P, P, P, I64, I64, P],
         "lin_gemm_skinny_bf16": [P, P, P, I64, I64, I64, P],
+        "lin_gemm_skinny_bf16_noalloc": [P, P, P, I64, I64, I64, ctypes.POINTER(LinConfig), P],
         "lin_gemm_skinny_q4g64": [P, P, P, P, I64, I64, I64, P],
         "lin_q4g64_tiled_size": [I64, I64, ctypes.POINTER(I64), ctypes.POINTER(I64)],
         "lin_q4g64_tile": [P, P, P, P, I64, I64, P],
@@ -364,6 +367,27 @@ def lin_gemm_skinny_bf16(W, X, Y=None):
     Y = _out(Y, M, N, W.device)
     _check(_lib.lin_gemm_skinny_bf16(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K,
                                      _stream(W)), "lin_gemm_skinny_bf16")
+    return Y
+
+
+def lin_gemm_skinny_bf16_noalloc(W, X, Y, cfg=None):
+    """lin_gemm_skinny_bf16 without any device allocation: split-K
+    configurations use the library's static scratch array.  Y must be given
+    (nothing is allocated here either); cfg: a candidate dict, or None for the
+    configuration lin_get_config reports."""
+    X = _as2d(X)
+    _need(W, torch.bfloat16, "W", 2)
+    _need(X, torch.bfloat16, "X", 2)
+    N, K = W.shape
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X must have K = %d columns" % K)
+    _need(Y, torch.float32, "Y", 2)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be [%d, %d]" % (M, N))
+    c = ctypes.byref(LinConfig.from_dict(cfg)) if cfg is not None else None
+    _check(_lib.lin_gemm_skinny_bf16_noalloc(W.data_ptr(), X.data_ptr(), Y.data_ptr(), M, N, K,
+                                             c, _stream(W)), "lin_gemm_skinny_bf16_noalloc")
     return Y
 
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -242,8 +243,11 @@ bool allow_lds(size_t lds, const void* func) {
 
 // geom_n: the row count the launch grid is sized for, when it differs from a.N
 // (the gated epilogue).
+// ws: split-K workspace to use instead of the device's library-owned one
+// (the static scratch of the allocation-free entry point), or nullptr.
 int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = nullptr,
-                   hipEvent_t ev1 = nullptr, const void* func = nullptr, int64_t geom_n = -1) {
+                   hipEvent_t ev1 = nullptr, const void* func = nullptr, int64_t geom_n = -1,
+                   void* ws = nullptr) {
     const Variant& v = registry()[vi];
     if (!func) func = v.func;
     dim3 grid;
@@ -255,7 +259,9 @@ int launch_variant(int vi, const KArgs& a, hipStream_t stream, hipEvent_t ev0 = 
     args.splits = v.cfg.algo == LIN_ALGO_MFMA ? v.cfg.split : 1;
     args.ws = nullptr;
     const size_t need = workspace_need(v, a.M, a.N, a.K);
-    if (need) {
+    if (need && ws) {
+        args.ws = ws;
+    } else if (need) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess) return LIN_ERR_HIP;
         std::lock_guard<std::mutex> lk(g_mu);
@@ -348,6 +354,9 @@ const char* lin_status_string(int status) {
         case LIN_ERR_UNSUPPORTED: return "configuration not available for this shape";
         case LIN_ERR_HIP: return "the HIP runtime reported an error";
         case LIN_ERR_ARG: return "invalid argument";
+        case LIN_ERR_SCRATCH:
+            return "the product needs more split-K scratch than the static array holds "
+                   "(LIN_STATIC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -769,3 +778,88 @@ int lin_autotune_set(int kind, const void* const* W, const void* const* S, int c
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free entry point
+
+namespace lin {
+namespace {
+
+// Split-K scratch of lin_gemm_skinny_bf16_noalloc: a file-scope device array,
+// one copy per GPU, held until the process ends.  Layout as the library-owned
+// workspace: kMaxTileCounters 32-bit tile counters, then the partial tiles.
+constexpr size_t kStaticScratchBytes = LIN_STATIC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes > (size_t)kMaxTileCounters * 4, "room for the partial tiles");
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+__global__ void zero_words(uint32_t* p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// Per device: the array's device address (from hipGetSymbolAddress with that
+// device current; host code never passes the array's name itself) and whether
+// its tile counters have been cleared.  Fixed slots, so no host allocation.
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+    std::atomic<int> ready{0};
+    void* ptr = nullptr;
+};
+ScratchSlot g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address of the current device `dev`.  The first call on a
+// device resolves it and clears the tile counters with a fill kernel on
+// `stream` (stream-ordered before the caller's product; no memset node).
+// Split-K kernels leave every counter they use at 0 again, so later calls
+// find them cleared.
+int device_scratch(int dev, hipStream_t stream, void** out) {
+    if (dev < 0 || dev >= kMaxDevices) return LIN_ERR_UNSUPPORTED;
+    ScratchSlot& slot = g_scratch[dev];
+    if (slot.ready.load(std::memory_order_acquire)) {
+        *out = slot.ptr;
+        return LIN_OK;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!slot.ready.load(std::memory_order_relaxed)) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LIN_ERR_HIP;
+        hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, stream, (uint32_t*)p,
+                           kMaxTileCounters);
+        if (hipGetLastError() != hipSuccess) return LIN_ERR_HIP;
+        slot.ptr = p;
+        slot.ready.store(1, std::memory_order_release);
+    }
+    *out = slot.ptr;
+    return LIN_OK;
+}
+
+// The registry entry of `kind` matching cfg for this shape, found without
+// building a candidate list.
+int match_variant(int kind, int64_t M, int64_t N, int64_t K, const lin_config& cfg) {
+    const auto& reg = registry();
+    for (int i = 0; i < (int)reg.size(); ++i)
+        if (same_cfg(reg[i].cfg, cfg) && applicable(reg[i], kind, M, N, K)) return i;
+    return -1;
+}
+
+}  // namespace
+}  // namespace lin
+
+extern "C" int lin_gemm_skinny_bf16_noalloc(const void* W, const void* X, float* Y, int64_t M,
+                                            int64_t N, int64_t K, const lin_config* cfg,
+                                            void* stream) {
+    const int kind = LIN_KIND_SKINNY_BF16;
+    int st = check(kind, W, nullptr, X, Y, M, N, K);
+    if (st != LIN_OK) return st > 0 ? LIN_OK : st;
+    const int vi = cfg ? match_variant(kind, M, N, K, *cfg) : lookup(kind, M, N, K);
+    if (vi < 0) return LIN_ERR_UNSUPPORTED;
+    const size_t need = workspace_need(registry()[vi], M, N, K);
+    void* ws = nullptr;
+    if (need) {
+        if (need > kStaticScratchBytes) return LIN_ERR_SCRATCH;
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return LIN_ERR_HIP;
+        if (int rc = device_scratch(dev, (hipStream_t)stream, &ws)) return rc;
+    }
+    KArgs a{W, nullptr, X, Y, (int)M, (int)N, (int)K, 1, nullptr};
+    return launch_variant(vi, a, (hipStream_t)stream, nullptr, nullptr, nullptr, -1, ws);
+}

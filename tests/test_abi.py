@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
 def test_version_and_status_strings():
     assert L.lin_version() >> 16 == 1
     for st in (L.LIN_OK, L.LIN_ERR_NULL, L.LIN_ERR_SHAPE, L.LIN_ERR_ALIGN,
-               L.LIN_ERR_UNSUPPORTED, L.LIN_ERR_HIP, L.LIN_ERR_ARG):
+               L.LIN_ERR_UNSUPPORTED, L.LIN_ERR_HIP, L.LIN_ERR_ARG, L.LIN_ERR_SCRATCH):
         assert L.status_string(st) != "unknown status"
     assert L.status_string(12345) == "unknown status"
 
@@ -49,6 +49,8 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_i8", (P, P, P, P, 1, 8, 24, None), L.LIN_ERR_SHAPE),
     ("lin_gemv_i8", (P, P, P, P, 9, 8, 32, None), L.LIN_ERR_SHAPE),
     ("lin_gemm_skinny_bf16", (P, P, P, 257, 8, 8, None), L.LIN_ERR_SHAPE),
+    ("lin_gemm_skinny_bf16_noalloc", (P, P, P, 257, 8, 8, None, None), L.LIN_ERR_SHAPE),
+    ("lin_gemm_skinny_bf16_noalloc", (P, P, P, 4, 8, 12, None, None), L.LIN_ERR_SHAPE),
     ("lin_gemm_skinny_q4g64", (P, P, P, P, 257, 8, 64, None), L.LIN_ERR_SHAPE),
     ("lin_gemm_skinny_q4g64", (P, P, P, P, 4, 8, 96, None), L.LIN_ERR_SHAPE),
     # empty calls succeed without pointers
@@ -57,6 +59,7 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_q4g64", (None, None, None, None, 0, 0, 64, None), L.LIN_OK),
     ("lin_gemv_i8", (None, None, None, None, 0, 8, 32, None), L.LIN_OK),
     ("lin_gemm_skinny_bf16", (None, None, None, 0, 0, 0, None), L.LIN_OK),
+    ("lin_gemm_skinny_bf16_noalloc", (None, None, None, 0, 8, 8, None, None), L.LIN_OK),
     ("lin_gemm_skinny_q4g64", (None, None, None, None, 0, 8, 64, None), L.LIN_OK),
     # null pointers
     ("lin_gemv_bf16", (P, P, None, 1, 8, 8, None), L.LIN_ERR_NULL),
@@ -65,6 +68,7 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_q4g64", (P, None, P, P, 1, 8, 64, None), L.LIN_ERR_NULL),
     ("lin_gemv_i8", (P, None, P, P, 1, 8, 32, None), L.LIN_ERR_NULL),
     ("lin_gemm_skinny_bf16", (P, P, None, 4, 8, 8, None), L.LIN_ERR_NULL),
+    ("lin_gemm_skinny_bf16_noalloc", (P, P, None, 4, 8, 8, None, None), L.LIN_ERR_NULL),
     ("lin_gemm_skinny_q4g64", (P, None, P, P, 4, 8, 64, None), L.LIN_ERR_NULL),
     # alignment
     ("lin_gemv_bf16", (P + 8, P, P, 1, 8, 8, None), L.LIN_ERR_ALIGN),
@@ -74,6 +78,7 @@ P = 1 << 20   # a 16-byte aligned fake address; never dereferenced
     ("lin_gemv_i8", (P, P + 2, P, P, 1, 8, 32, None), L.LIN_ERR_ALIGN),
     ("lin_gemv_i8", (P + 8, P, P, P, 1, 8, 32, None), L.LIN_ERR_ALIGN),
     ("lin_gemm_skinny_bf16", (P + 4, P, P, 4, 8, 8, None), L.LIN_ERR_ALIGN),
+    ("lin_gemm_skinny_bf16_noalloc", (P, P + 4, P, 4, 8, 8, None, None), L.LIN_ERR_ALIGN),
     ("lin_gemm_skinny_q4g64", (P, P + 2, P, P, 4, 8, 64, None), L.LIN_ERR_ALIGN),
     ("lin_gemm_skinny_q4g64", (P + 8, P, P, P, 4, 8, 64, None), L.LIN_ERR_ALIGN),
 ])

@@ -29,6 +29,7 @@ const std::vector<Variant>& registry() {
         register_gemm_q4_ring(*r);
         register_gemv_i8(*r);
         register_gemv_q4t(*r);
+        register_gemv_q4x(*r);
         return r;
     }();
     return *reg;

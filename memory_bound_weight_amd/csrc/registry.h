@@ -39,6 +39,7 @@ void register_gemm_mfma_ring(std::vector<Variant>& out);
 void register_gemm_q4_ring(std::vector<Variant>& out);
 void register_gemv_i8(std::vector<Variant>& out);
 void register_gemv_q4t(std::vector<Variant>& out);
+void register_gemv_q4x(std::vector<Variant>& out);
 
 // Quantiser launches (int4-g64 and INT8 weight preparation).
 hipError_t launch_quantize_q4g64(const void* W, void* Wq, void* S, int N, int K, hipStream_t stream);

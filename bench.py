@@ -143,6 +143,10 @@ def autotune(mats, only=None, norms=False):
                 groups.setdefault(key, []).append(m)
     seen = {}
     for key, ms in groups.items():
+        # time every candidate over more distinct weights than the caches hold,
+        # as the step streams them (a shape's layers alone may fit the 256 MB
+        # Infinity Cache)
+        ms = with_copies(ms, 600 << 20)
         m = ms[0]
         if m.fmt == "bf16":
             cfg = L.lin_autotune_set(key[0], [g.W for g in ms], m.x, m.y)
@@ -151,6 +155,7 @@ def autotune(mats, only=None, norms=False):
         seen[key] = cfg
         log("tuned kind %d %-5s %6d x %-6d over %d matrices -> %s" % (key[0], m.fmt, m.N, m.K,
                                                                     len(ms), cfg))
+        del ms
     return seen
 
 

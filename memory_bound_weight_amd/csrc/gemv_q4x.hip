@@ -128,7 +128,10 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_xres(KArgs a) {
     }
     u32x4 w[P][NR][J];
     uint16_t sc[P][NR][J];
+    // The scheduling barriers keep every row's loads where they are issued
+    // (left free, the scheduler may sink them next to their products).
     auto issue = [&](int s, int i) {   // output o0 + i (past n_out: zeros, no access)
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < NR; ++r)
 #pragma unroll
@@ -139,6 +142,7 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_xres(KArgs a) {
                 sc[s][r][j] = __builtin_amdgcn_raw_buffer_load_b16(rs[r], (int)soff[j],
                                                                    i * sstride, kNontemporal);
             }
+        __builtin_amdgcn_sched_barrier(0);
     };
     constexpr int PRE = P < RW ? P : RW;
 #pragma unroll

@@ -255,6 +255,18 @@ def replay_times(g, reps, warmup):
     return [a.elapsed_time(b) / 1000.0 for a, b in ev]
 
 
+def counter_pass(mats):
+    """Two eager passes over the step's launches, in step order, one dispatch per
+    launch, for a profiler's per-dispatch counters; prints the launch list
+    (variant, shape) that the counter converter matches the last pass against."""
+    seq = [[variant_key(m), "%dx%d" % (m.N, m.K)] for m in mats]
+    for _ in range(2):
+        for m in mats:
+            launch(m)
+        torch.cuda.synchronize()
+    print(json.dumps({"counter_pass": seq, "passes": 2}), flush=True)
+
+
 def quartiles(ts):
     q1, q2, q3 = np.percentile(np.asarray(ts, dtype=np.float64), [25, 50, 75])
     return q2, q3 - q1
@@ -795,6 +807,10 @@ def main():
                     help="layers in the oracle's timed sample (default: 8 for qwen7b, 16 for "
                          "tinyllama)")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="only launch every matrix of the decode step once, eagerly and in step "
+                         "order, twice over (the dispatches a profiler's HBM byte counters are "
+                         "read from), print the launch list and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES three times (scales the HBM "
                          "byte counters of a profiler run) and exit")
@@ -832,6 +848,9 @@ def main():
     tfile = args.tuning or os.path.join(L.TUNING_DIR, "%s.json" % tname)
     tuning = apply_tuning(allm, tfile, args.tune, norms=args.epilogues, save_to=args.save_tuning)
     log("tuning: " + tuning)
+    if args.counter_pass:
+        counter_pass(allm)
+        return
 
     step_bytes = sum(m.bytes for m in allm)
     fmt_bytes = {f: sum(m.bytes for m in sets[f]) for f in sets}
@@ -877,7 +896,9 @@ def main():
     kernels = {k: {"avg_us": round(v["avg_s"] * 1e6, 3), "median_us": round(v["median_s"] * 1e6, 3),
                    "iqr_us": round(v["iqr_s"] * 1e6, 3), "launches": v["launches"],
                    "GB_s": round(v["bytes_per_launch"] / v["avg_s"] / 1e9, 1),
-                   "read_ceiling_GB_s": round(ceil[k], 1)}
+                   "read_ceiling_GB_s": round(ceil[k], 1),
+                   "algorithmic_bytes": int(v["bytes_per_launch"]),
+                   "traffic": measured_traffic(v["variant"], {v["shape"]: 1})}
                for k, v in sorted(kt.items(), key=lambda kv: -kv[1]["step_s"])}
 
     out = {"metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,

@@ -50,6 +50,12 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
 // with agent-scope atomic accesses, which go to the device-coherent level
 // directly, so publishing needs no L2 write-back and reading no L2 invalidate
 // (whole-cache operations on this chip that cost more than the product).
+// Ordering without acquire/release: the partial stores bypass the per-XCD L2s
+// and s_waitcnt(0) returns only once the coherence point has acknowledged
+// them; the barrier then keeps the counter increment (and the compiler) after
+// them.  The workgroup whose increment returns S - 1 therefore runs after
+// every other workgroup's partials are visible at that point, and reads them
+// with agent-scope loads, which do not hit a stale L2 line.
 // Every thread of the workgroup must call this (it contains workgroup
 // barriers when S > 1).
 template <int BN, int TM, int NF, int MT>

@@ -259,7 +259,8 @@ size_t ws_ring(const Variant& v, int M, int N, int K) {
 
 template <int BN, int TM, int D, bool LINE, int NW = 4, int KB = 64>
 void add_ring1(std::vector<Variant>& out, int S) {
-    static_assert(D * Shape<BN, TM, NW, KB>::F * 1024 <= 160 * 1024, "LDS ring too large");
+    // the ring plus the split-K flag must fit the 160 KB of LDS
+    static_assert(D * Shape<BN, TM, NW, KB>::F * 1024 < 160 * 1024, "LDS ring too large");
     Variant v{};
     v.kind = LIN_KIND_SKINNY_BF16;
     v.cfg.algo = LIN_ALGO_MFMA;
@@ -312,6 +313,7 @@ void register_gemm_mfma_ring(std::vector<Variant>& out) {
         add_ring1<128, 128, 3, true, 8>(out, S);
         add_ring1<256, 128, 3, true, 8>(out, S);
         add_ring1<256, 128, 3, true, 4>(out, S);
+        add_ring1<64, 128, 5, true, 8>(out, S);
     }
 }
 

@@ -217,6 +217,7 @@ def time_runs(fns, steps, warmup):
 
 
 def time_graph(g, steps, warmup):
+    warm(g)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -239,9 +240,26 @@ def variant_key(m):
                                    c["stage_x"])
 
 
+WARM_S = 0.25   # steady state: replay a fresh graph this long before timing it
+
+
+def warm(g, seconds=WARM_S):
+    """Replay a graph for about `seconds`.  The first passes over freshly
+    allocated weights run slower (measured: the Qwen2.5-7B bf16 pass 2.31 ms for
+    its first ~0.1 s, 2.20 ms from then on, also after an idle pause), so every
+    timed graph is first brought to that steady state."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            g.replay()
+        torch.cuda.synchronize()
+
+
 def replay_times(g, reps, warmup):
     """Durations (s) of `reps` replays of a graph, each bracketed by its own HIP
-    events on the stream the replays run on."""
+    events on the stream the replays run on, after `warmup` replays and the
+    steady-state warm-up above."""
+    warm(g)
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()

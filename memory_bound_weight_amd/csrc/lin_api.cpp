@@ -744,9 +744,12 @@ int lin_autotune_set(int kind, const void* const* W, const void* const* S, int c
         if (rc == LIN_OK && hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess)
             rc = LIN_ERR_HIP;
         float ms = 0.f;
-        if (rc == LIN_OK && (hipGraphLaunch(ge, ts) != hipSuccess ||   // warm replay
-                             hipEventRecord(e0, ts) != hipSuccess))
-            rc = LIN_ERR_HIP;
+        // warm replays; the first candidate gets more, since the first passes
+        // over freshly allocated matrices run slower than the steady state
+        const int warm = ci == 0 ? 16 : 1;
+        for (int r = 0; r < warm && rc == LIN_OK; ++r)
+            if (hipGraphLaunch(ge, ts) != hipSuccess) rc = LIN_ERR_HIP;
+        if (rc == LIN_OK && hipEventRecord(e0, ts) != hipSuccess) rc = LIN_ERR_HIP;
         for (int r = 0; r < reps && rc == LIN_OK; ++r)
             if (hipGraphLaunch(ge, ts) != hipSuccess) rc = LIN_ERR_HIP;
         if (rc == LIN_OK && (hipEventRecord(e1, ts) != hipSuccess ||

@@ -89,9 +89,21 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_xres(KArgs a) {
     const uint8_t* __restrict__ X = (const uint8_t*)a.X;
 
     // this group's outputs: a balanced contiguous share (at most RW) of the N
-    const int64_t ng = (int64_t)gridDim.x * GROUPS;
-    const int64_t gi = (int64_t)blockIdx.x * GROUPS + grp;
-    const int o0 = (int)(N * gi / ng), o1 = (int)(N * (gi + 1) / ng);
+    // floor(N g / ng) for g = gi, gi + 1.  With N = q ng + r that is
+    // q g + floor(r g / ng), whose products fit 32 bits while ng < 2^16 (every
+    // shape here); the 64-bit division it replaces is a few hundred scalar
+    // instructions in front of the first load of every wavefront.
+    const uint32_t ng = gridDim.x * GROUPS;
+    const uint32_t gi = blockIdx.x * GROUPS + grp;
+    int o0, o1;
+    if (ng < 65536u) {
+        const uint32_t q = (uint32_t)N / ng, r = (uint32_t)N - q * ng;
+        o0 = (int)(q * gi + r * gi / ng);
+        o1 = (int)(q * (gi + 1) + r * (gi + 1) / ng);
+    } else {
+        o0 = (int)((int64_t)N * gi / ng);
+        o1 = (int)((int64_t)N * (gi + 1) / ng);
+    }
     const int n_out = o1 - o0;
 
     // the lane's chunks (clamped to the last chunk; their products are dropped)

@@ -101,6 +101,9 @@ void register_gemv_bf16(std::vector<Variant>& out) {
     add_splits<8, 1, 2>(out);
     add_splits<8, 2, 1>(out);
     add_splits<8, 4, 1>(out);
+    add_splits<8, 2, 2>(out);
+    add_splits<8, 4, 2>(out);
+    add_splits<8, 8, 1>(out);
 
     add_splits<16, 1, 1>(out);
     add_splits<16, 2, 1>(out);

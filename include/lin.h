@@ -115,8 +115,10 @@ typedef enum lin_algo {
  * 64-k block of X is staged in LDS per step; `stage_x` = 3 or 4: W and X
  * blocks both stream through an LDS ring of `unroll` stages filled by direct
  * global-to-LDS loads, in the matrix-core operand order (3) or in whole
- * 128-byte lines with a swizzled layout (4); `waves` = wavefronts per
- * workgroup of the ring kernel (0 means the default, four; 8 puts two on each
+ * 128-byte lines with a swizzled layout (4); `stage_x` = 5: the same line-order
+ * ring with four more wavefronts per workgroup that issue every load, so the
+ * product wavefronts never wait to issue one; `waves` = product wavefronts per
+ * workgroup of the ring kernels (0 means the default, four; 8 puts two on each
  * SIMD).  LIN_KIND_SKINNY_Q4G64 has one family, `stage_x` = 4: codes, scales
  * and X stream through an LDS ring of `unroll` stages of 128 k, `rows` W rows
  * by `tile_m` tokens per workgroup, `split` as above.  `us` is filled by

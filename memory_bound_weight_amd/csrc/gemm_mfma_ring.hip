@@ -45,21 +45,28 @@ namespace {
 
 // Position of k-chunk c (8 k, 16 bytes) in row r of a ring group is
 // c ^ ring_swz(r).  The 16 rows of a group are 128 bytes apart, so unswizzled
-// the 16 lanes reading one chunk of 16 rows would hit the same banks; with
-// this swizzle any 8 consecutive rows, and the 8 even and the 8 odd rows of
-// a group, use 8 different 16-byte positions, which spreads them over the
-// banks whether the LDS serves 128 or 256 bytes per clock.
-__device__ __forceinline__ int ring_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// the 16 lanes reading one chunk of 16 rows would hit the same banks (measured
+// 12 conflict cycles per ds_read_b128).  XOR with the row modulo 8 gives any 8
+// consecutive rows 8 different 16-byte positions; measured on gfx950 that is
+// conflict-free for both 32-k halves.  Also folding in bit 3 of the row (so
+// that all 16 rows differ within 256 bytes) measured 4 conflict cycles per
+// read instead: the banks are not simply the low address bits.
+__device__ __forceinline__ int ring_swz(int r) { return r & 7; }
 
 // The ring's direct-to-LDS loads use dma16 (ordinary cache policy: a
 // non-temporal hint on the weights measured slower); k >= K lanes load
 // g_zero16 instead of reading past a row.
 
-// s_waitcnt with vmcnt <= N (N < 64) and lgkmcnt = 0; expcnt not waited on.
+// s_waitcnt with vmcnt <= V (V < 64, 63 = no wait) and lgkmcnt <= G (G < 16);
+// expcnt not waited on.
+template <int V, int G>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(V >= 0 && V < 64 && G >= 0 && G < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (G << 8));
+}
 template <int N>
 __device__ __forceinline__ void wait_vm_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+    wait_vm_lgkm<N, 0>();
 }
 
 template <int L, int D, int J = 0>
@@ -94,15 +101,90 @@ struct Shape {
     static_assert(KB == 64, "a ring group is 16 rows x 128 bytes");
 };
 
+// Load unit u of a stage (W units 0 .. FW - 1, then X units, then padding):
+// a wavefront-uniform base (the first row of the unit's 16-row group,
+// clamped), the lane's byte offset from it and its k within a block, and the
+// bytes per block (0 for padding, which re-reads the zero word).  Fragment
+// order: unit u is half u % 2 of 16-row group u / 2, lane l takes row l % 16
+// and k 32 (u % 2) + 8 (l / 16).  Line order: unit u is rows 8 (u % 2) .. + 7
+// of group u / 2, lane l takes row 8 (u % 2) + l / 8 and stores, at position
+// l % 8 of that row, k-chunk (l % 8) ^ swz(row).
+template <int BN, int TM, int FW, int FX, int KB, bool LINE>
+__device__ __forceinline__ void ring_unit(const KArgs& a, int u, int lane, int n_tile, int m_tile,
+                                          const uint8_t*& base, uint32_t& voff, int& koff,
+                                          int& step) {
+    const int N = a.N, M = a.M, K = a.K;
+    const int r = LINE ? (u & 1) * 8 + (lane >> 3) : (lane & 15);   // row within the group
+    koff = LINE ? ((lane & 7) ^ ring_swz(r)) * 8 : (u & 1) * 32 + (lane >> 4) * 8;
+    base = (const uint8_t*)&g_zero16;
+    voff = 0;
+    step = 0;
+    if (u < FW + FX) {
+        const bool isw = u < FW;
+        const int lim = isw ? N : M;
+        const int g0 = isw ? n_tile * BN + (u >> 1) * 16 : m_tile * TM + ((u - FW) >> 1) * 16;
+        const int r0 = min(g0, lim - 1);
+        const int row = min(g0 + r, lim - 1);   // rows past the end: computed, never stored
+        base = (const uint8_t*)(isw ? a.W : a.X) + (int64_t)r0 * K * 2;
+        voff = (uint32_t)(row - r0) * (uint32_t)K * 2u + 2u * koff;
+        step = KB * 2;
+    }
+    base = uniform_ptr(base);
+}
+
+// The products of one ring stage for a wavefront: its NF W fragments and MT
+// X fragments of both 32-k halves, read from the stage's units, then H x NF x
+// MT products.  Operand of lane l for half h of a 16-row group: fragment
+// order, entry l of unit 2 g + h; line order, row l % 16 of the group at
+// position (4 h + l / 16) ^ swz(row) (the two units of the group are
+// contiguous).  All operand reads of the stage are issued up front; the
+// scheduler is then asked to interleave the reads of the second half with the
+// products of the first, so that their LDS latency overlaps the matrix cores
+// instead of stalling in front of them.
+template <typename SH, bool LINE>
+__device__ __forceinline__ void stage_products(f32x4 (&acc)[SH::NF][SH::MT], const u32x4 (*st)[64],
+                                               int wr, int wc, int lane) {
+    constexpr int NF = SH::NF, MT = SH::MT, H = SH::H, FW = SH::FW;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const int rsw = ring_swz(l16);
+    auto operand = [&](int unit0, int h) -> u32x4 {
+        if constexpr (LINE)
+            return (&st[unit0][0])[l16 * 8 + ((4 * h + lg) ^ rsw)];
+        else
+            return st[unit0 + h][lane];
+    };
+    u32x4 bw[H][NF], ax[H][MT];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) bw[h][f] = operand(2 * (wr * NF + f), h);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) ax[h][t] = operand(FW + 2 * (wc * MT + t), h);
+    }
+#pragma unroll
+    for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int t = 0; t < MT; ++t) acc[f][t] = mfma16(ax[h][t], bw[h][f], acc[f][t]);
+    // first half's reads, then one read of the second half per product
+    __builtin_amdgcn_sched_group_barrier(0x100, NF + MT, 0);
+#pragma unroll
+    for (int q = 0; q < (H - 1) * (NF + MT); ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, H * NF * MT - (H - 1) * (NF + MT), 0);
+}
+
 template <int BN, int TM, int D, int NW, int KB, bool LINE>
 __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
     using SH = Shape<BN, TM, NW, KB>;
-    constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, F = SH::F, L = SH::L, H = SH::H;
+    constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, F = SH::F, L = SH::L;
     const int M = a.M, N = a.N, K = a.K;
     const int S = a.splits;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
-    const int l16 = lane & 15, lg = lane >> 4;
 
     const int m_tiles = (M + TM - 1) / TM;
     const int n_tiles = (N + BN - 1) / BN;
@@ -116,42 +198,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
 
     __shared__ u32x4 ring[D][F][64];
 
-    // Load units this wavefront issues per stage: u = wave * L + i.  Per lane
-    // a fixed row pointer and k offset within the stage.  Fragment order:
-    // unit u is half u % 2 of 16-row group u / 2, lane l takes row l % 16 and
-    // k 32 (u % 2) + 8 (l / 16).  Line order: unit u is rows 8 (u % 2) .. + 7
-    // of group u / 2, lane l takes row 8 (u % 2) + l / 8 and stores, at
-    // position l % 8 of that row, k-chunk (l % 8) ^ swz(row).
-    // Per unit: a wavefront-uniform base (the first row of its 16-row group,
-    // clamped), the lane's byte offset from it, and the lane's k within a
-    // block.  Steady-state loads use the scalar-base form with no per-lane
-    // address arithmetic; only the last block of a K that is not a multiple of
-    // KB checks each chunk against K (k >= K loads the zero word).  Padding
-    // units read bytes nobody uses.
+    // Load units this wavefront issues per stage: u = wave * L + i.
+    // Steady-state loads use the scalar-base form with no per-lane address
+    // arithmetic; only the last block of a K that is not a multiple of KB
+    // checks each chunk against K (k >= K loads the zero word).  Padding units
+    // read bytes nobody uses.
     const uint8_t* base[L];
     uint32_t voff[L];
     int koff[L];
     int step[L];
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int u = wave * L + i;
-        const int r = LINE ? (u & 1) * 8 + (lane >> 3) : l16;   // row within the group
-        koff[i] = LINE ? ((lane & 7) ^ ring_swz(r)) * 8 : (u & 1) * 32 + lg * 8;
-        base[i] = (const uint8_t*)&g_zero16;
-        voff[i] = 0;
-        step[i] = 0;
-        if (u < FW + SH::FX) {
-            const bool isw = u < FW;
-            const int lim = isw ? N : M;
-            const int g0 = isw ? n_tile * BN + (u >> 1) * 16 : m_tile * TM + ((u - FW) >> 1) * 16;
-            const int r0 = min(g0, lim - 1);
-            const int row = min(g0 + r, lim - 1);   // rows past the end: computed, never stored
-            base[i] = (const uint8_t*)(isw ? a.W : a.X) + (int64_t)r0 * K * 2;
-            voff[i] = (uint32_t)(row - r0) * (uint32_t)K * 2u + 2u * koff[i];
-            step[i] = KB * 2;
-        }
-        base[i] = uniform_ptr(base[i]);
-    }
+    for (int i = 0; i < L; ++i)
+        ring_unit<BN, TM, FW, SH::FX, KB, LINE>(a, wave * L + i, lane, n_tile, m_tile, base[i],
+                                                voff[i], koff[i], step[i]);
     const bool ktail = (K % KB) != 0;
     auto issue = [&](int kb, int slot) {
         if (ktail && kb == nkb_all - 1) {
@@ -182,53 +241,115 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
     for (int d = 0; d < D - 1; ++d)
         if (d < nkb) issue(kb0 + d, d);
 
-    // Operand of lane l for half h of a 16-row group: fragment order, entry l
-    // of unit 2 g + h; line order, row l % 16 of the group at position
-    // (4 h + l / 16) ^ swz(row) (the two units of the group are contiguous).
-    const int rsw = ring_swz(l16);
-    auto operand = [&](int slot, int unit0, int h) -> u32x4 {
-        if constexpr (LINE)
-            return (&ring[slot][unit0][0])[l16 * 8 + ((4 * h + lg) ^ rsw)];
-        else
-            return ring[slot][unit0 + h][lane];
-    };
     for (int i = 0; i < nkb; ++i) {
         wait_stages<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();                  // everyone's loads of stage i landed
         asm volatile("" ::: "memory");
         if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
-        const int slot = i % D;
-        // All operand reads of the stage are issued up front; the scheduler
-        // is then asked to interleave the reads of the second half with the
-        // products of the first, so that their LDS latency overlaps the
-        // matrix cores instead of stalling in front of them.
-        u32x4 bw[H][NF], ax[H][MT];
-#pragma unroll
-        for (int h = 0; h < H; ++h) {
-#pragma unroll
-            for (int f = 0; f < NF; ++f) bw[h][f] = operand(slot, 2 * (wr * NF + f), h);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) ax[h][t] = operand(slot, FW + 2 * (wc * MT + t), h);
-        }
-#pragma unroll
-        for (int h = 0; h < H; ++h)
-#pragma unroll
-            for (int f = 0; f < NF; ++f)
-#pragma unroll
-                for (int t = 0; t < MT; ++t) acc[f][t] = mfma16(ax[h][t], bw[h][f], acc[f][t]);
-        // first half's reads, then one read of the second half per product
-        __builtin_amdgcn_sched_group_barrier(0x100, NF + MT, 0);
-#pragma unroll
-        for (int q = 0; q < (H - 1) * (NF + MT); ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, H * NF * MT - (H - 1) * (NF + MT), 0);
+        stage_products<SH, LINE>(acc, ring[i % D], wr, wc, lane);
     }
 
     // Output: lane holds W row n_tile BN + wr WN + 16 f + l16, tokens
     // m_tile TM + wc WM + 16 t + 4 lg + r.
+    store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,
+                                wc * SH::WM);
+}
+
+
+// Ring with loader wavefronts.  The direct-to-LDS loads of a stage are issued
+// by NL wavefronts of their own; the NW product wavefronts only read
+// operands and multiply.  A load instruction does not leave the issuing
+// wavefront until the compute unit's load path accepts it (about 1 KB per 16
+// cycles), so in the ring above every wavefront stalls for its share of that
+// queue right after the barrier, in lockstep with the others, and the matrix
+// cores idle meanwhile; here those stalls fall on wavefronts that have no
+// products to hold up.  Protocol per iteration i (every wavefront meets every
+// barrier): a loader waits until its loads of stage i have landed, meets the
+// barrier, then refills the slot of stage i - 1 with stage i + D - 1; a product
+// wavefront waits for its own operand reads of stage i - 1, meets the barrier
+// (so stage i has landed and nobody still reads stage i - 1), then multiplies
+// stage i.  For split-K the loaders also meet the two barriers of the store.
+template <int BN, int TM, int D, int NW, int NL>
+__global__ __launch_bounds__(64 * (NW + NL)) void gemm_mfma_ring_ld_kernel(KArgs a) {
+    constexpr int KB = 64;
+    using SH = Shape<BN, TM, NW, KB>;
+    constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, FX = SH::FX;
+    constexpr int LL = (FW + FX + NL - 1) / NL;   // loads per loader and stage
+    constexpr int FP = LL * NL;                    // units per stage, padded
+    static_assert((D - 1) * LL < 64, "vmcnt range");
+    const int M = a.M, N = a.N, K = a.K;
+    const int S = a.splits;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+
+    const int m_tiles = (M + TM - 1) / TM;
+    const int n_tiles = (N + BN - 1) / BN;
+    int n_tile, m_tile, ks;
+    if (!tile_of(blockIdx.x, n_tiles, m_tiles, S, n_tile, ks, m_tile))
+        return;   // padding slot: the whole workgroup leaves together
+    const int nkb_all = (K + KB - 1) / KB;
+    const int bps = (nkb_all + S - 1) / S;
+    const int kb0 = ks * bps;
+    const int nkb = max(0, min(nkb_all, kb0 + bps) - kb0);
+
+    __shared__ u32x4 ring[D][FP][64];
+
+    if (wave >= NW) {
+        const int j = wave - NW;
+        const uint8_t* base[LL];
+        uint32_t voff[LL];
+        int koff[LL];
+        int step[LL];
+#pragma unroll
+        for (int i = 0; i < LL; ++i)
+            ring_unit<BN, TM, FW, FX, KB, true>(a, j * LL + i, lane, n_tile, m_tile, base[i], voff[i],
+                                                koff[i], step[i]);
+        const bool ktail = (K % KB) != 0;
+        auto issue = [&](int kb, int slot) {
+            if (ktail && kb == nkb_all - 1) {
+#pragma unroll
+                for (int i = 0; i < LL; ++i) {
+                    const uint8_t* p = base[i] + (int64_t)kb * step[i] + voff[i];
+                    if (kb * KB + koff[i] >= K) p = (const uint8_t*)&g_zero16;   // K % 8 == 0
+                    dma16(p, &ring[slot][j * LL + i][0]);
+                }
+                return;
+            }
+#pragma unroll
+            for (int i = 0; i < LL; ++i)
+                dma16s(base[i] + (int64_t)kb * step[i], voff[i], &ring[slot][j * LL + i][0]);
+        };
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (d < nkb) issue(kb0 + d, d);
+        for (int i = 0; i < nkb; ++i) {
+            wait_stages<LL, D>(min(D - 2, nkb - 1 - i));   // own loads of stage i landed
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
+        }
+        if (S > 1) {   // the two barriers of the split-K store
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
+
+    f32x4 acc[NF][MT];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wr = wave / SH::WC, wc = wave - (wave / SH::WC) * SH::WC;
+    for (int i = 0; i < nkb; ++i) {
+        wait_vm_lgkm<63, 0>();   // own operand reads of stage i - 1 complete
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        stage_products<SH, true>(acc, ring[i % D], wr, wc, lane);
+    }
     store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,
                                 wc * SH::WM);
 }
@@ -281,6 +402,32 @@ void add_ring1(std::vector<Variant>& out, int S) {
     out.push_back(v);
 }
 
+// Loader-wavefront ring (stage_x 5): NW product wavefronts (`waves`, 0 for
+// four) plus four loader wavefronts, line order.
+template <int BN, int TM, int D, int NW>
+void add_ring_ld(std::vector<Variant>& out, int S) {
+    constexpr int NL = 4;
+    using SH = Shape<BN, TM, NW, 64>;
+    constexpr int FP = (SH::FW + SH::FX + NL - 1) / NL * NL;
+    static_assert(D * FP * 1024 < 160 * 1024, "LDS ring too large");
+    Variant v{};
+    v.kind = LIN_KIND_SKINNY_BF16;
+    v.cfg.algo = LIN_ALGO_MFMA;
+    v.cfg.rows = BN;
+    v.cfg.unroll = D;
+    v.cfg.split = S;
+    v.cfg.stage_x = 5;
+    v.cfg.waves = NW == 4 ? 0 : NW;
+    v.cfg.tile_m = TM;
+    v.mt = 0;
+    v.min_m = TM <= 16 ? 1 : 16;
+    v.func = (const void*)&gemm_mfma_ring_ld_kernel<BN, TM, D, NW, NL>;
+    v.geometry = &geom_ring<BN, TM, D, NW, 64>;
+    v.workspace = &ws_ring<BN, TM, D, NW, 64>;
+    v.block = 64 * (NW + NL);
+    out.push_back(v);
+}
+
 template <int BN, int TM, int D>
 void add_ring(std::vector<Variant>& out, int S) {
     add_ring1<BN, TM, D, false>(out, S);
@@ -314,6 +461,25 @@ void register_gemm_mfma_ring(std::vector<Variant>& out) {
         add_ring1<256, 128, 3, true, 8>(out, S);
         add_ring1<256, 128, 3, true, 4>(out, S);
         add_ring1<64, 128, 5, true, 8>(out, S);
+        add_ring_ld<64, 16, 8, 4>(out, S);
+        add_ring_ld<128, 16, 6, 4>(out, S);
+        add_ring_ld<32, 32, 8, 4>(out, S);
+        add_ring_ld<64, 32, 8, 4>(out, S);
+        add_ring_ld<64, 64, 4, 4>(out, S);
+        add_ring_ld<64, 64, 6, 4>(out, S);
+        add_ring_ld<64, 64, 4, 8>(out, S);
+        add_ring_ld<128, 64, 4, 4>(out, S);
+        add_ring_ld<128, 64, 4, 8>(out, S);
+        add_ring_ld<128, 128, 3, 4>(out, S);
+        add_ring_ld<128, 128, 4, 4>(out, S);
+        add_ring_ld<128, 128, 3, 8>(out, S);
+        add_ring_ld<128, 128, 4, 8>(out, S);
+        add_ring_ld<256, 64, 3, 8>(out, S);
+        add_ring_ld<256, 128, 3, 4>(out, S);
+        add_ring_ld<256, 128, 3, 8>(out, S);
+        add_ring_ld<128, 256, 3, 8>(out, S);
+        add_ring_ld<64, 256, 3, 4>(out, S);
+        add_ring_ld<64, 256, 3, 8>(out, S);
     }
 }
 

@@ -43,8 +43,9 @@ constexpr int kQB = 128;   // k per ring stage and per tiled unit
 constexpr uint32_t kNegOff = kQ4NegOffsetPair;
 
 // Wave tile of a workgroup tile: NW wavefronts as WR x WC (as the bf16 ring).
-template <int BN, int TM, int NW>
+template <int BN_, int TM_, int NW>
 struct Q4Shape {
+    static constexpr int BN = BN_, TM = TM_;
     static constexpr int WR = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4));
     static constexpr int WC = NW / WR;
     static constexpr int WN = BN / WR, WM = TM / WC;
@@ -97,23 +98,115 @@ __device__ __forceinline__ void wait_stages_q4(int after) {
     }
 }
 
+// Load unit u of a stage (code units 0 .. FW - 1, the scale unit FW, X units,
+// then padding): a wavefront-uniform base at block 0, the bytes per block and
+// the lane's byte offset from the base, and for X units the k of the lane's
+// chunk within a block.  Row tiles past the last one re-read the last (their
+// outputs are never stored); lanes of the scale unit past the workgroup's row
+// tiles, and padding units, read bytes nobody uses.  Only X chunks past K must
+// be zero: the last block of a K that is not a multiple of 128 takes the
+// per-lane path with the zero word.
+template <typename SH>
+__device__ __forceinline__ void q4_unit(const KArgs& a, int u, int lane, int n_tile, int m_tile,
+                                        const uint8_t*& base, int64_t& step, uint32_t& voff,
+                                        int& kx) {
+    constexpr int FW = SH::FW, FX = SH::FX, XU = SH::XU, BN = SH::BN, TM = SH::TM;
+    const int M = a.M, N = a.N, K = a.K;
+    const int N16 = (N + 15) >> 4;
+    const int KBn = (K + kQB - 1) / kQB;
+    const int T0 = n_tile * (BN / 16);
+    base = (const uint8_t*)&g_zero16;
+    step = 0;
+    voff = 0;
+    kx = 0;
+    if (u < FW) {
+        const int T = min(T0 + u, N16 - 1);
+        base = (const uint8_t*)a.W + (int64_t)T * KBn * 1024;
+        step = 1024;
+        voff = 16 * lane;
+    } else if (u == FW) {
+        // lanes 4 f .. 4 f + 3 carry the 64-byte unit of row tile f
+        base = (const uint8_t*)a.S + (int64_t)T0 * 64;
+        step = (int64_t)N16 * 64;
+        const int f = min(lane >> 2, FW - 1);
+        voff = 64 * (min(T0 + f, N16 - 1) - T0) + 16 * (lane & 3);
+    } else if (u < XU + FX) {
+        const int x = u - XU;
+        const int r = 4 * (x & 3) + (lane >> 4);   // token row within the 16-token tile
+        const int c = (lane & 15) ^ r;             // chunk stored at position lane & 15
+        int m = m_tile * TM + (x >> 2) * 16 + r;
+        m = m < M ? m : M - 1;                     // rows past M: computed, never stored
+        base = (const uint8_t*)a.X;
+        step = kQB * 2;
+        voff = (uint32_t)m * (uint32_t)K * 2u + 16u * c;
+        kx = 8 * c;
+    }
+    base = uniform_ptr(base);
+}
+
+// The products of one ring stage for a wavefront: per scale group of 64 k,
+// the offset products (X times the constant -24 operand), then for each W
+// fragment the unpacked codes times X, scaled into the accumulators.
+template <typename SH>
+__device__ __forceinline__ void q4_stage_products(f32x4 (&acc)[SH::NF][SH::MT],
+                                                  const u32x4 (*st)[64], int wr, int wc, int lane) {
+    constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, XU = SH::XU;
+    const int l16 = lane & 15, lg = lane >> 4;
+    const u32x4 neg = {kNegOff, kNegOff, kNegOff, kNegOff};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    u32x4 wq[NF];
+    uint32_t sc[NF];
+    const uint32_t* su = (const uint32_t*)&st[FW][0];
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+        wq[f] = st[wr * NF + f][lane];
+        sc[f] = su[(wr * NF + f) * 16 + l16];
+    }
+    // X operand of token tile t, k-step q: row l16, chunk 4 q + lg.
+    u32x4 ax[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+        const u32x4* xt = &st[XU + 4 * (wc * MT + t)][0];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ax[t][q] = xt[l16 * 16 + ((4 * q + lg) ^ l16)];
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {   // the stage's two scale groups
+        f32x4 cor[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            cor[t] = mfma16(ax[t][2 * h], neg, zero);
+            cor[t] = mfma16(ax[t][2 * h + 1], neg, cor[t]);
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            u32x4 b0, b1;
+            unpack2(wq[f][2 * h], wq[f][2 * h + 1], b0, b1);
+            const float s = h ? half_hi(sc[f]) : half_lo(sc[f]);
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                f32x4 d = mfma16(ax[t][2 * h], b0, cor[t]);
+                d = mfma16(ax[t][2 * h + 1], b1, d);
+                acc[f][t] = d * s + acc[f][t];
+            }
+        }
+    }
+}
+
 template <int BN, int TM, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
     using SH = Q4Shape<BN, TM, NW>;
-    constexpr int NF = SH::NF, MT = SH::MT, FW = SH::FW, FX = SH::FX, XU = SH::XU, F = SH::F,
-                  L = SH::L;
+    constexpr int NF = SH::NF, MT = SH::MT, FX = SH::FX, XU = SH::XU, F = SH::F, L = SH::L;
     const int M = a.M, N = a.N, K = a.K;
     const int S = a.splits;
     const int lane = threadIdx.x & 63;
     const int wave = wave_id();
-    const int l16 = lane & 15, lg = lane >> 4;
 
     const int m_tiles = (M + TM - 1) / TM;
     const int n_tiles = (N + BN - 1) / BN;
     int n_tile, m_tile, ks;
     if (!tile_of(blockIdx.x, n_tiles, m_tiles, S, n_tile, ks, m_tile))
         return;   // padding slot: the whole workgroup leaves together
-    const int N16 = (N + 15) >> 4;
     const int KBn = (K + kQB - 1) / kQB;   // 128-k blocks (units per row tile)
     const int bps = (KBn + S - 1) / S;
     const int kb0 = ks * bps;
@@ -121,49 +214,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
 
     __shared__ u32x4 ring[D][F][64];
 
-    // Per unit this wavefront loads: a wavefront-uniform base at block 0, the
-    // bytes per block and the lane's byte offset from the base.  Row tiles past
-    // the last one re-read the last (their outputs are never stored); lanes of
-    // the scale unit past the workgroup's row tiles, and padding units, read
-    // bytes nobody uses.  Only X chunks past K must be zero: the last block of
-    // a K that is not a multiple of 128 takes the per-lane path with the zero
-    // word.
     const uint8_t* base[L];
     int64_t step[L];
     uint32_t voff[L];
     int kx[L];   // X units: k of the lane's chunk within a block
-    const int T0 = n_tile * (BN / 16);
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-        const int u = wave * L + i;
-        base[i] = (const uint8_t*)&g_zero16;
-        step[i] = 0;
-        voff[i] = 0;
-        kx[i] = 0;
-        if (u < FW) {
-            const int T = min(T0 + u, N16 - 1);
-            base[i] = (const uint8_t*)a.W + (int64_t)T * KBn * 1024;
-            step[i] = 1024;
-            voff[i] = 16 * lane;
-        } else if (u == FW) {
-            // lanes 4 f .. 4 f + 3 carry the 64-byte unit of row tile f
-            base[i] = (const uint8_t*)a.S + (int64_t)T0 * 64;
-            step[i] = (int64_t)N16 * 64;
-            const int f = min(lane >> 2, FW - 1);
-            voff[i] = 64 * (min(T0 + f, N16 - 1) - T0) + 16 * (lane & 3);
-        } else if (u < XU + FX) {
-            const int x = u - XU;
-            const int r = 4 * (x & 3) + (lane >> 4);   // token row within the 16-token tile
-            const int c = (lane & 15) ^ r;             // chunk stored at position lane & 15
-            int m = m_tile * TM + (x >> 2) * 16 + r;
-            m = m < M ? m : M - 1;                     // rows past M: computed, never stored
-            base[i] = (const uint8_t*)a.X;
-            step[i] = kQB * 2;
-            voff[i] = (uint32_t)m * (uint32_t)K * 2u + 16u * c;
-            kx[i] = 8 * c;
-        }
-        base[i] = uniform_ptr(base[i]);
-    }
+    for (int i = 0; i < L; ++i)
+        q4_unit<SH>(a, wave * L + i, lane, n_tile, m_tile, base[i], step[i], voff[i], kx[i]);
     const bool ktail = (K % kQB) != 0;
     auto issue = [&](int kb, int slot) {
         if (ktail && kb == KBn - 1) {
@@ -195,55 +252,104 @@ __global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
     for (int d = 0; d < D - 1; ++d)
         if (d < nkb) issue(kb0 + d, d);
 
-    const u32x4 neg = {kNegOff, kNegOff, kNegOff, kNegOff};
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     for (int i = 0; i < nkb; ++i) {
         wait_stages_q4<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();                     // everyone's loads of stage i landed
         asm volatile("" ::: "memory");
         if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
-        const int slot = i % D;
-
-        u32x4 wq[NF];
-        uint32_t sc[NF];
-        const uint32_t* su = (const uint32_t*)&ring[slot][FW][0];
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-            wq[f] = ring[slot][wr * NF + f][lane];
-            sc[f] = su[(wr * NF + f) * 16 + l16];
-        }
-        // X operand of token tile t, k-step q: row l16, chunk 4 q + lg.
-        u32x4 ax[MT][4];
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const u32x4* xt = &ring[slot][XU + 4 * (wc * MT + t)][0];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ax[t][q] = xt[l16 * 16 + ((4 * q + lg) ^ l16)];
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {   // scale group 2 (kb0 + i) + h
-            f32x4 cor[MT];
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                cor[t] = mfma16(ax[t][2 * h], neg, zero);
-                cor[t] = mfma16(ax[t][2 * h + 1], neg, cor[t]);
-            }
-#pragma unroll
-            for (int f = 0; f < NF; ++f) {
-                u32x4 b0, b1;
-                unpack2(wq[f][2 * h], wq[f][2 * h + 1], b0, b1);
-                const float s = h ? half_hi(sc[f]) : half_lo(sc[f]);
-#pragma unroll
-                for (int t = 0; t < MT; ++t) {
-                    f32x4 d = mfma16(ax[t][2 * h], b0, cor[t]);
-                    d = mfma16(ax[t][2 * h + 1], b1, d);
-                    acc[f][t] = d * s + acc[f][t];
-                }
-            }
-        }
+        q4_stage_products<SH>(acc, ring[i % D], wr, wc, lane);
     }
 
+    store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,
+                                wc * SH::WM);
+}
+
+
+// The same product with NL loader wavefronts issuing every direct-to-LDS load
+// (the protocol of the bf16 loader-wavefront ring): the NW product wavefronts
+// only read operands, unpack and multiply, so none of them stalls on the load
+// queue right after a barrier.
+template <int BN, int TM, int D, int NW, int NL>
+__global__ __launch_bounds__(64 * (NW + NL)) void gemm_q4_ring_ld_kernel(KArgs a) {
+    using SH = Q4Shape<BN, TM, NW>;
+    constexpr int NF = SH::NF, MT = SH::MT, FX = SH::FX, XU = SH::XU;
+    constexpr int LL = (XU + FX + NL - 1) / NL;   // loads per loader and stage
+    constexpr int FP = LL * NL;                    // units per stage, padded
+    static_assert((D - 1) * LL < 64, "vmcnt range");
+    const int M = a.M, N = a.N, K = a.K;
+    const int S = a.splits;
+    const int lane = threadIdx.x & 63;
+    const int wave = wave_id();
+
+    const int m_tiles = (M + TM - 1) / TM;
+    const int n_tiles = (N + BN - 1) / BN;
+    int n_tile, m_tile, ks;
+    if (!tile_of(blockIdx.x, n_tiles, m_tiles, S, n_tile, ks, m_tile))
+        return;   // padding slot: the whole workgroup leaves together
+    const int KBn = (K + kQB - 1) / kQB;
+    const int bps = (KBn + S - 1) / S;
+    const int kb0 = ks * bps;
+    const int nkb = max(0, min(KBn, kb0 + bps) - kb0);
+
+    __shared__ u32x4 ring[D][FP][64];
+
+    if (wave >= NW) {
+        const int j = wave - NW;
+        const uint8_t* base[LL];
+        int64_t step[LL];
+        uint32_t voff[LL];
+        int kx[LL];
+#pragma unroll
+        for (int i = 0; i < LL; ++i)
+            q4_unit<SH>(a, j * LL + i, lane, n_tile, m_tile, base[i], step[i], voff[i], kx[i]);
+        const bool ktail = (K % kQB) != 0;
+        auto issue = [&](int kb, int slot) {
+            if (ktail && kb == KBn - 1) {
+#pragma unroll
+                for (int i = 0; i < LL; ++i) {
+                    const int u = j * LL + i;
+                    const bool isx = u >= XU && u < XU + FX;
+                    const uint8_t* p = base[i] + kb * step[i] + voff[i];
+                    if (isx && kb * kQB + kx[i] >= K) p = (const uint8_t*)&g_zero16;
+                    dma16(p, &ring[slot][u][0]);
+                }
+                return;
+            }
+#pragma unroll
+            for (int i = 0; i < LL; ++i) dma16s(base[i] + kb * step[i], voff[i], &ring[slot][j * LL + i][0]);
+        };
+#pragma unroll
+        for (int d = 0; d < D - 1; ++d)
+            if (d < nkb) issue(kb0 + d, d);
+        for (int i = 0; i < nkb; ++i) {
+            wait_stages_q4<LL, D>(min(D - 2, nkb - 1 - i));   // own loads of stage i landed
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
+        }
+        if (S > 1) {   // the two barriers of the split-K store
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
+
+    f32x4 acc[NF][MT];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wr = wave / SH::WC, wc = wave - (wave / SH::WC) * SH::WC;
+    for (int i = 0; i < nkb; ++i) {
+        // own operand reads of stage i - 1 complete (lgkmcnt 0, no vmcnt wait)
+        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        q4_stage_products<SH>(acc, ring[i % D], wr, wc, lane);
+    }
     store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,
                                 wc * SH::WM);
 }
@@ -290,6 +396,31 @@ void add_q4(std::vector<Variant>& out, int S) {
     v.geometry = &geom_q4_ring<BN, TM, D, NW>;
     v.workspace = &ws_q4_ring<BN, TM, D, NW>;
     v.block = 64 * NW;
+    out.push_back(v);
+}
+
+// Loader-wavefront form (stage_x 5): NW product wavefronts plus four loaders.
+template <int BN, int TM, int D, int NW>
+void add_q4_ld(std::vector<Variant>& out, int S) {
+    constexpr int NL = 4;
+    using SH = Q4Shape<BN, TM, NW>;
+    constexpr int FP = (SH::XU + SH::FX + NL - 1) / NL * NL;
+    static_assert(D * FP * 1024 <= 160 * 1024, "LDS ring too large");
+    Variant v{};
+    v.kind = LIN_KIND_SKINNY_Q4G64;
+    v.cfg.algo = LIN_ALGO_MFMA;
+    v.cfg.rows = BN;
+    v.cfg.unroll = D;
+    v.cfg.split = S;
+    v.cfg.stage_x = 5;
+    v.cfg.waves = NW == 4 ? 0 : NW;
+    v.cfg.tile_m = TM;
+    v.mt = 0;
+    v.min_m = 1;
+    v.func = (const void*)&gemm_q4_ring_ld_kernel<BN, TM, D, NW, NL>;
+    v.geometry = &geom_q4_ring<BN, TM, D, NW>;
+    v.workspace = &ws_q4_ring<BN, TM, D, NW>;
+    v.block = 64 * (NW + NL);
     out.push_back(v);
 }
 
@@ -389,6 +520,18 @@ void register_gemm_q4_ring(std::vector<Variant>& out) {
         add_q4<128, 128, 2, 8>(out, S);
         add_q4<256, 128, 2, 8>(out, S);
         add_q4<64, 256, 2, 8>(out, S);
+        add_q4_ld<64, 16, 6, 4>(out, S);
+        add_q4_ld<128, 16, 6, 4>(out, S);
+        add_q4_ld<128, 16, 6, 8>(out, S);
+        add_q4_ld<64, 32, 6, 4>(out, S);
+        add_q4_ld<128, 32, 4, 4>(out, S);
+        add_q4_ld<64, 64, 4, 4>(out, S);
+        add_q4_ld<128, 64, 4, 4>(out, S);
+        add_q4_ld<128, 64, 4, 8>(out, S);
+        add_q4_ld<256, 64, 3, 8>(out, S);
+        add_q4_ld<64, 128, 3, 4>(out, S);
+        add_q4_ld<128, 128, 3, 8>(out, S);
+        add_q4_ld<128, 128, 2, 8>(out, S);
     }
 }
 

@@ -2,6 +2,7 @@
 rejects invalid arguments before touching the GPU.  CPU only: every call here
 returns from argument validation, no kernel is launched."""
 import ctypes
+import json
 import os
 import re
 
@@ -257,3 +258,21 @@ def test_default_q4_skinny_config_needs_no_workspace():
             c = L.lin_get_config(L.LIN_KIND_SKINNY_Q4G64, M, N, K)
             assert c["algo"] == L.LIN_ALGO_MFMA and c["split"] == 1, (M, N, K, c)
             assert c["tile_m"] >= min(M, 128) or c["tile_m"] == 16, (M, N, K, c)
+
+
+def test_loader_wavefront_rings_are_candidates():
+    """Both batched products offer the ring with four loader wavefronts
+    (stage_x 5) at every split, beside the rings whose product wavefronts
+    issue their own loads; the tables pick them by shape."""
+    for kind in (L.LIN_KIND_SKINNY_BF16, L.LIN_KIND_SKINNY_Q4G64):
+        for M in (8, 64, 256):
+            cands = L.lin_candidates(kind, M, 14336, 4096)
+            ld = [c for c in cands if c["algo"] == L.LIN_ALGO_MFMA and c["stage_x"] == 5]
+            own = [c for c in cands if c["algo"] == L.LIN_ALGO_MFMA and c["stage_x"] == 4]
+            assert ld and own, (kind, M)
+            assert {c["split"] for c in ld} == {1, 2, 4, 8}, (kind, M)
+    for name, kind in (("mistral-7b-skinny.json", L.LIN_KIND_SKINNY_BF16),
+                       ("mistral-7b-skinny-q4.json", L.LIN_KIND_SKINNY_Q4G64)):
+        table = json.load(open(os.path.join(os.path.dirname(L.__file__), "tuning", name)))
+        picked = [e["cfg"]["stage_x"] for e in table["entries"] if e["kind"] == kind]
+        assert 5 in picked, name

@@ -57,31 +57,6 @@ __device__ __forceinline__ int ring_swz(int r) { return r & 7; }
 // non-temporal hint on the weights measured slower); k >= K lanes load
 // g_zero16 instead of reading past a row.
 
-// s_waitcnt with vmcnt <= V (V < 64, 63 = no wait) and lgkmcnt <= G (G < 16);
-// expcnt not waited on.
-template <int V, int G>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    static_assert(V >= 0 && V < 64 && G >= 0 && G < 16, "counter range");
-    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (G << 8));
-}
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-    wait_vm_lgkm<N, 0>();
-}
-
-template <int L, int D, int J = 0>
-__device__ __forceinline__ void wait_stages(int after) {
-    if constexpr (J <= D - 2) {
-        if (after == J) {
-            wait_vm_lgkm0<J * L>();
-            return;
-        }
-        wait_stages<L, D, J + 1>(after);
-    } else {
-        wait_vm_lgkm0<0>();
-    }
-}
-
 // Wave tile of a workgroup tile: NW wavefronts as WR x WC; KB k per stage
 // (eight wavefronts and 128-k stages measured no faster than 4 and 64).  A
 // 16-token tile stacks the wavefronts along W (4 x 1).  The fragment loads of
@@ -243,9 +218,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
 
     for (int i = 0; i < nkb; ++i) {
         wait_stages<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();                  // everyone's loads of stage i landed
-        asm volatile("" ::: "memory");
+        ring_barrier();                                // everyone's loads of stage i landed
         if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
         stage_products<SH, LINE>(acc, ring[i % D], wr, wc, lane);
     }
@@ -264,12 +237,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_mfma_ring_kernel(KArgs a) {
 // cycles), so in the ring above every wavefront stalls for its share of that
 // queue right after the barrier, in lockstep with the others, and the matrix
 // cores idle meanwhile; here those stalls fall on wavefronts that have no
-// products to hold up.  Protocol per iteration i (every wavefront meets every
-// barrier): a loader waits until its loads of stage i have landed, meets the
-// barrier, then refills the slot of stage i - 1 with stage i + D - 1; a product
-// wavefront waits for its own operand reads of stage i - 1, meets the barrier
-// (so stage i has landed and nobody still reads stage i - 1), then multiplies
-// stage i.  For split-K the loaders also meet the two barriers of the store.
+// products to hold up.  Per iteration i (every wavefront meets every
+// barrier): a loader waits until its own loads of stage i have landed, meets
+// the barrier, then refills the slot of stage i - 1 with stage i + D - 1; a
+// product wavefront waits for its own operand reads of stage i - 1, meets the
+// barrier (stage i has landed, nobody still reads stage i - 1), then
+// multiplies stage i.  For split-K the loaders also meet the two barriers of
+// the store.
 template <int BN, int TM, int D, int NW, int NL>
 __global__ __launch_bounds__(64 * (NW + NL)) void gemm_mfma_ring_ld_kernel(KArgs a) {
     constexpr int KB = 64;
@@ -325,9 +299,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gemm_mfma_ring_ld_kernel(KArgs
             if (d < nkb) issue(kb0 + d, d);
         for (int i = 0; i < nkb; ++i) {
             wait_stages<LL, D>(min(D - 2, nkb - 1 - i));   // own loads of stage i landed
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
+            ring_barrier();
             if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
         }
         if (S > 1) {   // the two barriers of the split-K store
@@ -345,9 +317,7 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gemm_mfma_ring_ld_kernel(KArgs
     const int wr = wave / SH::WC, wc = wave - (wave / SH::WC) * SH::WC;
     for (int i = 0; i < nkb; ++i) {
         wait_vm_lgkm<63, 0>();   // own operand reads of stage i - 1 complete
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+        ring_barrier();
         stage_products<SH, true>(acc, ring[i % D], wr, wc, lane);
     }
     store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,

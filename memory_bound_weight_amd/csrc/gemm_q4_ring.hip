@@ -78,26 +78,6 @@ __device__ __forceinline__ float half_hi(uint32_t v) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm0_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-}
-// Wait until the loads of the stage `after` stages back have landed: L loads
-// per stage, issued in stage order, complete in order.
-template <int L, int D, int J = 0>
-__device__ __forceinline__ void wait_stages_q4(int after) {
-    if constexpr (J <= D - 2) {
-        if (after == J) {
-            wait_vm0_lgkm0<J * L>();
-            return;
-        }
-        wait_stages_q4<L, D, J + 1>(after);
-    } else {
-        wait_vm0_lgkm0<0>();
-    }
-}
-
 // Load unit u of a stage (code units 0 .. FW - 1, the scale unit FW, X units,
 // then padding): a wavefront-uniform base at block 0, the bytes per block and
 // the lane's byte offset from the base, and for X units the k of the lane's
@@ -253,10 +233,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_q4_ring_kernel(KArgs a) {
         if (d < nkb) issue(kb0 + d, d);
 
     for (int i = 0; i < nkb; ++i) {
-        wait_stages_q4<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();                     // everyone's loads of stage i landed
-        asm volatile("" ::: "memory");
+        wait_stages<L, D>(min(D - 2, nkb - 1 - i));   // stage i landed (own loads)
+        ring_barrier();                                // everyone's loads of stage i landed
         if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
         q4_stage_products<SH>(acc, ring[i % D], wr, wc, lane);
     }
@@ -323,10 +301,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gemm_q4_ring_ld_kernel(KArgs a
         for (int d = 0; d < D - 1; ++d)
             if (d < nkb) issue(kb0 + d, d);
         for (int i = 0; i < nkb; ++i) {
-            wait_stages_q4<LL, D>(min(D - 2, nkb - 1 - i));   // own loads of stage i landed
-            asm volatile("" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
+            wait_stages<LL, D>(min(D - 2, nkb - 1 - i));   // own loads of stage i landed
+            ring_barrier();
             if (i + D - 1 < nkb) issue(kb0 + i + D - 1, (i + D - 1) % D);
         }
         if (S > 1) {   // the two barriers of the split-K store
@@ -343,11 +319,8 @@ __global__ __launch_bounds__(64 * (NW + NL)) void gemm_q4_ring_ld_kernel(KArgs a
         for (int t = 0; t < MT; ++t) acc[f][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int wr = wave / SH::WC, wc = wave - (wave / SH::WC) * SH::WC;
     for (int i = 0; i < nkb; ++i) {
-        // own operand reads of stage i - 1 complete (lgkmcnt 0, no vmcnt wait)
-        __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
+        wait_vm_lgkm<63, 0>();   // own operand reads of stage i - 1 complete
+        ring_barrier();
         q4_stage_products<SH>(acc, ring[i % D], wr, wc, lane);
     }
     store_tiles<BN, TM, NF, MT>(acc, a, S, n_tile, m_tile, ks, n_tiles, m_tiles, wr * SH::WN,

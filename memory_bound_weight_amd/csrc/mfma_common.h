@@ -40,6 +40,38 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4& a, const u32x4& b, const f3
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// s_waitcnt with vmcnt <= V (V < 64; 63 does not wait on loads) and
+// lgkmcnt <= G (G < 16); expcnt not waited on.
+template <int V, int G>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(V >= 0 && V < 64 && G >= 0 && G < 16, "counter range");
+    __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4) | (G << 8));
+}
+
+// Wait (also for every LDS access) until the loads of the current ring stage
+// have landed while `after` later stages, L loads each, may still be in
+// flight: loads are issued in stage order and complete in order.
+template <int L, int D, int J = 0>
+__device__ __forceinline__ void wait_stages(int after) {
+    if constexpr (J <= D - 2) {
+        if (after == J) {
+            wait_vm_lgkm<J * L, 0>();
+            return;
+        }
+        wait_stages<L, D, J + 1>(after);
+    } else {
+        wait_vm_lgkm<0, 0>();
+    }
+}
+
+// Workgroup barrier that the compiler may not move memory accesses across
+// (a bare s_barrier: __syncthreads would also wait for the loads in flight).
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Store the NF x MT 16x16 accumulators of one wavefront: lane l holds W row
 // n_tile * BN + nl0 + 16 f + l mod 16 and tokens m_tile * TM + ml0 + 16 t +
 // 4 (l / 16) + r.  S == 1 writes Y directly.  Otherwise the partial tile goes

@@ -43,14 +43,15 @@ constexpr int kQB = 128;   // k per ring stage and per tiled unit
 constexpr uint32_t kNegOff = kQ4NegOffsetPair;
 
 // Wave tile of a workgroup tile: NW wavefronts as WR x WC, as the bf16 ring
-// except that eight wavefronts split a 128-token tile 4 x 2, not 2 x 4: every
-// wavefront that reads a W fragment unpacks it, so fewer wavefronts across
-// the tokens means less unpacking per product (M = 256, 32000x4096 with
-// 256 x 128 tiles: 83 -> 77 us).
+// except that eight wavefronts split a 128-token tile 4 x 2, not 2 x 4, and a
+// 256 x 64 tile 8 x 1: every wavefront that reads a W fragment unpacks it, so
+// fewer wavefronts across the tokens means less unpacking per product, at one
+// offset product per NF fragments (M = 256, 32000x4096 with 256 x 128 tiles:
+// 83 -> 77 us; 14336x4096 with 256 x 64 tiles: 43.5 -> 42.8 us).
 template <int BN_, int TM_, int NW>
 struct Q4Shape {
     static constexpr int BN = BN_, TM = TM_;
-    static constexpr int WR = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 256 ? 2 : 4));
+    static constexpr int WR = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 256 ? 2 : (TM >= 128 || BN < 256 ? 4 : 8)));
     static constexpr int WC = NW / WR;
     static constexpr int WN = BN / WR, WM = TM / WC;
     static constexpr int NF = WN / 16, MT = WM / 16;

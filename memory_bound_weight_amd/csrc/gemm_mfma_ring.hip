@@ -64,7 +64,9 @@ __device__ __forceinline__ int ring_swz(int r) { return r & 7; }
 // divide, the stage is padded with fragments that load the zero word.
 template <int BN, int TM, int NW, int KB>
 struct Shape {
-    static constexpr int WR = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4));
+    static constexpr int WR0 = TM <= 16 ? NW : (NW == 4 ? (TM >= 256 ? 1 : 2) : (TM >= 128 ? 2 : 4));
+    // a tile whose 16-row fragments do not split WR0 ways stacks the wavefronts along the tokens
+    static constexpr int WR = (BN / 16) % WR0 == 0 ? WR0 : 1;
     static constexpr int WC = NW / WR;
     static constexpr int WN = BN / WR, WM = TM / WC;
     static constexpr int NF = WN / 16, MT = WM / 16;
@@ -450,6 +452,10 @@ void register_gemm_mfma_ring(std::vector<Variant>& out) {
         add_ring_ld<128, 256, 3, 8>(out, S);
         add_ring_ld<64, 256, 3, 4>(out, S);
         add_ring_ld<64, 256, 3, 8>(out, S);
+        add_ring1<112, 128, 4, true, 4>(out, S);
+        add_ring1<112, 128, 4, true, 8>(out, S);
+        add_ring_ld<112, 128, 4, 4>(out, S);
+        add_ring_ld<112, 128, 4, 8>(out, S);
     }
 }
 

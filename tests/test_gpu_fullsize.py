@@ -136,6 +136,34 @@ def test_mistral_skinny_sampled(M):
         assert_within_bound(Y[:, idx], Yo, Bo, "skinny M=%d %dx%d" % (M, N, K))
 
 
+
+@pytest.mark.parametrize("M", [1, 33, 200])
+def test_mistral_skinny_default_configs_sampled(M):
+    """Token counts the tables hold no entry for run in the library's default
+    configurations (no tuning at this M): full Mistral shapes, bf16 and tiled
+    int4-g64, sampled rows against the oracle."""
+    _tuned("mistral-7b-skinny")
+    _tuned("mistral-7b-skinny-q4")
+    for N, K in synth.MISTRAL_SHAPES:
+        print("case skinny default full M=%d %dx%d" % (M, N, K), flush=True)
+        W = synth.weight(synth.MISTRAL_SEED + 7, 0, N, N, K, device=DEV)
+        X = synth.activation(synth.MISTRAL_SEED + 7, 0, N, M, K, device=DEV)
+        rows = _sample_rows(N, k=12)
+        idx = torch.from_numpy(rows).to(DEV)
+        Y = L.lin_gemm_skinny_bf16(W, X)
+        torch.cuda.synchronize()
+        Yo, Bo = oracle.gemm_dense(u16(W[idx]), u16(X))
+        assert_within_bound(Y[:, idx], Yo, Bo, "skinny default M=%d %dx%d" % (M, N, K))
+        Wq, S = L.lin_quantize_q4g64(W)
+        T = L.lin_q4g64_tile(Wq, S)
+        Yq = L.lin_gemm_skinny_q4g64(T, X)
+        torch.cuda.synchronize()
+        Wq_o, S_o = oracle.quantize_q4g64(u16(W[idx]))
+        Yqo, Bqo = oracle.gemm_q4g64(Wq_o, S_o, u16(X))
+        assert_within_bound(Yq[:, idx], Yqo, Bqo, "skinny q4 default M=%d %dx%d" % (M, N, K))
+        del W, Wq, S, T
+
+
 def test_maximum_k():
     K = 1 << 22   # LIN_MAX_K
     for N in (3,):

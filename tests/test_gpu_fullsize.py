@@ -70,6 +70,39 @@ def test_decode_shapes_bf16_and_int4_sampled(model):
         del W, Wq, S
 
 
+
+@pytest.mark.parametrize("M", [3, 8])
+def test_decode_shapes_few_tokens_sampled(M):
+    """The batch-1 products at 2-8 tokens (no table entry: default
+    configurations) on every Qwen2.5-7B shape, bf16, int4-g64 and INT8,
+    sampled rows against the oracle."""
+    model = synth.QWEN7B
+    _tuned(model["name"])
+    for N, K in _shapes(model):
+        print("case fullsize few tokens M=%d %dx%d" % (M, N, K), flush=True)
+        W = synth.weight(model["seed"] + 3, 0, 98, N, K, device=DEV)
+        x = synth.activation(model["seed"] + 3, 0, 98, M, K, device=DEV)
+        rows = _sample_rows(N, k=12)
+        idx = torch.from_numpy(rows).to(DEV)
+        Wr = u16(W[idx])
+        xb = u16(x)
+        y = L.lin_gemv_bf16(W, x)
+        torch.cuda.synchronize()
+        Y, B = oracle.gemm_dense(Wr, xb)
+        assert_within_bound(y[:, idx], Y, B, "bf16 M=%d %dx%d" % (M, N, K))
+        Wq, S = L.lin_quantize_q4g64(W)
+        y4 = L.lin_gemv_q4g64(Wq, S, x)
+        torch.cuda.synchronize()
+        Y4, B4 = oracle.gemm_q4g64(*oracle.quantize_q4g64(Wr), xb)
+        assert_within_bound(y4[:, idx], Y4, B4, "int4 M=%d %dx%d" % (M, N, K))
+        W8, S8 = L.lin_quantize_i8(W)
+        y8 = L.lin_gemv_i8(W8, S8, x)
+        torch.cuda.synchronize()
+        Y8, B8 = oracle.gemm_i8(*oracle.quantize_i8(Wr), xb)
+        assert_within_bound(y8[:, idx], Y8, B8, "i8 M=%d %dx%d" % (M, N, K))
+        del W, Wq, S, W8, S8
+
+
 def test_single_gemv_full_oracle():
     N, K = synth.SINGLE_SHAPE
     W = synth.weight(synth.SINGLE_SEED, 0, 0, N, K, device=DEV)

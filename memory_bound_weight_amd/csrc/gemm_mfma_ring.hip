@@ -34,9 +34,14 @@
 //
 // Wave tile.  The workgroup tile BN x TM is split 2 x 2 (or 1 x 4 when TM is
 // 256) among four wavefronts, or 2 x 4 / 4 x 2 among eight (two per SIMD,
-// so one can multiply while the other waits); each keeps its NF x MT 16x16 fp32
-// accumulators in registers and writes them directly, or as a split-K partial
-// that the last workgroup of the tile adds in split order (deterministic).
+// so one can multiply while the other waits), or 1 x NW when the tile's
+// 16-row fragments do not split evenly (112-row tiles); each keeps its NF x MT
+// 16x16 fp32 accumulators in registers and writes them directly, or as a
+// split-K partial that the last workgroup of the tile adds in split order
+// (deterministic).
+//
+// A second kernel below adds loader wavefronts that issue every load of the
+// ring, so that the product wavefronts never stall on the load queue.
 #include "mfma_common.h"
 #include "registry.h"
 

@@ -276,3 +276,19 @@ def test_loader_wavefront_rings_are_candidates():
         table = json.load(open(os.path.join(os.path.dirname(L.__file__), "tuning", name)))
         picked = [e["cfg"]["stage_x"] for e in table["entries"] if e["kind"] == kind]
         assert 5 in picked, name
+
+
+def test_candidate_configs_are_unique():
+    """A configuration names one kernel: no two candidates of a kind and shape
+    share every public field, so a tuning-table entry is unambiguous."""
+    fields = ("algo", "rows", "unroll", "split", "stage_x", "tile_m", "waves")
+    kinds = [getattr(L, k) for k in dir(L) if k.startswith("LIN_KIND_")]
+    for kind in kinds:
+        for M, N, K in ((1, 4096, 4096), (3, 37888, 3584), (8, 4096, 4096), (64, 14336, 4096),
+                        (256, 14336, 4096), (256, 300, 4104)):
+            try:
+                cands = L.lin_candidates(kind, M, N, K)
+            except L.LinError:
+                continue
+            keys = [tuple(c[f] for f in fields) for c in cands]
+            assert len(keys) == len(set(keys)), (kind, M, N, K)

@@ -360,6 +360,30 @@ def read_ceiling(nbytes, dev, reps):
     return nbytes / (gpu / n) / 1e9
 
 
+def read_chain(mats, dev, reps, warmup):
+    """The floor of a step launched one kernel per matrix: lin_stream_read over a
+    buffer of each matrix's algorithmic bytes (weights, scales, x and y), one
+    launch per matrix in step order, captured as one graph and replayed like the
+    step.  Each launch is a read-only pass that does nothing else, so the chain's
+    time is what the launches, their start ramps and their drains cost with no
+    products at all.  Mean seconds per replay."""
+    bufs = [torch.empty(max(16, m.bytes // 16 * 16), dtype=torch.uint8, device=dev) for m in mats]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for b in bufs:
+            L.lin_stream_read(b)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for b in bufs:
+            L.lin_stream_read(b)
+    ts = replay_times(g, reps, warmup)
+    del g, bufs
+    return float(np.mean(ts))
+
+
 def measured_traffic(key, shapes_mix):
     """HBM bytes per launch of kernel variant `key` over the step's shape mix,
     from the counter table, or None if none was taken for the current source."""
@@ -883,13 +907,18 @@ def main():
         # the same pass without the graph: one host call per matrix
         eager, _ = time_runs([lambda f=f: [launch(m) for m in sets[f]]], max(10, args.steps // 2),
                              args.warmup)
+        chain = read_chain(sets[f], dev, max(30, args.steps), args.warmup)
         per_fmt[f] = {"ms_per_token": round(gpu_f * 1e3, 4), "equiv_tok_s": round(1.0 / gpu_f, 1),
                       "GB_s": round(fmt_bytes[f] / gpu_f / 1e9, 1), "bytes": fmt_bytes[f],
                       "median_ms": round(med * 1e3, 4), "iqr_ms": round(iqr * 1e3, 4),
-                      "no_graph_ms_per_token": round(eager * 1e3, 4)}
+                      "no_graph_ms_per_token": round(eager * 1e3, 4),
+                      "read_chain_ms": round(chain * 1e3, 4),
+                      "read_chain_GB_s": round(fmt_bytes[f] / chain / 1e9, 1),
+                      "frac_of_read_chain": round(chain / gpu_f, 4)}
         log("%s step: %.1f us (median %.1f, IQR %.1f), %.1f GB/s, %.0f tok/s; without the graph "
-            "%.1f us" % (f, gpu_f * 1e6, med * 1e6, iqr * 1e6, fmt_bytes[f] / gpu_f / 1e9, 1 / gpu_f,
-                         eager * 1e6))
+            "%.1f us; read chain %.1f us" % (f, gpu_f * 1e6, med * 1e6, iqr * 1e6,
+                                             fmt_bytes[f] / gpu_f / 1e9, 1 / gpu_f, eager * 1e6,
+                                             chain * 1e6))
     # the timed region: K steps of the whole path (one decode pass per format, in order)
     torch.cuda.synchronize()
     wall, gpu = time_runs([graphs[f].replay for f in fmts], args.steps, args.warmup)

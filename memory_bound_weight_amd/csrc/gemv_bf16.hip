@@ -86,6 +86,12 @@ void register_gemv_bf16(std::vector<Variant>& out) {
     add_splits<1, 4, 1>(out);
     add_splits<1, 4, 2>(out);
     add_splits<1, 8, 1>(out);
+    // K = 3584 has 448 chunks, 7 x 64: one wavefront per row with seven loads
+    // per lane covers it with no idle lanes (every split leaves some idle)
+    add<1, 1, 7, 1, false>(out);
+    add<1, 1, 7, 1, true>(out);
+    add<1, 2, 7, 1, false>(out);
+    add<1, 2, 7, 1, true>(out);
 
     add_splits<2, 1, 2>(out);
     add_splits<2, 2, 1>(out);

@@ -19,10 +19,10 @@ its kernels are built from: bench.py ignores it once those change.
 
 Example (repository root):
 
-  python memory_bound_weight_amd/tuning/hbm_counters.py --fetch gpurun_out/pa_fetch \\
-      --write gpurun_out/pa_write --copy-fetch gpurun_out/pa_cfetch \\
-      --copy-write gpurun_out/pa_cwrite --copy-bytes 1073741824 \\
-      --launches gpurun_out/counter_pass.log --out memory_bound_weight_amd/tuning/hbm_traffic.json
+  python memory_bound_weight_amd/tuning/hbm_counters.py --fetch prof/pa_fetch \\
+      --write prof/pa_write --copy-fetch prof/pa_cfetch \\
+      --copy-write prof/pa_cwrite --copy-bytes 1073741824 \\
+      --launches prof/counter_pass.log --out memory_bound_weight_amd/tuning/hbm_traffic.json
 """
 import argparse
 import collections

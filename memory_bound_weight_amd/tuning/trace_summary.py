@@ -18,8 +18,8 @@ small CSV, so that the raw trace need not be kept.
 
 Example (repository root):
 
-  python memory_bound_weight_amd/tuning/trace_summary.py --trace gpurun_out/pa_qwen/bench \\
-      --bench gpurun_out/bench.log --out gpurun_out/kernel_stats.md
+  python memory_bound_weight_amd/tuning/trace_summary.py --trace prof/pa_qwen/bench \\
+      --bench prof/bench.log --out prof/kernel_stats.md
 """
 import argparse
 import collections
@@ -68,6 +68,16 @@ def col(row, *names):
     raise KeyError(names[0])
 
 
+def grid_of(row):
+    """Work-items of a traced dispatch (the product of the grid's dimensions;
+    a missing or empty Y or Z column counts as 1)."""
+    g = int(col(row, "Grid_Size_X", "Grid_Size"))
+    for d in ("Grid_Size_Y", "Grid_Size_Z"):
+        if row.get(d, "") != "":
+            g *= int(row[d])
+    return g
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--trace", required=True)
@@ -88,8 +98,7 @@ def main():
     durs = collections.defaultdict(list)
     for r in csv.DictReader(open(args.trace + "_kernel_trace.csv")):
         name = short(col(r, "Kernel_Name"))
-        grid = int(col(r, "Grid_Size_X", "Grid_Size")) * int(col(r, "Grid_Size_Y") if "Grid_Size_Y" in r else 1) \
-            * int(col(r, "Grid_Size_Z") if "Grid_Size_Z" in r else 1)
+        grid = grid_of(r)
         d = (int(col(r, "End_Timestamp")) - int(col(r, "Start_Timestamp"))) / 1000.0
         durs[(name, grid)].append(d)
 

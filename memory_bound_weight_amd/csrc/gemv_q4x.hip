@@ -30,11 +30,13 @@
 // N g / ng .. N (g + 1) / ng - 1, at most RW, so every group streams the same
 // number of rows (+-1) for any N, and each streams one contiguous block of
 // the matrix (interleaving the groups' rows so that all groups read one
-// sliding window was measured slower).  The loop over RW rows is unrolled
-// (every wait an exact immediate count, no branches that would make the
-// compiler drain the pipeline); a group with fewer rows reads its missing
-// rows past the end of its buffer resource, which returns zeros without
-// touching memory, and drops them.
+// sliding window was measured slower).  Group numbers follow the XCD the
+// workgroup runs on, so each XCD streams one contiguous eighth of the rows
+// (1-2 % faster on the 7B shapes: fewer scale lines fetched twice).  The loop
+// over RW rows is unrolled (every wait an exact immediate count, no branches
+// that would make the compiler drain the pipeline); a group with fewer rows
+// reads its missing rows past the end of its buffer resource, which returns
+// zeros without touching memory, and drops them.
 //
 // Epilogues as the other GEMV kernels: the residual add, and the gated
 // product over gate|up, where an output needs its gate row and its up row
@@ -94,7 +96,14 @@ __global__ __launch_bounds__(kBlock) void gemv_q4_xres(KArgs a) {
     // shape here); the 64-bit division it replaces is a few hundred scalar
     // instructions in front of the first load of every wavefront.
     const uint32_t ng = gridDim.x * GROUPS;
-    const uint32_t gi = blockIdx.x * GROUPS + grp;
+    // Workgroups go round-robin over the eight XCDs: hand XCD x the x-th
+    // eighth of the row groups, so that the scale-row line two neighbouring
+    // groups share is fetched into one XCD's L2, not two (a bijection on the
+    // workgroup index; the grid is a whole number of compute units).
+    const uint32_t nb = gridDim.x;
+    const uint32_t bx = (nb & 7u) == 0 ? (blockIdx.x & 7u) * (nb >> 3) + (blockIdx.x >> 3)
+                                       : blockIdx.x;
+    const uint32_t gi = bx * GROUPS + grp;
     int o0, o1;
     if (ng < 65536u) {
         const uint32_t q = (uint32_t)N / ng, r = (uint32_t)N - q * ng;

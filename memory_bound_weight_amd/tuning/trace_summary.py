@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--bench", required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--reduced", default=None)
+    ap.add_argument("--from-reduced", default=None, metavar="CSV",
+                    help="take the per-(kernel, grid) dispatch statistics from a CSV that an "
+                         "earlier run wrote with --reduced instead of NAME_kernel_trace.csv")
     ap.add_argument("--top", type=int, default=12)
     args = ap.parse_args()
 
@@ -95,12 +98,21 @@ def main():
         raise SystemExit("no bench.py JSON line with per-kernel figures in %s" % args.bench)
 
     stats = list(csv.DictReader(open(args.trace + "_kernel_stats.csv")))
-    durs = collections.defaultdict(list)
-    for r in csv.DictReader(open(args.trace + "_kernel_trace.csv")):
-        name = short(col(r, "Kernel_Name"))
-        grid = grid_of(r)
-        d = (int(col(r, "End_Timestamp")) - int(col(r, "Start_Timestamp"))) / 1000.0
-        durs[(name, grid)].append(d)
+    # (kernel, grid) -> (dispatches, mean us, median us, min us, max us)
+    groups = {}
+    if args.from_reduced:
+        for r in csv.DictReader(open(args.from_reduced)):
+            groups[(r["kernel"], int(r["grid_items"]))] = (
+                int(r["dispatches"]), float(r["avg_us"]), float(r["median_us"]),
+                float(r["min_us"]), float(r["max_us"]))
+    else:
+        durs = collections.defaultdict(list)
+        for r in csv.DictReader(open(args.trace + "_kernel_trace.csv")):
+            name = short(col(r, "Kernel_Name"))
+            d = (int(col(r, "End_Timestamp")) - int(col(r, "Start_Timestamp"))) / 1000.0
+            durs[(name, grid_of(r))].append(d)
+        for key, v in durs.items():
+            groups[key] = (len(v), statistics.mean(v), statistics.median(v), min(v), max(v))
 
     out = []
     out.append("Top kernels from `%s_kernel_stats.csv` (every dispatch of the run):\n" % args.trace.split("/")[-1])
@@ -120,30 +132,38 @@ def main():
     out.append("| kernel variant | shape | instance | launches per step | rocprof dispatches | "
                "rocprof avg us | rocprof median us | bench.py live us | difference |")
     out.append("|---|---|---|---|---|---|---|---|---|")
+    # shapes of one variant with the same N launch the same instance on the same
+    # grid: their dispatches cannot be told apart, and the row says so
+    same = collections.defaultdict(list)
+    for key in bench["kernels"]:
+        variant, shape = key.rsplit(" ", 1)
+        same[(variant, grid_items(variant, int(shape.split("x")[0])))].append(shape)
     for key, k in bench["kernels"].items():
         variant, shape = key.rsplit(" ", 1)
         N = int(shape.split("x")[0])
         pat = re.compile(instance_pattern(variant))
         g = grid_items(variant, N)
-        hits = [(n, v) for (n, gr), v in durs.items() if gr == g and pat.search(n)]
+        others = [o for o in same[(variant, g)] if o != shape]
+        hits = [(n, v) for (n, gr), v in groups.items() if gr == g and pat.search(n)]
         if len(hits) != 1:
             out.append("| `%s` | %s | (%d matching instances at grid %d) | %d | | | | %.2f | |"
                        % (variant, shape, len(hits), g, k["launches"], k["avg_us"]))
             continue
-        n, v = hits[0]
-        avg, med = statistics.mean(v), statistics.median(v)
-        out.append("| `%s` | %s | `%s` | %d | %d | %.2f | %.2f | %.2f | %.1f %% |" % (
-            variant, shape, n, k["launches"], len(v), avg, med, k["avg_us"],
-            100.0 * (avg - k["avg_us"]) / k["avg_us"]))
+        n, (cnt, avg, med, _, _) = hits[0]
+        diff = "%.1f %%" % (100.0 * (avg - k["avg_us"]) / k["avg_us"])
+        if others:
+            diff = "(traced with %s: same instance and grid)" % ", ".join(others)
+        out.append("| `%s` | %s | `%s` | %d | %d | %.2f | %.2f | %.2f | %s |" % (
+            variant, shape, n, k["launches"], cnt, avg, med, k["avg_us"], diff))
     with open(args.out, "w") as f:
         f.write("\n".join(out) + "\n")
     if args.reduced:
         with open(args.reduced, "w", newline="") as f:
             w = csv.writer(f)
             w.writerow(["kernel", "grid_items", "dispatches", "avg_us", "median_us", "min_us", "max_us"])
-            for (n, gr), v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-                w.writerow([n, gr, len(v), round(statistics.mean(v), 3), round(statistics.median(v), 3),
-                            round(min(v), 3), round(max(v), 3)])
+            for (n, gr), (cnt, avg, med, lo, hi) in sorted(groups.items(),
+                                                          key=lambda kv: -kv[1][0] * kv[1][1]):
+                w.writerow([n, gr, cnt, round(avg, 3), round(med, 3), round(lo, 3), round(hi, 3)])
     print("\n".join(out))
 
 

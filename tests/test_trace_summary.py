@@ -64,3 +64,16 @@ def test_unmatched_shape_is_reported_not_guessed(tmp_path):
     r, md = _write(tmp_path, disp, kernels)
     assert r.returncode == 0, r.stderr
     assert "(0 matching instances at grid 294912)" in md
+
+
+def test_shapes_sharing_instance_and_grid_are_flagged(tmp_path):
+    # o 2048x2048 and down 2048x5632 with one variant: same N, same grid
+    grid = 512 * 256
+    bf = "void lin::gemv_bf16_valu<1, 1, 4, 1, false, 0, false>(lin::KArgs)"
+    disp = [(bf, grid, 3000), (bf, grid, 5000)]
+    kernels = {"gemv_bf16 R1 U4 S1 X0 2048x2048": {"avg_us": 3.0, "launches": 22},
+               "gemv_bf16 R1 U4 S1 X0 2048x5632": {"avg_us": 5.0, "launches": 22}}
+    r, md = _write(tmp_path, disp, kernels)
+    assert r.returncode == 0, r.stderr
+    assert "(traced with 2048x5632: same instance and grid)" in md
+    assert "(traced with 2048x2048: same instance and grid)" in md
